@@ -1,0 +1,96 @@
+"""Random small transfer descriptions shared by the oracle pins and the GPU parity tests.
+
+Every case is drawn from a seeded generator and obeys the call's preconditions:
+spans start on page boundaries, block ids are distinct across the call (so a
+scatter has one writer per pool byte), chunk_layers divides the layer range,
+chunk_tokens is a whole number of pages and every chunk owns its own slot.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LAYER_FIRST = 0
+PAGE_FIRST = 1
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def slot_capacity(pool: dict, chunks: dict) -> int:
+    """Bytes of a full chunk's worth of tokens: chunk_layers x K/V x chunk_tokens
+    tokens.  chunk_tokens is a whole number of pages, so every chunk of either
+    layout fits; used only to size staging slots."""
+    tok = pool["num_heads"] * pool["head_dim"] * pool["elem_bytes"]
+    return chunks["chunk_layers"] * pool["num_kv"] * chunks["chunk_tokens"] * tok
+
+
+def make_case(rng: np.random.Generator, *, tok_multiple: int = 1, max_bytes: int = 1 << 20,
+              layout: int | None = None, n_spans: int | None = None):
+    """A random small case: (pool, spans, chunks) with tables as int32 arrays."""
+    while True:
+        L = int(rng.integers(1, 4))
+        KV = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 4))
+        D = int(rng.choice([8, 16, 24]))
+        E = int(rng.choice([1, 2]))
+        tok = H * D * E
+        if tok % tok_multiple:
+            continue
+        bs = int(rng.choice([2, 4, 16]))
+        tile = bs * tok
+        block_stride = tile + int(rng.choice([0, 0, 16, 48]))
+        if block_stride % tok_multiple:
+            block_stride = tile
+        ns = int(n_spans) if n_spans else int(rng.integers(1, 4))
+        spans_tok = []
+        for _ in range(ns):
+            p0 = int(rng.integers(0, 3))
+            length = int(rng.integers(1, 4 * bs + 3))
+            spans_tok.append((p0 * bs, p0 * bs + length))
+        pages = [cdiv(t1, bs) for _, t1 in spans_tok]
+        N = sum(pages) + int(rng.integers(0, 6))
+        if N * block_stride * L * KV > max_bytes:
+            continue
+        perm = rng.permutation(N).astype(np.int32)
+        tables, pos = [], 0
+        for n in pages:
+            tables.append(perm[pos:pos + n].copy())
+            pos += n
+        lb = int(rng.integers(0, L))
+        le = int(rng.integers(lb + 1, L + 1))
+        divs = [c for c in range(1, le - lb + 1) if (le - lb) % c == 0]
+        CL = int(rng.choice(divs))
+        CT = bs * int(rng.integers(1, 4))
+        lay = int(rng.integers(0, 2)) if layout is None else layout
+        pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E,
+                    block_size=bs, num_blocks=N, block_stride=block_stride)
+        chunks = dict(layout=lay, chunk_layers=CL, chunk_tokens=CT, layer_begin=lb,
+                      layer_end=le, slot_bytes=0, n_slots=0)
+        n_chunks = [((le - lb) // CL) * cdiv(t1 - t0, CT) for t0, t1 in spans_tok]
+        total = sum(n_chunks)
+        n_slots = total + int(rng.integers(0, 4))
+        start = int(rng.integers(0, n_slots))  # may wrap around the ring
+        spans, c = [], start
+        for (t0, t1), tbl, nc in zip(spans_tok, tables, n_chunks):
+            spans.append((tbl, t0, t1, c))
+            c += nc
+        sb = slot_capacity(pool, chunks) + int(rng.choice([0, 0, 16]))
+        if sb % tok_multiple:
+            sb += tok_multiple - sb % tok_multiple
+        chunks.update(slot_bytes=sb, n_slots=n_slots)
+        if sb * n_slots > max_bytes:
+            continue
+        return pool, spans, chunks
+
+
+def regions_for(pool: dict, rng: np.random.Generator) -> np.ndarray:
+    n = pool["num_layers"] * pool["num_kv"]
+    return rng.integers(0, 256, size=(n, pool["num_blocks"] * pool["block_stride"]), dtype=np.uint8)
+
+
+def staging_for(chunks: dict, fill: int | None = None, rng: np.random.Generator | None = None) -> np.ndarray:
+    n = chunks["slot_bytes"] * chunks["n_slots"]
+    if rng is not None:
+        return rng.integers(0, 256, size=n, dtype=np.uint8)
+    return np.full(n, 0xA5 if fill is None else fill, dtype=np.uint8)

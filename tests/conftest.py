@@ -1,0 +1,26 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds")
+    # Build what is missing (a fresh checkout has no built libraries); an
+    # existing build is used as it is.
+    import oracle
+
+    oracle.build(force=False)
+    try:
+        from paged_layout_transfer_amd import _build
+    except ImportError:
+        return
+    _build.build_library(force=False)
