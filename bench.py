@@ -1,0 +1,436 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV gather/scatter path on one MI355X.
+
+Default workload (one "step" = one gather + one scatter of it, all in HBM): the
+Llama-3-8B-shaped KV cache -- 32 layers x K/V x 8 heads x 128 dims bf16,
+16-token pages (32 KiB per layer-page), a 16384-block pool, one 32768-token
+request with a seeded shuffled block table, 256-token layer-first chunks
+(128 chunks of 32 MiB) in HBM.  4 GiB moves each way per step.
+
+The pinned-host path is measured on the Llama-3-70B-shaped context (80 layers,
+one 131072-token request, 2 MiB chunks = 1 layer x 512 tokens) streamed through a
+pinned host staging ring in windows of whole layers, against the host link
+bandwidth measured in the same run by one large hipMemcpy each way.
+
+Prints one JSON line (see the "roofline", "cpu_baseline" and "host_path" keys).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "KV GB/s moved (gather+scatter, HBM and pinned-host) and % of roofline"
+KERNEL_SOURCES = ["paged_layout_transfer_amd/csrc/kvxfer_kernels.hip",
+                  "paged_layout_transfer_amd/csrc/kvxfer_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama8b.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
+def resolve(name):
+    from paged_layout_transfer_amd import workloads as W
+    w = W.resolve(W.WORKLOADS[name])
+    tok = W.token_bytes(w)
+    pool = {k: w[k] for k in ("num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
+                              "block_size", "num_blocks")}
+    pool["block_stride"] = w["block_size"] * tok
+    return w, pool
+
+
+class DevicePool:
+    """A pool of num_layers*num_kv regions in one device tensor, with its handle."""
+
+    def __init__(self, pool, dev):
+        import torch
+        from paged_layout_transfer_amd import kvxfer as K
+        self.pool = pool
+        n = pool["num_layers"] * pool["num_kv"]
+        self.t = torch.empty((n, pool["num_blocks"] * pool["block_stride"]), dtype=torch.uint8, device=dev)
+        bases = [self.t.data_ptr() + i * self.t.stride(0) for i in range(n)]
+        self.desc = K.make_pool_desc(pool["num_layers"], pool["num_kv"], pool["num_heads"],
+                                     pool["head_dim"], pool["elem_bytes"], pool["block_size"],
+                                     pool["num_blocks"], pool["block_stride"], bases)
+        self.h = K.kv_pool_create(self.desc)
+
+    def close(self):
+        from paged_layout_transfer_amd import kvxfer as K
+        K.kv_pool_destroy(self.h)
+        self.h = None
+
+
+def written_mask_check(direction, pool, spans, chunks, host_regions, host_staging_in, got, layer):
+    """Compare one layer of a GPU result with the oracle.  For a gather, got is the GPU
+    staging buffer and the oracle's written bytes are found by running it over two
+    different fills; for a scatter, got is the list of that layer's GPU regions."""
+    import numpy as np
+    import oracle
+    if direction == 0:
+        a = np.zeros(got.size, dtype=np.uint8)
+        b = np.full(got.size, 0xFF, dtype=np.uint8)
+        oracle.gather(pool, host_regions, spans, chunks, a, only_layers=(layer, layer + 1))
+        oracle.gather(pool, host_regions, spans, chunks, b, only_layers=(layer, layer + 1))
+        m = a == b
+        return int(m.sum()) > 0 and bool(np.array_equal(got[m], a[m]))
+    regs = [r.copy() if r is not None else None for r in host_regions]
+    oracle.scatter(pool, regs, spans, chunks, host_staging_in, only_layers=(layer, layer + 1))
+    kv = pool["num_kv"]
+    return all(np.array_equal(regs[layer * kv + k], got[k]) for k in range(kv))
+
+
+def hbm_leg(args, dev):
+    import numpy as np
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    from paged_layout_transfer_amd import workloads as W
+
+    w, pool = resolve(args.workload)
+    plan = W.staging_plan(w)
+    L, KV = pool["num_layers"], pool["num_kv"]
+    payload = sum(t1 - t0 for t0, t1 in w["requests"]) * L * KV * W.token_bytes(w)
+    log("workload %s: pool %.1f GiB, staging %.2f GiB, payload %.3f GB each way" % (
+        args.workload, L * KV * pool["num_blocks"] * pool["block_stride"] / 2**30,
+        plan["slot_bytes"] * plan["n_chunks"] / 2**30, payload / 1e9))
+    P = DevicePool(pool, dev)
+    W.device_fill_(P.t.view(-1), w["fill"], w["k"])
+    S = torch.empty(plan["slot_bytes"] * plan["n_chunks"], dtype=torch.uint8, device=dev)
+    tabs = [torch.from_numpy(t).to(dev) for t in w["block_tables"]]
+    spans_d = K.make_spans([(tb, tb.numel(), t0, t1, fc) for tb, (t0, t1), fc in
+                            zip(tabs, w["requests"], plan["first_chunk"])])
+    spans_h = [(t, t0, t1, fc) for t, (t0, t1), fc in zip(w["block_tables"], w["requests"], plan["first_chunk"])]
+    chunks = dict(layout=w["layout"], chunk_layers=w["chunk_layers"], chunk_tokens=w["chunk_tokens"],
+                  layer_begin=0, layer_end=L, slot_bytes=plan["slot_bytes"], n_slots=plan["n_chunks"])
+    spec = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"], 0, L,
+                             S, plan["slot_bytes"], plan["n_chunks"], args.max_workgroups, 0)
+    info = K.kv_check_transfer(P.desc, spans_d, spec)
+    assert info.payload_bytes == payload
+    stream = torch.cuda.current_stream()
+
+    parity = {}
+    if not args.skip_parity:
+        layer = L - 1
+        K.kv_gather_chunks(P.h, spans_d, spec, stream)
+        assert K.kv_pool_get_error(P.h, stream) == 0
+        host_regions = [None] * (L * KV)
+        for k in range(KV):
+            host_regions[layer * KV + k] = P.t[layer * KV + k].cpu().numpy()
+        got = S.cpu().numpy()
+        parity["gather"] = written_mask_check(0, pool, spans_h, chunks, host_regions, None, got, layer)
+        del got
+        W.device_fill_(S, "bytes", 100 + w["k"])
+        s_host = S.cpu().numpy()
+        K.kv_scatter_chunks(P.h, spans_d, spec, stream)
+        assert K.kv_pool_get_error(P.h, stream) == 0
+        got = [P.t[layer * KV + k].cpu().numpy() for k in range(KV)]
+        parity["scatter"] = written_mask_check(1, pool, spans_h, chunks, host_regions, s_host, got, layer)
+        log("parity (layer %d vs oracle): %s" % (layer, parity))
+        if not all(parity.values()):
+            raise SystemExit("parity check failed: %s" % parity)
+        del got, s_host, host_regions
+
+    def step(n, which=("g", "s")):
+        for _ in range(n):
+            if "g" in which:
+                K.kv_gather_chunks(P.h, spans_d, spec, stream)
+            if "s" in which:
+                K.kv_scatter_chunks(P.h, spans_d, spec, stream)
+
+    step(args.warmup)
+    torch.cuda.synchronize()
+    K.kv_pool_timing_start(P.h)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    step(args.steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms, launches = K.kv_pool_timing_read(P.h)
+    assert K.kv_pool_get_error(P.h, stream) == 0
+    ms_per_step = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+
+    # per-direction breakdown (kernel time only)
+    per_dir = {}
+    for name, which in (("gather", ("g",)), ("scatter", ("s",))):
+        K.kv_pool_timing_start(P.h)
+        step(max(3, args.steps // 2), which)
+        ms, n = K.kv_pool_timing_read(P.h)
+        per_dir[name] = dict(kernel_ms=ms / n, gbs=payload / (ms / n * 1e-3) / 1e9,
+                             hbm_frac=2 * payload / (ms / n * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+    # device-to-device memcpy of the same payload, for context
+    import torch as _t
+    a = S
+    b = _t.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    _t.cuda.synchronize()
+    c0, c1 = _t.cuda.Event(enable_timing=True), _t.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    c1.record(stream)
+    _t.cuda.synchronize()
+    d2d_gbs = a.numel() / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
+    del b
+
+    avg_kernel_s = kern_ms / launches * 1e-3
+    res = dict(
+        payload=payload, ms_per_step=ms_per_step, kernel_ms_avg=kern_ms / launches, launches=launches,
+        value=2 * payload / (ms_per_step * 1e-3) / 1e9,
+        achieved=2 * payload / avg_kernel_s / 1e9, per_dir=per_dir, parity=parity,
+        d2d_copy_gbs=d2d_gbs, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
+        name=args.workload)
+    # keep host copies for the CPU baseline (first layers), then free the device
+    res["host_sample"] = None
+    if args.cpu_baseline:
+        nl = min(L, args.cpu_layers)
+        res["host_sample"] = [P.t[i].cpu().numpy() if i < nl * KV else None for i in range(L * KV)]
+        res["host_sample_layers"] = nl
+    P.close()
+    del P, S, tabs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(res, budget_s):
+    """The oracle, as it is, on the first layers of the same gather."""
+    import numpy as np
+    import oracle
+    w, pool, chunks = res["w"], res["pool"], res["chunks_spec"]
+    regions = res["host_sample"]
+    from paged_layout_transfer_amd import workloads as W
+    spans = [(t, t0, t1, fc) for t, (t0, t1), fc in
+             zip(w["block_tables"], w["requests"], W.staging_plan(w)["first_chunk"])]
+    buf = np.zeros(chunks["slot_bytes"] * chunks["n_slots"], dtype=np.uint8)
+    moved, spent, layers = 0, 0.0, 0
+    for l in range(res["host_sample_layers"]):
+        t0 = time.perf_counter()
+        moved += oracle.gather(pool, regions, spans, chunks, buf, only_layers=(l, l + 1))
+        spent += time.perf_counter() - t0
+        layers += 1
+        if spent >= budget_s:
+            break
+    return dict(value=round(moved / spent / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample="gather of layers 0..%d of the %s workload (%d of %d layers, %.3f GB moved), "
+                       "single-threaded C oracle, %.1f s" % (layers - 1, res["name"], layers,
+                                                            pool["num_layers"], moved / 1e9, spent))
+
+
+def host_leg(args, dev):
+    """Pinned-host path on the 70B-shaped context, streamed through a ring of whole layers."""
+    import numpy as np
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    from paged_layout_transfer_amd import workloads as W
+
+    w, pool = resolve("llama70b")
+    L, KV = pool["num_layers"], pool["num_kv"]
+    tok = W.token_bytes(w)
+    T = w["tokens"]
+    n_tc = -(-T // w["chunk_tokens"])
+    slot = w["chunk_layers"] * KV * w["chunk_tokens"] * tok            # 2 MiB
+    win_layers = args.ring_layers                                       # layers per window
+    n_slots = win_layers * n_tc
+    payload_layer = T * KV * tok
+    P = DevicePool(pool, dev)
+    W.device_fill_(P.t.view(-1), w["fill"], w["k"])
+    tab = torch.from_numpy(w["block_tables"][0]).to(dev)
+    spans_d = K.make_spans([(tab, tab.numel(), 0, T, 0)])
+    ring = K.kv_ring_create(slot, n_slots, K.KV_RING_COHERENT)
+    ring_dev = K.kv_ring_slot(ring, 0)[1]
+    ring_host = K.ring_host_array(ring, slot * n_slots)
+    stream = torch.cuda.current_stream()
+
+    def spec_for(l0, wg=0):
+        return K.make_chunk_spec(K.KV_LAYER_FIRST, w["chunk_layers"], w["chunk_tokens"], l0,
+                                 l0 + win_layers, ring_dev, slot, n_slots, wg, 0)
+
+    parity = {}
+    try:
+        # parity on the first window, layer 0, both directions
+        spans_h = [(w["block_tables"][0], 0, T, 0)]
+        chunks = dict(layout=0, chunk_layers=w["chunk_layers"], chunk_tokens=w["chunk_tokens"],
+                      layer_begin=0, layer_end=win_layers, slot_bytes=slot, n_slots=n_slots)
+        if not args.skip_parity:
+            K.kv_gather_chunks(P.h, spans_d, spec_for(0), stream)
+            assert K.kv_pool_get_error(P.h, stream) == 0
+            regs = [P.t[i].cpu().numpy() if i < KV else None for i in range(L * KV)]
+            parity["gather"] = written_mask_check(0, pool, spans_h, chunks, regs, None, ring_host.copy(), 0)
+            rnd = torch.empty(slot * n_slots, dtype=torch.uint8, device=dev)
+            W.device_fill_(rnd, "bytes", 103)
+            ring_host[:] = rnd.cpu().numpy()
+            del rnd
+            K.kv_scatter_chunks(P.h, spans_d, spec_for(0), stream)
+            assert K.kv_pool_get_error(P.h, stream) == 0
+            got = [P.t[k].cpu().numpy() for k in range(KV)]
+            parity["scatter"] = written_mask_check(1, pool, spans_h, chunks, regs, ring_host.copy(), got, 0)
+            log("host-path parity (layer 0 vs oracle): %s" % parity)
+            if not all(parity.values()):
+                raise SystemExit("host-path parity failed: %s" % parity)
+
+        # link reference: one large hipMemcpy each way between ring memory and HBM
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+        dbuf = torch.empty(slot * n_slots, dtype=torch.uint8, device=dev)
+        host0 = K.kv_ring_slot(ring, 0)[0]
+        link = {}
+        for name, (dst, src, kind) in (("h2d", (dbuf.data_ptr(), host0, 1)),
+                                       ("d2h", (host0, dbuf.data_ptr(), 2))):
+            best = 0.0
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = hip.hipMemcpyAsync(dst, src, slot * n_slots, kind, stream.cuda_stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                assert rc == 0, rc
+                best = max(best, slot * n_slots / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+            link[name] = best
+        del dbuf
+
+        def run_pass(fn, windows, wg=0):
+            K.kv_pool_timing_start(P.h)
+            for i in range(windows):
+                fn(P.h, spans_d, spec_for((i * win_layers) % L, wg), stream)
+            ms, n = K.kv_pool_timing_read(P.h)
+            assert K.kv_pool_get_error(P.h, stream) == 0
+            return ms, n
+
+        windows = L // win_layers if args.host_windows <= 0 else args.host_windows
+        out = {}
+        for name, fn, ref in (("scatter", K.kv_scatter_chunks, "h2d"), ("gather", K.kv_gather_chunks, "d2h")):
+            run_pass(fn, 1)  # warm-up window
+            ms, n = run_pass(fn, windows)
+            moved = payload_layer * win_layers * windows
+            gbs = moved / (ms * 1e-3) / 1e9
+            out[name] = dict(gbs=gbs, link_gbs=link[ref], link_frac=gbs / link[ref],
+                             bytes=moved, kernel_ms=ms, launches=n)
+        sweep = {}
+        if args.sweep:
+            for wg in (1, 2, 4, 8, 16, 32, 0):
+                row = {}
+                for name, fn in (("scatter", K.kv_scatter_chunks), ("gather", K.kv_gather_chunks)):
+                    ms, n = run_pass(fn, 1, wg)
+                    row[name] = payload_layer * win_layers / (ms * 1e-3) / 1e9
+                sweep[str(wg) if wg else "full"] = row
+        return dict(workload="llama70b: 80 layers x K/V x 8 x 128 bf16, 16-token pages, one 131072-token "
+                             "request, 2 MiB chunks (1 layer x 512 tokens) through a pinned host ring of "
+                             "%d slots (%d layers per window)" % (n_slots, win_layers),
+                    payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep, **out)
+    finally:
+        K.kv_ring_destroy(ring)
+        P.close()
+        del P
+        torch.cuda.empty_cache()
+
+
+def traffic_for(achieved_bytes_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--max-workgroups", type=int, default=0)
+    ap.add_argument("--skip-parity", action="store_true")
+    ap.add_argument("--no-host-path", dest="host_path", action="store_false")
+    ap.add_argument("--host-windows", type=int, default=0, help="0 = the whole 80-layer context")
+    ap.add_argument("--ring-layers", type=int, default=4, help="layers per ring window")
+    ap.add_argument("--sweep", action="store_true", help="sweep max_workgroups on the host path")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path has no cross-GPU step (each GPU would move "
+              "its own pool shard over its own HBM and host link); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
+    from paged_layout_transfer_amd import kvxfer  # noqa: F401  (fails loudly if not built)
+    dev = torch.device("cuda", 0)
+
+    res = hbm_leg(args, dev)
+    log("hbm leg: %.1f GB/s moved, kernel avg %.3f ms, %.1f%% of HBM peak" % (
+        res["value"], res["kernel_ms_avg"], 100 * res["achieved"] / HBM_PEAK_GBS))
+    cpu = cpu_baseline(res, args.cpu_budget) if args.cpu_baseline else None
+    res.pop("host_sample", None)
+    host = host_leg(args, dev) if args.host_path else None
+
+    w = res["w"]
+    traffic = traffic_for(2 * res["payload"])
+    out = {
+        "metric": METRIC,
+        "value": round(res["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama8b: 32 layers x K/V x 8 heads x 128 dims bf16, 16-token pages (32 KiB "
+                        "per layer-page), 16384-block pool, one 32768-token request with a shuffled "
+                        "block table, 256-token layer-first chunks in HBM; step = gather + scatter",
+            "global_batch": 1, "seq_len": w["tokens"], "parallelism": "none",
+            "payload_bytes_each_way": res["payload"], "tiles_per_launch": res["tiles"],
+            "chunks": res["chunks"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(res["achieved"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "kvx::tile_copy (gather and scatter, layer-first), %d launches averaged" % res["launches"],
+        },
+        "cpu_baseline": cpu,
+        "breakdown": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res["per_dir"].items()},
+        "d2d_memcpy_gbs": round(res["d2d_copy_gbs"], 1),
+        "parity": res["parity"],
+        "host_path": host,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

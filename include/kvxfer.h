@@ -1,0 +1,266 @@
+/*
+ * kvxfer.h -- paged KV-cache gather/scatter for AMD Instinct MI355X (gfx950).
+ *
+ * The library moves a request's KV pages between a paged pool (per-layer K/V
+ * regions addressed through a block table) and large contiguous transfer
+ * chunks, in either direction, with one kernel launch per call:
+ *
+ *   gather  (offload): pool pages  -> chunks   (Strata guide, "Implementation"
+ *                      lifecycle figure, step 6: background eviction of cold
+ *                      pages to host memory with a one-block kernel)
+ *   scatter (reload) : chunks      -> pool pages (same figure, step 3, and
+ *                      "Step 1: High-Performance GPU-Assisted I/O CUDA Kernel")
+ *
+ * Chunks may sit in HBM or in pinned host memory that the kernel reads and
+ * writes directly with ordinary loads and stores, instead of one DMA per page
+ * (Strata guide, "The Mechanics of GPU-Assisted I/O").  The layout change
+ * between the pool (layer-first) and the chunk (layer-first or page-first) is
+ * done by address arithmetic during the copy (Strata guide, "Two-Dimensional
+ * Memory Layout Decoupling").  Host work per call is proportional to the number
+ * of spans, not to pages x layers (Tutti summary, Q2 "Design 1": CPU work drops
+ * from O(layer x blocks) to O(layer)).
+ *
+ * ---------------------------------------------------------------------------
+ * Data model
+ * ---------------------------------------------------------------------------
+ * Pool.  For layer l < num_layers and kv < num_kv (2 = K and V, 1 = a single
+ * latent) the caller provides one device region, bases[l*num_kv + kv].  Block
+ * b of that region starts at bases[l*num_kv+kv] + b*block_stride and holds
+ * block_size tokens, token-major, each token num_heads x head_dim elements of
+ * elem_bytes bytes: tok = num_heads*head_dim*elem_bytes bytes per token.  One
+ * block id names the same page in every (layer, kv) region.  K and V are
+ * separate objects per layer, as in the Tutti summary's Figure 4 (2L objects
+ * per block).  block_stride >= block_size*tok; block_stride == block_size*tok
+ * gives a vLLM-style [num_blocks][block_size][H][D] region, block_stride ==
+ * num_kv*block_size*tok with bases offset by kv*block_size*tok gives a per-layer
+ * [num_blocks][num_kv][block_size][H][D] pool.
+ *
+ * Span.  (block_table, t_begin, t_end, first_chunk): tokens [t_begin, t_end)
+ * of one request, whose token t lives at slot t % block_size of block
+ * block_table[t / block_size].  t_begin must be a multiple of block_size
+ * (prefix matches end on page boundaries: Strata guide, "The Conflict Between
+ * PagedAttention and Transfer Efficiency"); t_end is arbitrary, so the last
+ * page may be partial.
+ *
+ * Chunks.  A call moves layers [layer_begin, layer_end).  Each span splits into
+ * chunks of chunk_layers layers x chunk_tokens tokens, layer-chunk major:
+ *     c = first_chunk + lc*n_tc + tc,  lc = (l - layer_begin) / chunk_layers,
+ *     tc = (t - t_begin) / chunk_tokens,  n_tc = ceil((t_end - t_begin) / chunk_tokens)
+ * and chunk c occupies slot (c mod n_slots), at base + (c mod n_slots)*slot_bytes.
+ * With li = (l - layer_begin) % chunk_layers, a chunk is laid out as
+ *     KV_LAYER_FIRST: [chunk_layers][num_kv][T_c][H][D], T_c = tokens in the
+ *                     chunk (the span's last chunk may be short, and is dense)
+ *     KV_PAGE_FIRST : [P_c][chunk_layers][num_kv][block_size][H][D], P_c = pages
+ *                     in the chunk; a partial last page leaves pad bytes that
+ *                     are neither written (gather) nor read (scatter).
+ * The page-first order is the Strata guide's host-side [P, L, H, D] tensor
+ * ("Two-Dimensional Memory Layout Decoupling", item 2); layer-first matches its
+ * HBM-side [L, P, H, D] tensor (item 1).
+ *
+ * Nothing outside the referenced pool tokens and the chunk bytes is written.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ * ---------------------------------------------------------------------------
+ * Every function returns KV_OK (0) or a negative KV_ERR_* code; no exception
+ * crosses the ABI.  A call that returns an error has launched nothing and
+ * changed no state.
+ * Pointers named "device" must be valid on the device current when the call
+ * is made (HBM, or mapped pinned host memory from kv_ring_create / hipHostMalloc).
+ * All device and chunk pointers, block_stride, slot_bytes and tok must be
+ * multiples of 16 bytes (16-byte vector loads and stores).
+ * Transfers are asynchronous on the given stream (0 = the null stream): the
+ * caller keeps every buffer alive and unmodified until the stream has passed
+ * the call.  Handles are not thread-safe.
+ */
+#ifndef KVXFER_H
+#define KVXFER_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_API __attribute__((visibility("default")))
+
+/* ---- error codes ------------------------------------------------------- */
+#define KV_OK 0
+#define KV_ERR_ARG (-1)    /* null pointer, bad shape, empty or inverted range */
+#define KV_ERR_ALIGN (-2)  /* pointer, stride, slot size or token size not a multiple of 16 */
+#define KV_ERR_RANGE (-3)  /* span past its block table, slot too small, block id out of range */
+#define KV_ERR_OOM (-4)    /* allocator exhausted, or a host/device allocation failed */
+#define KV_ERR_RING (-5)   /* two chunks of one call share a staging slot */
+#define KV_ERR_HIP (-6)    /* a HIP runtime call failed (no device, launch failure, ...) */
+#define KV_ERR_DEVICE (-7) /* kv_pool_get_error: the device reported a bad block id */
+#define KV_ERR_DUP (-8)    /* KV_FLAG_VALIDATE: a scatter writes one pool page twice */
+
+/* ---- chunk layouts, directions, flags ---------------------------------- */
+#define KV_LAYER_FIRST 0
+#define KV_PAGE_FIRST 1
+
+#define KV_GATHER 0  /* pool -> chunks (offload) */
+#define KV_SCATTER 1 /* chunks -> pool (reload)  */
+
+/* kv_chunk_spec.flags */
+#define KV_FLAG_VALIDATE 0x1 /* copy the block tables to the host (synchronously) and check
+                                ids in range and, for scatter, one writer per pool page */
+
+/* device error bits reported through kv_pool_get_error */
+#define KV_DEVERR_BLOCK_RANGE 0x1 /* a block table held an id outside [0, num_blocks); that
+                                     (layer, kv, page) tile was skipped */
+
+/* kv_ring_create flags */
+#define KV_RING_COHERENT 0x0     /* hipHostMalloc coherent mapped memory (default) */
+#define KV_RING_NONCOHERENT 0x1  /* hipHostMallocNonCoherent: the GPU may cache it */
+
+/* Limits of one call. */
+#define KV_MAX_SPANS 4096
+
+typedef struct kv_pool kv_pool; /* opaque, owned by the library */
+typedef struct kv_ring kv_ring; /* opaque, owned by the library */
+
+typedef struct {
+    int32_t num_layers;   /* L >= 1 */
+    int32_t num_kv;       /* 1 or 2 */
+    int32_t num_heads;    /* H >= 1 */
+    int32_t head_dim;     /* D >= 1 */
+    int32_t elem_bytes;   /* 1, 2, 4 or 8 (the payload is moved as opaque bytes) */
+    int32_t block_size;   /* tokens per page, >= 1 */
+    int64_t num_blocks;   /* blocks per (layer, kv) region, 1 .. 2^31-1 */
+    int64_t block_stride; /* bytes between consecutive blocks of one region */
+    void *const *bases;   /* host array of num_layers*num_kv device pointers; the
+                             library copies it, the regions stay caller-owned */
+} kv_pool_desc;
+
+typedef struct {
+    const int32_t *block_table; /* device array (host array for kv_validate_targets) */
+    int64_t table_len;          /* entries in block_table; >= ceil(t_end / block_size) */
+    int64_t t_begin;            /* first token, a multiple of block_size, >= 0 */
+    int64_t t_end;              /* one past the last token, >= t_begin (an empty span moves nothing) */
+    int64_t first_chunk;        /* chunk index of the span's first chunk, >= 0 */
+} kv_span;
+
+typedef struct {
+    int32_t layout;        /* KV_LAYER_FIRST or KV_PAGE_FIRST */
+    int32_t chunk_layers;  /* CL, divides layer_end - layer_begin */
+    int64_t chunk_tokens;  /* CT, a multiple of block_size */
+    int32_t layer_begin;   /* first layer moved */
+    int32_t layer_end;     /* one past the last layer moved (<= num_layers) */
+    void *base;            /* device-visible staging: HBM or mapped pinned host memory */
+    int64_t slot_bytes;    /* bytes per staging slot, >= the largest chunk of the call */
+    int64_t n_slots;       /* slots at base; chunk c uses slot c mod n_slots */
+    int32_t max_workgroups;/* 0 = library default grid; > 0 caps the grid to that many
+                              workgroups (host-link paths need few: Strata guide,
+                              "Non-Intrusive Resource Sizing") */
+    int32_t flags;         /* KV_FLAG_* */
+} kv_chunk_spec;
+
+/* Sizes of one call, as kv_check_transfer reports them. */
+typedef struct {
+    int64_t tiles;          /* (layer, kv, page) tiles the kernel copies */
+    int64_t chunks;         /* chunks the call touches */
+    int64_t payload_bytes;  /* bytes copied (each read once and written once) */
+    int64_t max_chunk_bytes;/* largest chunk of the call */
+} kv_transfer_info;
+
+/* ---- pool ------------------------------------------------------------------ */
+
+/* Validates desc and creates a pool handle with a host free list of all
+ * num_blocks ids.  Device-side state (a descriptor buffer, an error word) is
+ * created on the first transfer, on the device current then; later transfers
+ * must run with the same device current.  Errors: KV_ERR_ARG, KV_ERR_ALIGN
+ * (a base or block_stride not 16-byte aligned), KV_ERR_OOM. */
+KV_API int kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
+
+/* Frees the handle and its device state (after synchronizing the device work it
+ * issued).  The caller's regions are untouched.  NULL is accepted. */
+KV_API int kv_pool_destroy(kv_pool *pool);
+
+/* Block allocator (host free list, preallocated at create time, no allocation on
+ * the call path: Tutti summary, "Key implementation details", item 1).
+ * alloc: writes n distinct free ids to out_ids, or fails with KV_ERR_OOM and
+ * allocates nothing.  free: ids must be currently allocated and distinct, else
+ * KV_ERR_RANGE and nothing is freed. */
+KV_API int kv_pool_alloc_blocks(kv_pool *pool, int32_t n, int32_t *out_ids);
+KV_API int kv_pool_free_blocks(kv_pool *pool, int32_t n, const int32_t *ids);
+KV_API int kv_pool_free_count(const kv_pool *pool, int64_t *out);
+
+/* ---- calls -------------------------------------------------------------------- */
+
+/* Host-only dry run: validates a prospective call exactly as kv_gather_chunks /
+ * kv_scatter_chunks do (shapes, alignment, span ranges, slot sizes, one slot per
+ * chunk) and reports its sizes.  Makes no HIP call; info may be NULL. */
+KV_API int kv_check_transfer(const kv_pool_desc *desc, const kv_span *spans, int32_t n_spans,
+                      const kv_chunk_spec *spec, kv_transfer_info *info);
+
+/* Bytes of a chunk holding `tokens` tokens (1 <= tokens <= chunk_tokens) in the
+ * spec's layout. */
+KV_API int kv_chunk_bytes(const kv_pool_desc *desc, const kv_chunk_spec *spec, int64_t tokens,
+                   int64_t *out);
+
+/* Host-side check of the block tables of a call, given host copies of them
+ * (host_tables[i] holds spans[i].table_len ids): every id of every referenced
+ * page lies in [0, num_blocks) (else KV_ERR_RANGE) and, for KV_SCATTER, no pool
+ * page receives two writers (else KV_ERR_DUP).  Gather may read a page twice. */
+KV_API int kv_validate_targets(const kv_pool_desc *desc, const kv_span *spans, int32_t n_spans,
+                        const int32_t *const *host_tables, int32_t direction);
+
+/* Gather (offload): for every span, layer in [layer_begin, layer_end), kv and
+ * token, copies the pool token into its chunk position.  One kernel launch on
+ * `stream`, preceded by one small stream-ordered descriptor upload.  spans is a
+ * host array of n_spans (1 .. KV_MAX_SPANS) entries; each block_table is a
+ * device pointer.  n_spans == 0, or spans that are all empty, is a no-op.  Loads
+ * and stores are nontemporal.  Returns after enqueueing. */
+KV_API int kv_gather_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                     const kv_chunk_spec *spec, hipStream_t stream);
+
+/* Scatter (reload): the inverse move, chunk positions -> pool tokens.  The
+ * spans of one call must not write one pool page twice (checked only with
+ * KV_FLAG_VALIDATE); then every written byte has exactly one writer. */
+KV_API int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                      const kv_chunk_spec *spec, hipStream_t stream);
+
+/* Synchronizes `stream`, then reads and clears the pool's sticky device error
+ * word.  *out_bits receives KV_DEVERR_* bits (0 if none); the return value is
+ * KV_ERR_DEVICE when any bit was set, else KV_OK. */
+KV_API int kv_pool_get_error(kv_pool *pool, hipStream_t stream, int32_t *out_bits);
+
+/* Kernel timing.  After kv_pool_timing_start, every transfer records a HIP
+ * event pair around its kernel launch on its stream (up to 4096 launches).
+ * kv_pool_timing_read synchronizes those events, writes the summed kernel time
+ * in milliseconds and the number of launches timed, and stops timing. */
+KV_API int kv_pool_timing_start(kv_pool *pool);
+KV_API int kv_pool_timing_read(kv_pool *pool, double *total_ms, int64_t *launches);
+
+/* ---- pinned-host staging ring ------------------------------------------------ */
+
+/* Allocates and pins n_slots*slot_bytes bytes of host memory once, mapped into
+ * the device address space of the current device (hipHostMalloc; pinning is done
+ * up front, never on the transfer path: Strata guide, "Production Cluster Sizing
+ * and Configuration Guidelines", item 2).  slot_bytes must be a multiple of 16.
+ * The memory is zero-filled.  Use kv_ring_slot's device pointer as
+ * kv_chunk_spec.base. */
+KV_API int kv_ring_create(int64_t slot_bytes, int64_t n_slots, int32_t flags, kv_ring **out);
+
+/* Host and device addresses of slot i (0 <= i < n_slots); either out may be NULL. */
+KV_API int kv_ring_slot(const kv_ring *ring, int64_t i, void **host_ptr, void **dev_ptr);
+
+/* Frees the pinned memory; the caller must have synchronized every transfer
+ * that uses it.  NULL is accepted. */
+KV_API int kv_ring_destroy(kv_ring *ring);
+
+/* ---- misc ------------------------------------------------------------------------ */
+
+/* Static description of a KV_* return code. */
+KV_API const char *kv_strerror(int code);
+
+/* Library version: major*10000 + minor*100 + patch. */
+KV_API int kv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVXFER_H */

@@ -85,8 +85,9 @@ def transfer(direction: int, pool: dict, regions, spans, chunks: dict, chunk_buf
     pool     : dict with num_layers, num_kv, num_heads, head_dim, elem_bytes,
                block_size, num_blocks, block_stride
     regions  : sequence of L*KV writable uint8 numpy arrays (one per (layer, kv),
-               index l*KV+kv), each at least num_blocks*block_stride bytes, or a
-               2-D uint8 array whose rows are the regions
+               index l*KV+kv), each covering every block it addresses, or a
+               2-D uint8 array whose rows are the regions; with only_layers, the
+               entries of layers outside that range may be None
     spans    : sequence of (int32 block table, t_begin, t_end, first_chunk)
     chunks   : dict with layout, chunk_layers, chunk_tokens, layer_begin,
                layer_end, slot_bytes, n_slots
@@ -99,11 +100,14 @@ def transfer(direction: int, pool: dict, regions, spans, chunks: dict, chunk_buf
     nreg = p.num_layers * p.num_kv
     if len(regions) != nreg:
         raise ValueError("need one region per (layer, kv)")
-    need = p.num_blocks * p.block_stride
+    need = (p.num_blocks - 1) * p.block_stride + p.block_size * p.num_heads * p.head_dim * p.elem_bytes
+    l0, l1 = only_layers if only_layers is not None else (0, p.num_layers)
     ptrs = (ctypes.c_void_p * nreg)()
     for i in range(nreg):
         r = regions[i]
-        if r.dtype != np.uint8 or not r.flags.c_contiguous or r.size < need:
+        if r is None and not (l0 <= i // p.num_kv < l1):
+            continue  # a layer outside the evaluated range is never touched
+        if r is None or r.dtype != np.uint8 or not r.flags.c_contiguous or r.size < need:
             raise ValueError("region %d must be a contiguous uint8 array of >= %d bytes" % (i, need))
         ptrs[i] = r.ctypes.data
     if chunk_buf.dtype != np.uint8 or not chunk_buf.flags.c_contiguous:
@@ -118,7 +122,6 @@ def transfer(direction: int, pool: dict, regions, spans, chunks: dict, chunk_buf
             raise ValueError("span %d: block table shorter than ceil(t_end/block_size)" % i)
         tables.append(tbl)
         sp[i] = _Span(tbl.ctypes.data, int(t0), int(t1), int(fc))
-    l0, l1 = only_layers if only_layers is not None else (0, p.num_layers)
     n = lib.orc_transfer(int(direction), ctypes.byref(p), ptrs, sp, len(spans), ctypes.byref(c),
                          chunk_buf.ctypes.data, int(l0), int(l1))
     if n < 0:

@@ -25,8 +25,9 @@
  *   Tutti summary, "Memory management").
  *
  *   Spans and chunks. A span is (table, t_begin, t_end, first_chunk) with
- *   t_begin on a page boundary (prefix matches end at page boundaries, Strata
- *   guide, "The Conflict Between PagedAttention and Transfer Efficiency").  The
+ *   t_begin <= t_end (an empty span moves nothing) and t_begin on a page
+ *   boundary (prefix matches end at page boundaries, Strata guide, "The
+ *   Conflict Between PagedAttention and Transfer Efficiency").  The
  *   call moves layers [layer_begin, layer_end).  A span splits into chunks of
  *   chunk_layers layers x chunk_tokens tokens, layer-chunk major:
  *       c = first_chunk + lc*n_tc + tc,  lc = (l-layer_begin)/CL,
@@ -116,7 +117,7 @@ int64_t orc_transfer(int dir, const orc_pool *P, uint8_t *const *bases, const or
 
     for (int64_t r = 0; r < n_spans; ++r) {
         const orc_span *S = &spans[r];
-        if (S->t_begin < 0 || S->t_end <= S->t_begin || S->t_begin % bs != 0) return -1;
+        if (S->t_begin < 0 || S->t_end < S->t_begin || S->t_begin % bs != 0) return -1;
         const int64_t n_tc = ceil_div(S->t_end - S->t_begin, CT);
 
         for (int64_t l = C->layer_begin; l < C->layer_end; ++l) {

@@ -1,0 +1,640 @@
+// kvxfer.cpp -- host side of the paged-KV transfer library: validation, call
+// decomposition into tiles, the block allocator, the pinned staging ring and
+// the launch.  The exported functions are declared and documented in
+// include/kvxfer.h.
+//
+// Host work per call is O(n_spans): one descriptor record per span, one small
+// stream-ordered upload and one kernel launch, however many pages and layers the
+// call moves (the Tutti summary, Q2 "Design 1", cuts CPU work per transfer from
+// O(layer x blocks) to O(layer); the Strata guide, "The Mechanics of
+// GPU-Assisted I/O", replaces one DMA submission per page with one kernel).
+#include "kvxfer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kvxfer_internal.h"
+
+namespace {
+
+constexpr int kDescSlots = 4;           // descriptor upload buffers in flight per pool
+constexpr int kMaxTimed = 4096;         // launches one timing window can record
+constexpr int64_t kMaxU31 = 0x7fffffffLL;
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct SlotRange {
+    int64_t start;  // first slot
+    int64_t count;  // chunks
+};
+
+// Per-span figures of a validated call.
+struct SpanPlan {
+    int64_t n_pages, ppc, n_tc, n_chunks, tiles;
+};
+
+int check_desc(const kv_pool_desc *d)
+{
+    if (!d || !d->bases) return KV_ERR_ARG;
+    if (d->num_layers < 1 || d->num_kv < 1 || d->num_kv > 2 || d->num_heads < 1 ||
+        d->head_dim < 1 || d->block_size < 1)
+        return KV_ERR_ARG;
+    if (d->elem_bytes != 1 && d->elem_bytes != 2 && d->elem_bytes != 4 && d->elem_bytes != 8)
+        return KV_ERR_ARG;
+    if (d->num_blocks < 1 || d->num_blocks > kMaxU31) return KV_ERR_ARG;
+    const int64_t tok = (int64_t)d->num_heads * d->head_dim * d->elem_bytes;
+    if (tok > kMaxU31 || tok * d->block_size > kMaxU31) return KV_ERR_ARG;
+    if (tok % 16 != 0) return KV_ERR_ALIGN;
+    const int64_t tile = tok * d->block_size;
+    if (d->block_stride < tile) return KV_ERR_ARG;
+    if (d->block_stride % 16 != 0) return KV_ERR_ALIGN;
+    if (d->block_stride > INT64_MAX / d->num_blocks) return KV_ERR_ARG;
+    const int64_t n = (int64_t)d->num_layers * d->num_kv;
+    if (n > kMaxU31) return KV_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!d->bases[i]) return KV_ERR_ARG;
+        if (!aligned16(d->bases[i])) return KV_ERR_ALIGN;
+    }
+    return KV_OK;
+}
+
+int64_t tok_bytes(const kv_pool_desc *d)
+{
+    return (int64_t)d->num_heads * d->head_dim * d->elem_bytes;
+}
+
+int check_spec(const kv_pool_desc *d, const kv_chunk_spec *s)
+{
+    if (!s) return KV_ERR_ARG;
+    if (s->layout != KV_LAYER_FIRST && s->layout != KV_PAGE_FIRST) return KV_ERR_ARG;
+    if (s->layer_begin < 0 || s->layer_end > d->num_layers || s->layer_end <= s->layer_begin)
+        return KV_ERR_ARG;
+    if (s->chunk_layers < 1 || (s->layer_end - s->layer_begin) % s->chunk_layers != 0)
+        return KV_ERR_ARG;
+    if (s->chunk_tokens < d->block_size || s->chunk_tokens % d->block_size != 0) return KV_ERR_ARG;
+    if (!s->base) return KV_ERR_ARG;
+    if (!aligned16(s->base)) return KV_ERR_ALIGN;
+    if (s->slot_bytes <= 0 || s->n_slots <= 0) return KV_ERR_ARG;
+    if (s->slot_bytes % 16 != 0) return KV_ERR_ALIGN;
+    if (s->n_slots > INT64_MAX / s->slot_bytes) return KV_ERR_ARG;
+    if (s->max_workgroups < 0) return KV_ERR_ARG;
+    if (s->flags & ~KV_FLAG_VALIDATE) return KV_ERR_ARG;
+    return KV_OK;
+}
+
+int64_t chunk_bytes_for(const kv_pool_desc *d, const kv_chunk_spec *s, int64_t tokens)
+{
+    const int64_t tok = tok_bytes(d);
+    if (s->layout == KV_LAYER_FIRST) return (int64_t)s->chunk_layers * d->num_kv * tokens * tok;
+    return cdiv(tokens, d->block_size) * s->chunk_layers * d->num_kv * d->block_size * tok;
+}
+
+// Full validation of a call.  plans (n_spans entries) and ranges (n_spans entries)
+// are caller-provided scratch so the transfer path allocates nothing.
+int validate_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
+                  const kv_chunk_spec *s, kv_transfer_info *info, SpanPlan *plans,
+                  SlotRange *ranges)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    rc = check_spec(d, s);
+    if (rc) return rc;
+    if (n_spans < 0 || n_spans > KV_MAX_SPANS) return KV_ERR_ARG;
+    if (n_spans > 0 && !spans) return KV_ERR_ARG;
+
+    const int64_t bs = d->block_size;
+    const int64_t layers = s->layer_end - s->layer_begin;
+    const int64_t n_lc = layers / s->chunk_layers;
+    kv_transfer_info acc{0, 0, 0, 0};
+    int n_ranges = 0;
+    for (int32_t i = 0; i < n_spans; ++i) {
+        const kv_span &sp = spans[i];
+        if (sp.t_begin < 0 || sp.t_end < sp.t_begin || sp.t_begin % bs != 0) return KV_ERR_ARG;
+        if (sp.first_chunk < 0) return KV_ERR_ARG;
+        SpanPlan &p = plans[i];
+        const int64_t len = sp.t_end - sp.t_begin;
+        if (len == 0) {
+            p = SpanPlan{0, 0, 0, 0, 0};
+            continue;
+        }
+        if (!sp.block_table) return KV_ERR_ARG;
+        if (sp.t_end / bs >= kMaxU31) return KV_ERR_RANGE;
+        if (sp.table_len < cdiv(sp.t_end, bs)) return KV_ERR_RANGE;
+        p.n_pages = cdiv(len, bs);
+        p.ppc = std::min<int64_t>(s->chunk_tokens / bs, p.n_pages);
+        p.n_tc = cdiv(p.n_pages, p.ppc);
+        p.n_chunks = n_lc * p.n_tc;
+        p.tiles = layers * d->num_kv * p.n_pages;
+        if (p.tiles > kMaxU31) return KV_ERR_RANGE;
+        if (sp.first_chunk > INT64_MAX - p.n_chunks) return KV_ERR_ARG;
+        const int64_t first_chunk_tokens = std::min(len, p.ppc * bs);
+        const int64_t cb = chunk_bytes_for(d, s, first_chunk_tokens);
+        if (cb > s->slot_bytes) return KV_ERR_RANGE;
+        acc.max_chunk_bytes = std::max(acc.max_chunk_bytes, cb);
+        acc.tiles += p.tiles;
+        acc.chunks += p.n_chunks;
+        acc.payload_bytes += layers * d->num_kv * len * tok_bytes(d);
+        ranges[n_ranges++] = SlotRange{sp.first_chunk % s->n_slots, p.n_chunks};
+    }
+    // Every chunk of the call owns its slot: the chunk ranges, taken mod n_slots,
+    // must be disjoint arcs of the ring.
+    if (acc.chunks > s->n_slots) return KV_ERR_RING;
+    std::sort(ranges, ranges + n_ranges,
+              [](const SlotRange &a, const SlotRange &b) { return a.start < b.start; });
+    for (int i = 0; i + 1 < n_ranges; ++i)
+        if (ranges[i].start + ranges[i].count > ranges[i + 1].start) return KV_ERR_RING;
+    if (n_ranges > 1 &&
+        ranges[n_ranges - 1].start + ranges[n_ranges - 1].count > ranges[0].start + s->n_slots)
+        return KV_ERR_RING;
+    if (info) *info = acc;
+    return KV_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Validation plus launch-record construction, with caller-provided scratch.
+int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
+                 const kv_chunk_spec *spec, kvx::SpanDev *records, uint32_t *n_records,
+                 kvx::Launch *a, kv_transfer_info *info, SpanPlan *plans, SlotRange *ranges)
+{
+    kv_transfer_info inf;
+    int rc = validate_call(d, spans, n_spans, spec, &inf, plans, ranges);
+    if (rc) return rc;
+    uint32_t n = 0;
+    int64_t tile_begin = 0;
+    for (int32_t i = 0; i < n_spans; ++i) {
+        const SpanPlan &pl = plans[i];
+        if (pl.tiles == 0) continue;
+        kvx::SpanDev r{};
+        r.table = spans[i].block_table;
+        r.tile_begin = tile_begin;
+        r.t_end = spans[i].t_end;
+        r.slot0 = spans[i].first_chunk % spec->n_slots;
+        r.first_page = (uint32_t)(spans[i].t_begin / d->block_size);
+        r.n_pages = (uint32_t)pl.n_pages;
+        r.ppc = (uint32_t)pl.ppc;
+        r.n_tc = (uint32_t)pl.n_tc;
+        r.per_lc = (uint32_t)((int64_t)spec->chunk_layers * d->num_kv * pl.n_pages);
+        r.per_tc = (uint32_t)((int64_t)spec->chunk_layers * d->num_kv * pl.ppc);
+        records[n++] = r;
+        tile_begin += pl.tiles;
+    }
+    *n_records = n;
+    *a = kvx::Launch{};
+    a->chunk_base = static_cast<uint8_t *>(spec->base);
+    a->total_tiles = inf.tiles;
+    a->block_stride = d->block_stride;
+    a->slot_bytes = spec->slot_bytes;
+    a->n_slots = spec->n_slots;
+    a->tile_bytes = tok_bytes(d) * d->block_size;
+    a->num_blocks = (uint32_t)d->num_blocks;
+    a->n_spans = n;
+    a->num_kv = (uint32_t)d->num_kv;
+    a->chunk_layers = (uint32_t)spec->chunk_layers;
+    a->layer_begin = (uint32_t)spec->layer_begin;
+    a->tok = (uint32_t)tok_bytes(d);
+    a->block_size = (uint32_t)d->block_size;
+    a->layout = (uint32_t)spec->layout;
+    if (info) *info = inf;
+    return KV_OK;
+}
+
+}  // namespace
+
+namespace kvx {
+
+int prepare_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
+                 const kv_chunk_spec *spec, SpanDev *records, uint32_t *n_records, Launch *launch,
+                 kv_transfer_info *info)
+{
+    if (n_spans < 0 || n_spans > KV_MAX_SPANS || !records || !n_records || !launch)
+        return KV_ERR_ARG;
+    try {
+        std::vector<SpanPlan> plans(std::max(1, (int)n_spans));
+        std::vector<SlotRange> ranges(std::max(1, (int)n_spans));
+        return prepare_with(d, spans, n_spans, spec, records, n_records, launch, info,
+                            plans.data(), ranges.data());
+    } catch (...) {
+        return KV_ERR_OOM;
+    }
+}
+
+}  // namespace kvx
+
+struct kv_pool {
+    kv_pool_desc desc;
+    std::vector<void *> bases;
+    // allocator: LIFO stack of free ids plus an allocated bitmap
+    std::vector<int32_t> free_ids;
+    std::vector<uint8_t> allocated;
+    // validation scratch (no allocation on the call path)
+    std::vector<SpanPlan> plans;
+    std::vector<SlotRange> ranges;
+    // device state, created on the first transfer
+    int device = -1;
+    uint8_t **d_regions = nullptr;
+    int32_t *d_err = nullptr;
+    kvx::SpanDev *d_desc = nullptr;   // kDescSlots x KV_MAX_SPANS records
+    kvx::SpanDev *h_desc = nullptr;   // pinned host mirror
+    hipEvent_t desc_ev[kDescSlots] = {};
+    int desc_next = 0;
+    // timing
+    bool timing = false;
+    int n_timed = 0;
+    std::vector<hipEvent_t> t_ev;
+};
+
+struct kv_ring {
+    void *host = nullptr;
+    void *dev = nullptr;
+    int64_t slot_bytes = 0, n_slots = 0;
+};
+
+namespace {
+
+void free_device_state(kv_pool *p)
+{
+    for (int i = 0; i < kDescSlots; ++i)
+        if (p->desc_ev[i]) (void)hipEventDestroy(p->desc_ev[i]), p->desc_ev[i] = nullptr;
+    if (p->h_desc) (void)hipHostFree(p->h_desc), p->h_desc = nullptr;
+    if (p->d_desc) (void)hipFree(p->d_desc), p->d_desc = nullptr;
+    if (p->d_err) (void)hipFree(p->d_err), p->d_err = nullptr;
+    if (p->d_regions) (void)hipFree(p->d_regions), p->d_regions = nullptr;
+    p->device = -1;
+}
+
+int device_setup(kv_pool *p)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KV_ERR_HIP;
+    if (p->device >= 0) return dev == p->device ? KV_OK : KV_ERR_ARG;
+    const int64_t n = (int64_t)p->desc.num_layers * p->desc.num_kv;
+    const size_t desc_bytes = sizeof(kvx::SpanDev) * KV_MAX_SPANS * kDescSlots;
+    if (hipMalloc(&p->d_regions, n * sizeof(void *)) != hipSuccess) goto fail;
+    if (hipMemcpy(p->d_regions, p->bases.data(), n * sizeof(void *), hipMemcpyHostToDevice) !=
+        hipSuccess)
+        goto fail;
+    if (hipMalloc(&p->d_err, sizeof(int32_t)) != hipSuccess) goto fail;
+    if (hipMemset(p->d_err, 0, sizeof(int32_t)) != hipSuccess) goto fail;
+    if (hipMalloc(&p->d_desc, desc_bytes) != hipSuccess) goto fail;
+    if (hipHostMalloc((void **)&p->h_desc, desc_bytes, hipHostMallocDefault) != hipSuccess) goto fail;
+    for (int i = 0; i < kDescSlots; ++i)
+        if (hipEventCreateWithFlags(&p->desc_ev[i], hipEventDisableTiming) != hipSuccess) goto fail;
+    p->device = dev;
+    return KV_OK;
+fail:
+    (void)hipGetLastError();
+    free_device_state(p);
+    return KV_ERR_HIP;
+}
+
+void device_teardown(kv_pool *p)
+{
+    if (p->device >= 0) (void)hipDeviceSynchronize();
+    free_device_state(p);
+    for (hipEvent_t &e : p->t_ev)
+        if (e) (void)hipEventDestroy(e), e = nullptr;
+}
+
+int validate_tables(kv_pool *p, const kv_span *spans, int32_t n_spans, int direction,
+                    hipStream_t stream)
+{
+    // Host copies of the device tables (debug path; synchronous by design).
+    if (hipStreamSynchronize(stream) != hipSuccess) return KV_ERR_HIP;
+    std::vector<std::vector<int32_t>> host(n_spans);
+    std::vector<const int32_t *> ptrs(n_spans, nullptr);
+    for (int32_t i = 0; i < n_spans; ++i) {
+        if (spans[i].t_end == spans[i].t_begin) continue;
+        const int64_t n = cdiv(spans[i].t_end, p->desc.block_size);
+        host[i].resize(n);
+        if (hipMemcpy(host[i].data(), spans[i].block_table, n * sizeof(int32_t),
+                      hipMemcpyDeviceToHost) != hipSuccess)
+            return KV_ERR_HIP;
+        ptrs[i] = host[i].data();
+    }
+    std::vector<kv_span> local(spans, spans + n_spans);
+    for (int32_t i = 0; i < n_spans; ++i)
+        local[i].table_len = (int64_t)host[i].size();
+    return kv_validate_targets(&p->desc, local.data(), n_spans, ptrs.data(), direction);
+}
+
+int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
+             hipStream_t stream, int direction)
+{
+    if (!p) return KV_ERR_ARG;
+    // Validate first: a rejected call makes no HIP call at all.
+    kv_transfer_info info;
+    int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
+    if (rc) return rc;
+    if (info.tiles == 0) return KV_OK;
+    rc = device_setup(p);
+    if (rc) return rc;
+    if (spec->flags & KV_FLAG_VALIDATE) {
+        rc = validate_tables(p, spans, n_spans, direction, stream);
+        if (rc) return rc;
+    }
+
+    // Span records go to a pinned host buffer whose previous upload has finished,
+    // then one stream-ordered copy to the matching device buffer.
+    const int slot = p->desc_next;
+    p->desc_next = (p->desc_next + 1) % kDescSlots;
+    if (hipEventSynchronize(p->desc_ev[slot]) != hipSuccess) return KV_ERR_HIP;
+    kvx::SpanDev *h = p->h_desc + (size_t)slot * KV_MAX_SPANS;
+    kvx::SpanDev *dd = p->d_desc + (size_t)slot * KV_MAX_SPANS;
+    kvx::Launch a;
+    uint32_t n_rec = 0;
+    rc = prepare_with(&p->desc, spans, n_spans, spec, h, &n_rec, &a, &info, p->plans.data(),
+                      p->ranges.data());
+    if (rc) return rc;
+    if (hipMemcpyAsync(dd, h, n_rec * sizeof(kvx::SpanDev), hipMemcpyHostToDevice, stream) !=
+        hipSuccess)
+        return KV_ERR_HIP;
+    a.regions = p->d_regions;
+    a.spans = dd;
+    a.err = p->d_err;
+
+    uint32_t grid = kvx::default_grid(info.tiles);
+    if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
+
+    const bool timed = p->timing && p->n_timed < kMaxTimed;
+    if (timed && hipEventRecord(p->t_ev[2 * p->n_timed], stream) != hipSuccess) return KV_ERR_HIP;
+    if (kvx::launch_tile_copy(direction, a, grid, stream) != (int)hipSuccess) return KV_ERR_HIP;
+    if (timed) {
+        if (hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream) != hipSuccess) return KV_ERR_HIP;
+        ++p->n_timed;
+    }
+    if (hipEventRecord(p->desc_ev[slot], stream) != hipSuccess) return KV_ERR_HIP;
+    return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_pool_create(const kv_pool_desc *desc, kv_pool **out)
+{
+    if (!out) return KV_ERR_ARG;
+    *out = nullptr;
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    kv_pool *p = new (std::nothrow) kv_pool();
+    if (!p) return KV_ERR_OOM;
+    try {
+        const int64_t n = (int64_t)desc->num_layers * desc->num_kv;
+        p->desc = *desc;
+        p->bases.assign(desc->bases, desc->bases + n);
+        p->desc.bases = p->bases.data();
+        p->free_ids.resize(desc->num_blocks);
+        // LIFO: ids come out in increasing order from a fresh pool
+        for (int64_t i = 0; i < desc->num_blocks; ++i)
+            p->free_ids[i] = (int32_t)(desc->num_blocks - 1 - i);
+        p->allocated.assign(desc->num_blocks, 0);
+        p->plans.resize(KV_MAX_SPANS);
+        p->ranges.resize(KV_MAX_SPANS);
+    } catch (...) {
+        delete p;
+        return KV_ERR_OOM;
+    }
+    *out = p;
+    return KV_OK;
+}
+
+int kv_pool_destroy(kv_pool *pool)
+{
+    if (!pool) return KV_OK;
+    device_teardown(pool);
+    delete pool;
+    return KV_OK;
+}
+
+int kv_pool_alloc_blocks(kv_pool *p, int32_t n, int32_t *out_ids)
+{
+    if (!p || n < 0 || (n > 0 && !out_ids)) return KV_ERR_ARG;
+    if ((size_t)n > p->free_ids.size()) return KV_ERR_OOM;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t id = p->free_ids.back();
+        p->free_ids.pop_back();
+        p->allocated[id] = 1;
+        out_ids[i] = id;
+    }
+    return KV_OK;
+}
+
+int kv_pool_free_blocks(kv_pool *p, int32_t n, const int32_t *ids)
+{
+    if (!p || n < 0 || (n > 0 && !ids)) return KV_ERR_ARG;
+    // check everything first so a bad call frees nothing
+    for (int32_t i = 0; i < n; ++i) {
+        if (ids[i] < 0 || ids[i] >= p->desc.num_blocks || !p->allocated[ids[i]]) {
+            for (int32_t j = 0; j < i; ++j) p->allocated[ids[j]] = 1;
+            return KV_ERR_RANGE;
+        }
+        p->allocated[ids[i]] = 0;  // provisional mark, catches duplicates within the call
+    }
+    for (int32_t i = 0; i < n; ++i) p->free_ids.push_back(ids[i]);
+    return KV_OK;
+}
+
+int kv_pool_free_count(const kv_pool *p, int64_t *out)
+{
+    if (!p || !out) return KV_ERR_ARG;
+    *out = (int64_t)p->free_ids.size();
+    return KV_OK;
+}
+
+int kv_check_transfer(const kv_pool_desc *desc, const kv_span *spans, int32_t n_spans,
+                      const kv_chunk_spec *spec, kv_transfer_info *info)
+{
+    if (n_spans < 0 || n_spans > KV_MAX_SPANS) return KV_ERR_ARG;
+    try {
+        std::vector<SpanPlan> plans(std::max(1, (int)n_spans));
+        std::vector<SlotRange> ranges(std::max(1, (int)n_spans));
+        return validate_call(desc, spans, n_spans, spec, info, plans.data(), ranges.data());
+    } catch (...) {
+        return KV_ERR_OOM;
+    }
+}
+
+int kv_chunk_bytes(const kv_pool_desc *desc, const kv_chunk_spec *spec, int64_t tokens,
+                   int64_t *out)
+{
+    if (!out) return KV_ERR_ARG;
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!spec || (spec->layout != KV_LAYER_FIRST && spec->layout != KV_PAGE_FIRST) ||
+        spec->chunk_layers < 1 || spec->chunk_tokens < 1)
+        return KV_ERR_ARG;
+    if (tokens < 1 || tokens > spec->chunk_tokens) return KV_ERR_ARG;
+    *out = chunk_bytes_for(desc, spec, tokens);
+    return KV_OK;
+}
+
+int kv_validate_targets(const kv_pool_desc *desc, const kv_span *spans, int32_t n_spans,
+                        const int32_t *const *host_tables, int32_t direction)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (direction != KV_GATHER && direction != KV_SCATTER) return KV_ERR_ARG;
+    if (n_spans < 0 || n_spans > KV_MAX_SPANS || (n_spans > 0 && (!spans || !host_tables)))
+        return KV_ERR_ARG;
+    const int64_t bs = desc->block_size;
+    // For scatter, a pool page may be written by one span only, and within a span
+    // two logical pages must not share a block.
+    std::vector<uint8_t> used;
+    try {
+        if (direction == KV_SCATTER) used.assign(desc->num_blocks, 0);
+    } catch (...) {
+        return KV_ERR_OOM;
+    }
+    for (int32_t i = 0; i < n_spans; ++i) {
+        const kv_span &sp = spans[i];
+        if (sp.t_end <= sp.t_begin) continue;
+        if (!host_tables[i]) return KV_ERR_ARG;
+        const int64_t p0 = sp.t_begin / bs, p1 = cdiv(sp.t_end, bs);
+        if (sp.table_len < p1) return KV_ERR_RANGE;
+        for (int64_t pg = p0; pg < p1; ++pg) {
+            const int32_t b = host_tables[i][pg];
+            if (b < 0 || b >= desc->num_blocks) return KV_ERR_RANGE;
+            if (direction == KV_SCATTER) {
+                if (used[b]) return KV_ERR_DUP;
+                used[b] = 1;
+            }
+        }
+    }
+    return KV_OK;
+}
+
+int kv_gather_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                     const kv_chunk_spec *spec, hipStream_t stream)
+{
+    return transfer(pool, spans, n_spans, spec, stream, KV_GATHER);
+}
+
+int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                      const kv_chunk_spec *spec, hipStream_t stream)
+{
+    return transfer(pool, spans, n_spans, spec, stream, KV_SCATTER);
+}
+
+int kv_pool_get_error(kv_pool *p, hipStream_t stream, int32_t *out_bits)
+{
+    if (!p || !out_bits) return KV_ERR_ARG;
+    *out_bits = 0;
+    if (p->device < 0) return KV_OK;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KV_ERR_HIP;
+    int32_t v = 0;
+    if (hipMemcpy(&v, p->d_err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return KV_ERR_HIP;
+    if (v && hipMemset(p->d_err, 0, sizeof(int32_t)) != hipSuccess) return KV_ERR_HIP;
+    *out_bits = v;
+    return v ? KV_ERR_DEVICE : KV_OK;
+}
+
+int kv_pool_timing_start(kv_pool *p)
+{
+    if (!p) return KV_ERR_ARG;
+    if (p->t_ev.empty()) {
+        try {
+            p->t_ev.assign(2 * kMaxTimed, nullptr);
+        } catch (...) {
+            return KV_ERR_OOM;
+        }
+        for (auto &e : p->t_ev)
+            if (hipEventCreate(&e) != hipSuccess) return KV_ERR_HIP;
+    }
+    p->n_timed = 0;
+    p->timing = true;
+    return KV_OK;
+}
+
+int kv_pool_timing_read(kv_pool *p, double *total_ms, int64_t *launches)
+{
+    if (!p || !total_ms || !launches) return KV_ERR_ARG;
+    double sum = 0.0;
+    for (int i = 0; i < p->n_timed; ++i) {
+        if (hipEventSynchronize(p->t_ev[2 * i + 1]) != hipSuccess) return KV_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, p->t_ev[2 * i], p->t_ev[2 * i + 1]) != hipSuccess)
+            return KV_ERR_HIP;
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = p->n_timed;
+    p->timing = false;
+    p->n_timed = 0;
+    return KV_OK;
+}
+
+int kv_ring_create(int64_t slot_bytes, int64_t n_slots, int32_t flags, kv_ring **out)
+{
+    if (!out) return KV_ERR_ARG;
+    *out = nullptr;
+    if (slot_bytes <= 0 || n_slots <= 0 || n_slots > INT64_MAX / slot_bytes) return KV_ERR_ARG;
+    if (slot_bytes % 16 != 0) return KV_ERR_ALIGN;
+    if (flags & ~KV_RING_NONCOHERENT) return KV_ERR_ARG;
+    kv_ring *r = new (std::nothrow) kv_ring();
+    if (!r) return KV_ERR_OOM;
+    const size_t bytes = (size_t)(slot_bytes * n_slots);
+    const unsigned hflags = hipHostMallocMapped | hipHostMallocPortable |
+                            ((flags & KV_RING_NONCOHERENT) ? hipHostMallocNonCoherent
+                                                           : hipHostMallocCoherent);
+    if (hipHostMalloc(&r->host, bytes, hflags) != hipSuccess) {
+        (void)hipGetLastError();
+        delete r;
+        return KV_ERR_OOM;
+    }
+    if (hipHostGetDevicePointer(&r->dev, r->host, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipHostFree(r->host);
+        delete r;
+        return KV_ERR_HIP;
+    }
+    std::memset(r->host, 0, bytes);
+    r->slot_bytes = slot_bytes;
+    r->n_slots = n_slots;
+    *out = r;
+    return KV_OK;
+}
+
+int kv_ring_slot(const kv_ring *r, int64_t i, void **host_ptr, void **dev_ptr)
+{
+    if (!r || i < 0 || i >= r->n_slots) return KV_ERR_ARG;
+    if (host_ptr) *host_ptr = static_cast<uint8_t *>(r->host) + i * r->slot_bytes;
+    if (dev_ptr) *dev_ptr = static_cast<uint8_t *>(r->dev) + i * r->slot_bytes;
+    return KV_OK;
+}
+
+int kv_ring_destroy(kv_ring *r)
+{
+    if (!r) return KV_OK;
+    if (r->host) (void)hipHostFree(r->host);
+    delete r;
+    return KV_OK;
+}
+
+const char *kv_strerror(int code)
+{
+    switch (code) {
+    case KV_OK: return "ok";
+    case KV_ERR_ARG: return "invalid argument";
+    case KV_ERR_ALIGN: return "pointer, stride, slot size or token size not 16-byte aligned";
+    case KV_ERR_RANGE: return "out of range (table length, slot size or block id)";
+    case KV_ERR_OOM: return "out of memory or blocks";
+    case KV_ERR_RING: return "two chunks of one call share a staging slot";
+    case KV_ERR_HIP: return "HIP runtime error";
+    case KV_ERR_DEVICE: return "the device reported a block id out of range";
+    case KV_ERR_DUP: return "scatter writes one pool page twice";
+    default: return "unknown error";
+    }
+}
+
+int kv_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// kvxfer_internal.h -- launch descriptor and tile addressing shared by the host
+// code and the gfx950 kernel (not part of the public ABI).
+//
+// One call = one kernel launch over "tiles": a tile is the tokens of one page of
+// one (layer, kv) region that a span moves.  On both sides a tile is one
+// contiguous byte range (tokens are stored token-major, tok bytes each, in the
+// pool block and in either chunk layout), so the layout change between pool and
+// chunk is only the choice of the two base addresses -- made per tile by the
+// wavefront that copies it (Strata guide, "Two-Dimensional Memory Layout
+// Decoupling": the target address comes from a little integer arithmetic, and no
+// separate transposition pass is needed).
+//
+// Tiles of a span are numbered in chunk order so that consecutive wavefronts
+// walk the contiguous chunk side sequentially, as the printed load kernel walks
+// its page-first source linearly (Strata guide, "Step 1: High-Performance
+// GPU-Assisted I/O CUDA Kernel"):
+//   local tile r = (lc * n_tc + tc) * (tiles of a full chunk) + in-chunk index
+//   in-chunk index, layer-first chunk [CL][KV][pages]: (li * KV + kv) * pages_here + pi
+//   in-chunk index, page-first chunk  [pages][CL][KV]: (pi * CL + li) * KV + kv
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvxfer.h"
+
+namespace kvx {
+
+constexpr int kWavesPerBlock = 4;  // 256-thread workgroups of four 64-lane wavefronts
+constexpr int kThreads = 64 * kWavesPerBlock;
+
+// Per-span launch record, uploaded once per call (64 bytes: one scalar 16-dword load).
+struct alignas(64) SpanDev {
+    const int32_t *table;  // device block table
+    int64_t tile_begin;    // first global tile id of this span
+    int64_t t_end;         // one past the last token
+    int64_t slot0;         // first_chunk mod n_slots
+    uint32_t first_page;   // t_begin / block_size
+    uint32_t n_pages;      // pages the span touches (last may be partial)
+    uint32_t ppc;          // pages per full chunk (chunk_tokens / block_size, capped at n_pages)
+    uint32_t n_tc;         // token chunks of the span
+    uint32_t per_lc;       // tiles per layer chunk = CL * KV * n_pages
+    uint32_t per_tc;       // tiles per full token chunk = CL * KV * ppc
+    uint32_t pad_[2];
+};
+static_assert(sizeof(SpanDev) == 64, "SpanDev must stay 64 bytes");
+
+struct Launch {
+    uint8_t *const *regions;  // device array [num_layers * num_kv] of region bases
+    const SpanDev *spans;     // device array [n_spans]
+    uint8_t *chunk_base;      // staging base (HBM or mapped pinned host)
+    int32_t *err;             // sticky device error word
+    int64_t total_tiles;
+    int64_t block_stride;
+    int64_t slot_bytes;
+    int64_t n_slots;
+    int64_t tile_bytes;       // block_size * tok
+    uint32_t num_blocks;
+    uint32_t n_spans;
+    uint32_t num_kv;
+    uint32_t chunk_layers;
+    uint32_t layer_begin;
+    uint32_t tok;             // bytes per token per (layer, kv), multiple of 16
+    uint32_t block_size;
+    uint32_t layout;          // KV_LAYER_FIRST or KV_PAGE_FIRST
+};
+
+// Where one tile's bytes live, before the block-table lookup.
+struct TileRef {
+    uint32_t page;      // index into the span's block table
+    uint32_t region;    // layer * num_kv + kv
+    uint32_t nbytes;    // n_tok * tok, a multiple of 16
+    int64_t chunk_off;  // byte offset of the tile from chunk_base
+};
+
+__host__ __device__ inline int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ inline uint32_t min32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+// The last span whose first tile is <= tile, searching [lo, n).  Spans is any
+// pointer-like type (a constant-space pointer on the device, a plain one on the host).
+template <typename SpanPtr>
+__host__ __device__ inline uint32_t find_span(SpanPtr spans, uint32_t lo, uint32_t n, int64_t tile)
+{
+    uint32_t hi = n - 1;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (spans[mid].tile_begin <= tile) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Decompose a tile of span sp into its page, region, length and chunk offset.
+template <int LAYOUT>
+__host__ __device__ inline TileRef resolve_tile(const Launch &a, const SpanDev &sp, int64_t tile)
+{
+    uint32_t r = (uint32_t)(tile - sp.tile_begin);
+    const uint32_t lc = r / sp.per_lc;
+    r -= lc * sp.per_lc;
+    const uint32_t tc = r / sp.per_tc;
+    r -= tc * sp.per_tc;
+    const uint32_t pages_here = min32(sp.ppc, sp.n_pages - tc * sp.ppc);
+    uint32_t li, kv, pi;
+    if (LAYOUT == KV_LAYER_FIRST) {  // [CL][KV][pages]
+        pi = r % pages_here;
+        const uint32_t q = r / pages_here;
+        kv = q % a.num_kv;
+        li = q / a.num_kv;
+    } else {                          // [pages][CL][KV]
+        kv = r % a.num_kv;
+        const uint32_t q = r / a.num_kv;
+        li = q % a.chunk_layers;
+        pi = q / a.chunk_layers;
+    }
+    TileRef t;
+    t.page = sp.first_page + tc * sp.ppc + pi;
+    t.region = (a.layer_begin + lc * a.chunk_layers + li) * a.num_kv + kv;
+    const int64_t first_tok = (int64_t)t.page * a.block_size;
+    t.nbytes = (uint32_t)min64((int64_t)a.block_size, sp.t_end - first_tok) * a.tok;
+
+    int64_t slot = sp.slot0 + (int64_t)lc * sp.n_tc + tc;
+    if (slot >= a.n_slots) slot -= a.n_slots;
+    int64_t coff;
+    if (LAYOUT == KV_LAYER_FIRST) {
+        const int64_t chunk_tok0 = ((int64_t)sp.first_page + (int64_t)tc * sp.ppc) * a.block_size;
+        const int64_t t_c = min64((int64_t)sp.ppc * a.block_size, sp.t_end - chunk_tok0);
+        coff = ((int64_t)(li * a.num_kv + kv) * t_c + (int64_t)pi * a.block_size) * a.tok;
+    } else {
+        coff = ((int64_t)(pi * a.chunk_layers + li) * a.num_kv + kv) * a.tile_bytes;
+    }
+    t.chunk_off = slot * a.slot_bytes + coff;
+    return t;
+}
+
+// Host: validate a call and fill the launch descriptor (all fields but regions,
+// spans and err, which hold device addresses) and the span records (records has
+// room for KV_MAX_SPANS).  *n_records receives the number of non-empty spans.
+int prepare_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
+                 const kv_chunk_spec *spec, SpanDev *records, uint32_t *n_records, Launch *launch,
+                 kv_transfer_info *info);
+
+// Kernel launch (kernel file); returns a hipError_t value.
+int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t stream);
+
+// Default grid for a call of `tiles` tiles.
+uint32_t default_grid(int64_t tiles);
+
+}  // namespace kvx

@@ -1,0 +1,133 @@
+// kvxfer_kernels.hip -- the gather/scatter tile-copy kernel for gfx950.
+//
+// One 64-lane wavefront copies one (layer, kv, page) tile per iteration of a
+// grid-stride loop.  Per tile it
+//   1. finds the span (binary search over the per-span tile prefix, wave-uniform,
+//      so it runs on the scalar unit with scalar loads),
+//   2. splits the local tile index into (layer chunk, token chunk, layer, kv, page)
+//      in chunk order and loads the block id from the block table once,
+//   3. forms both byte addresses -- the layout transform is this address choice
+//      (Strata guide, "Two-Dimensional Memory Layout Decoupling"), and
+//   4. copies the tile's n_tok*tok contiguous bytes with 16-byte vector loads and
+//      stores, 64 lanes x 16 B = 1 KiB per wave instruction, eight in flight per
+//      lane, nontemporal on both sides (the Strata guide's reload kernel uses
+//      cache-streaming stores so a transfer does not evict the working set of
+//      concurrent compute kernels: "Non-Intrusive Resource Sizing").
+// No LDS and no matrix instructions: it is a pure byte copy, bound by HBM (both
+// sides in HBM) or by the host link (chunks in pinned host memory).
+//
+// A block id outside [0, num_blocks) is not followed: lane 0 sets the sticky
+// error bit and the wave skips that tile.  All offsets are 64-bit (the printed
+// kernel's 32-bit linear index would overflow past 2^31 16-byte items, which a
+// 128K-token 70B-shaped transfer exceeds).
+#include <hip/hip_runtime.h>
+
+#include "kvxfer.h"
+#include "kvxfer_internal.h"
+
+namespace kvx {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Address-space views.  Pointers read out of memory are "generic" to the compiler,
+// which then emits flat instructions; the tile data always lives in global memory
+// (HBM or mapped host memory), so it is accessed through the global space.  The
+// span records, region table and block tables are not written while the kernel
+// runs, and a wave reads them at uniform addresses, so they are read through the
+// constant space, which lets the compiler use scalar loads.
+#define KVX_GLOBAL __attribute__((address_space(1)))
+#define KVX_CONST __attribute__((address_space(4)))
+typedef KVX_GLOBAL u32x4 gvec;
+
+template <typename T>
+__device__ __forceinline__ const KVX_CONST T *as_const(const T *p)
+{
+    return (const KVX_CONST T *)p;
+}
+__device__ __forceinline__ gvec *as_global(uint8_t *p) { return (gvec *)p; }
+
+__device__ __forceinline__ SpanDev load_span(const KVX_CONST SpanDev *p)
+{
+    SpanDev r;
+    r.table = p->table;
+    r.tile_begin = p->tile_begin;
+    r.t_end = p->t_end;
+    r.slot0 = p->slot0;
+    r.first_page = p->first_page;
+    r.n_pages = p->n_pages;
+    r.ppc = p->ppc;
+    r.n_tc = p->n_tc;
+    r.per_lc = p->per_lc;
+    r.per_tc = p->per_tc;
+    return r;
+}
+
+// Copy nvec 16-byte vectors; lane i handles vectors i, i+64, i+128, ...
+template <int U>
+__device__ __forceinline__ void copy_run(const gvec *__restrict__ src, gvec *__restrict__ dst,
+                                         uint32_t nvec, uint32_t lane)
+{
+    uint32_t v = lane;
+    for (; v + 64u * (U - 1) < nvec; v += 64u * U) {
+        u32x4 r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = __builtin_nontemporal_load(src + v + 64u * u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], dst + v + 64u * u);
+    }
+    for (; v < nvec; v += 64u) __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
+}
+
+template <int DIR, int LAYOUT>
+__global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
+    const KVX_CONST SpanDev *spans = as_const(a.spans);
+    uint32_t s = 0;
+
+    for (int64_t tile = (int64_t)blockIdx.x * kWavesPerBlock + wave; tile < a.total_tiles;
+         tile += step) {
+        // tiles only grow along the loop, so the span search starts at the last span
+        s = find_span(spans, s, a.n_spans, tile);
+        const SpanDev sp = load_span(spans + s);
+        const TileRef t = resolve_tile<LAYOUT>(a, sp, tile);
+
+        const int32_t blk = as_const(sp.table)[t.page];
+        if ((uint32_t)blk >= a.num_blocks) {
+            if (lane == 0) atomicOr(a.err, KV_DEVERR_BLOCK_RANGE);
+            continue;
+        }
+        uint8_t *pool = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
+        uint8_t *chunk = a.chunk_base + t.chunk_off;
+        const uint32_t nvec = t.nbytes >> 4;
+        if (DIR == KV_GATHER) copy_run<8>(as_global(pool), as_global(chunk), nvec, lane);
+        else copy_run<8>(as_global(chunk), as_global(pool), nvec, lane);
+    }
+}
+
+int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t stream)
+{
+    const dim3 g(grid), b(kThreads);
+    if (direction == KV_GATHER && a.layout == KV_LAYER_FIRST)
+        hipLaunchKernelGGL((tile_copy<KV_GATHER, KV_LAYER_FIRST>), g, b, 0, stream, a);
+    else if (direction == KV_GATHER)
+        hipLaunchKernelGGL((tile_copy<KV_GATHER, KV_PAGE_FIRST>), g, b, 0, stream, a);
+    else if (a.layout == KV_LAYER_FIRST)
+        hipLaunchKernelGGL((tile_copy<KV_SCATTER, KV_LAYER_FIRST>), g, b, 0, stream, a);
+    else
+        hipLaunchKernelGGL((tile_copy<KV_SCATTER, KV_PAGE_FIRST>), g, b, 0, stream, a);
+    return (int)hipGetLastError();
+}
+
+uint32_t default_grid(int64_t tiles)
+{
+    // 256 CUs x 8 resident 4-wave workgroups = 2048; twice that keeps the queue fed
+    // while the first wave of workgroups drains.
+    const int64_t cap = 4096;
+    const int64_t need = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    return (uint32_t)(need < cap ? need : cap);
+}
+
+}  // namespace kvx

@@ -1,0 +1,287 @@
+"""Python binding of the C ABI in include/kvxfer.h (ctypes; argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does nothing
+but convert arguments and raise on error codes; all transfer work runs in the
+HIP library.  Device buffers are passed as integer addresses or as objects with
+``data_ptr()`` (torch tensors), streams as integer ``hipStream_t`` handles
+(``torch.cuda.current_stream().cuda_stream``) or objects with ``cuda_stream``.
+
+Importing this module loads ``libkvxfer.so`` from this package directory and
+raises ImportError if it has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Sequence
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvxfer.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        "libkvxfer.so is not built (%s); build it with __graft_entry__.build() or "
+        "python -m paged_layout_transfer_amd._build" % _LIB_PATH)
+_lib = ctypes.CDLL(_LIB_PATH)
+
+# ---- constants (mirror include/kvxfer.h) ---------------------------------------------
+KV_OK = 0
+KV_ERR_ARG = -1
+KV_ERR_ALIGN = -2
+KV_ERR_RANGE = -3
+KV_ERR_OOM = -4
+KV_ERR_RING = -5
+KV_ERR_HIP = -6
+KV_ERR_DEVICE = -7
+KV_ERR_DUP = -8
+KV_LAYER_FIRST = 0
+KV_PAGE_FIRST = 1
+KV_GATHER = 0
+KV_SCATTER = 1
+KV_FLAG_VALIDATE = 0x1
+KV_DEVERR_BLOCK_RANGE = 0x1
+KV_RING_COHERENT = 0x0
+KV_RING_NONCOHERENT = 0x1
+KV_MAX_SPANS = 4096
+
+
+class kv_pool_desc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_kv", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("block_stride", ctypes.c_int64),
+                ("bases", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class kv_span(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("table_len", ctypes.c_int64),
+                ("t_begin", ctypes.c_int64), ("t_end", ctypes.c_int64),
+                ("first_chunk", ctypes.c_int64)]
+
+
+class kv_chunk_spec(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("chunk_layers", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int64), ("layer_begin", ctypes.c_int32),
+                ("layer_end", ctypes.c_int32), ("base", ctypes.c_void_p),
+                ("slot_bytes", ctypes.c_int64), ("n_slots", ctypes.c_int64),
+                ("max_workgroups", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class kv_transfer_info(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_int64), ("chunks", ctypes.c_int64),
+                ("payload_bytes", ctypes.c_int64), ("max_chunk_bytes", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("kv_pool_create", ctypes.c_int, ctypes.POINTER(kv_pool_desc), ctypes.POINTER(_P))
+_sig("kv_pool_destroy", ctypes.c_int, _P)
+_sig("kv_pool_alloc_blocks", ctypes.c_int, _P, _I32, _P)
+_sig("kv_pool_free_blocks", ctypes.c_int, _P, _I32, _P)
+_sig("kv_pool_free_count", ctypes.c_int, _P, ctypes.POINTER(_I64))
+_sig("kv_check_transfer", ctypes.c_int, ctypes.POINTER(kv_pool_desc), ctypes.POINTER(kv_span), _I32,
+     ctypes.POINTER(kv_chunk_spec), ctypes.POINTER(kv_transfer_info))
+_sig("kv_chunk_bytes", ctypes.c_int, ctypes.POINTER(kv_pool_desc), ctypes.POINTER(kv_chunk_spec), _I64,
+     ctypes.POINTER(_I64))
+_sig("kv_validate_targets", ctypes.c_int, ctypes.POINTER(kv_pool_desc), ctypes.POINTER(kv_span), _I32,
+     ctypes.POINTER(_P), _I32)
+_sig("kv_gather_chunks", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
+_sig("kv_scatter_chunks", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
+_sig("kv_pool_get_error", ctypes.c_int, _P, _P, ctypes.POINTER(_I32))
+_sig("kv_pool_timing_start", ctypes.c_int, _P)
+_sig("kv_pool_timing_read", ctypes.c_int, _P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64))
+_sig("kv_ring_create", ctypes.c_int, _I64, _I64, _I32, ctypes.POINTER(_P))
+_sig("kv_ring_slot", ctypes.c_int, _P, _I64, ctypes.POINTER(_P), ctypes.POINTER(_P))
+_sig("kv_ring_destroy", ctypes.c_int, _P)
+_sig("kv_strerror", ctypes.c_char_p, ctypes.c_int)
+_sig("kv_version", ctypes.c_int)
+
+LIBRARY_PATH = _LIB_PATH
+EXPORTED = ("kv_pool_create", "kv_pool_destroy", "kv_pool_alloc_blocks", "kv_pool_free_blocks",
+            "kv_pool_free_count", "kv_check_transfer", "kv_chunk_bytes", "kv_validate_targets",
+            "kv_gather_chunks", "kv_scatter_chunks", "kv_pool_get_error", "kv_pool_timing_start",
+            "kv_pool_timing_read", "kv_ring_create", "kv_ring_slot", "kv_ring_destroy",
+            "kv_strerror", "kv_version")
+
+
+class KvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        super().__init__("%s: %s (%d)" % (where, kv_strerror(code), code))
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != KV_OK:
+        raise KvError(rc, where)
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x)
+
+
+def _stream(s) -> int:
+    if s is None:
+        return 0
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    return int(s)
+
+
+# ---- descriptor builders ---------------------------------------------------------------
+
+def make_pool_desc(num_layers: int, num_kv: int, num_heads: int, head_dim: int, elem_bytes: int,
+                   block_size: int, num_blocks: int, block_stride: int,
+                   bases: Sequence) -> kv_pool_desc:
+    """A kv_pool_desc; bases holds num_layers*num_kv device addresses (index l*num_kv+kv)."""
+    arr = (ctypes.c_void_p * len(bases))(*[_addr(b) for b in bases])
+    d = kv_pool_desc(num_layers, num_kv, num_heads, head_dim, elem_bytes, block_size,
+                     num_blocks, block_stride, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
+    d._bases_keepalive = arr
+    return d
+
+
+def make_spans(spans: Iterable) -> ctypes.Array:
+    """spans: (block_table, table_len, t_begin, t_end, first_chunk) tuples; block_table
+    is a device address or tensor (a host address for kv_validate_targets)."""
+    spans = list(spans)
+    arr = (kv_span * max(1, len(spans)))()
+    for i, (tbl, n, t0, t1, fc) in enumerate(spans):
+        arr[i] = kv_span(_addr(tbl), int(n), int(t0), int(t1), int(fc))
+    arr._n = len(spans)
+    return arr
+
+
+def make_chunk_spec(layout: int, chunk_layers: int, chunk_tokens: int, layer_begin: int,
+                    layer_end: int, base, slot_bytes: int, n_slots: int,
+                    max_workgroups: int = 0, flags: int = 0) -> kv_chunk_spec:
+    return kv_chunk_spec(layout, chunk_layers, chunk_tokens, layer_begin, layer_end, _addr(base),
+                         slot_bytes, n_slots, max_workgroups, flags)
+
+
+def _nspans(spans) -> int:
+    return getattr(spans, "_n", len(spans))
+
+
+# ---- entry points ------------------------------------------------------------------------
+
+def kv_pool_create(desc: kv_pool_desc) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.kv_pool_create(ctypes.byref(desc), ctypes.byref(h)), "kv_pool_create")
+    return h.value
+
+
+def kv_pool_destroy(pool: int) -> None:
+    _check(_lib.kv_pool_destroy(pool), "kv_pool_destroy")
+
+
+def kv_pool_alloc_blocks(pool: int, n: int) -> np.ndarray:
+    out = np.empty(max(1, n), dtype=np.int32)
+    _check(_lib.kv_pool_alloc_blocks(pool, n, out.ctypes.data), "kv_pool_alloc_blocks")
+    return out[:n]
+
+
+def kv_pool_free_blocks(pool: int, ids) -> None:
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    _check(_lib.kv_pool_free_blocks(pool, ids.size, ids.ctypes.data), "kv_pool_free_blocks")
+
+
+def kv_pool_free_count(pool: int) -> int:
+    n = ctypes.c_int64()
+    _check(_lib.kv_pool_free_count(pool, ctypes.byref(n)), "kv_pool_free_count")
+    return n.value
+
+
+def kv_check_transfer(desc: kv_pool_desc, spans, spec: kv_chunk_spec) -> kv_transfer_info:
+    info = kv_transfer_info()
+    _check(_lib.kv_check_transfer(ctypes.byref(desc), spans, _nspans(spans), ctypes.byref(spec),
+                                  ctypes.byref(info)), "kv_check_transfer")
+    return info
+
+
+def kv_chunk_bytes(desc: kv_pool_desc, spec: kv_chunk_spec, tokens: int) -> int:
+    n = ctypes.c_int64()
+    _check(_lib.kv_chunk_bytes(ctypes.byref(desc), ctypes.byref(spec), tokens, ctypes.byref(n)),
+           "kv_chunk_bytes")
+    return n.value
+
+
+def kv_validate_targets(desc: kv_pool_desc, spans, host_tables: Sequence[np.ndarray],
+                        direction: int) -> None:
+    tabs = [np.ascontiguousarray(t, dtype=np.int32) for t in host_tables]
+    ptrs = (ctypes.c_void_p * max(1, len(tabs)))(*[t.ctypes.data for t in tabs])
+    _check(_lib.kv_validate_targets(ctypes.byref(desc), spans, _nspans(spans), ptrs, direction),
+           "kv_validate_targets")
+
+
+def kv_gather_chunks(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
+    _check(_lib.kv_gather_chunks(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
+           "kv_gather_chunks")
+
+
+def kv_scatter_chunks(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
+    _check(_lib.kv_scatter_chunks(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
+           "kv_scatter_chunks")
+
+
+def kv_pool_get_error(pool: int, stream=None) -> int:
+    """Synchronizes the stream; returns (and clears) the device error bits (0 if none)."""
+    bits = ctypes.c_int32()
+    rc = _lib.kv_pool_get_error(pool, _stream(stream), ctypes.byref(bits))
+    if rc not in (KV_OK, KV_ERR_DEVICE):
+        raise KvError(rc, "kv_pool_get_error")
+    return bits.value
+
+
+def kv_pool_timing_start(pool: int) -> None:
+    _check(_lib.kv_pool_timing_start(pool), "kv_pool_timing_start")
+
+
+def kv_pool_timing_read(pool: int) -> tuple[float, int]:
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(_lib.kv_pool_timing_read(pool, ctypes.byref(ms), ctypes.byref(n)), "kv_pool_timing_read")
+    return ms.value, n.value
+
+
+def kv_ring_create(slot_bytes: int, n_slots: int, flags: int = KV_RING_COHERENT) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.kv_ring_create(slot_bytes, n_slots, flags, ctypes.byref(h)), "kv_ring_create")
+    return h.value
+
+
+def kv_ring_slot(ring: int, i: int) -> tuple[int, int]:
+    hp, dp = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(_lib.kv_ring_slot(ring, i, ctypes.byref(hp), ctypes.byref(dp)), "kv_ring_slot")
+    return hp.value, dp.value
+
+
+def kv_ring_destroy(ring: int) -> None:
+    _check(_lib.kv_ring_destroy(ring), "kv_ring_destroy")
+
+
+def kv_strerror(code: int) -> str:
+    return _lib.kv_strerror(code).decode()
+
+
+def kv_version() -> int:
+    return int(_lib.kv_version())
+
+
+def ring_host_array(ring: int, nbytes: int) -> np.ndarray:
+    """A numpy uint8 view of a ring's host mapping (first nbytes), for filling and reading."""
+    host, _ = kv_ring_slot(ring, 0)
+    return np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(host))

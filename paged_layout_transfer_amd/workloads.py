@@ -110,6 +110,22 @@ def resolve(w: dict) -> dict:
     return w
 
 
+def staging_plan(w: dict) -> dict:
+    """How a resolved workload's requests are staged: every request moves all
+    layers, chunk indices are numbered request after request, and each slot
+    holds a full chunk (chunk_layers x K/V x chunk_tokens tokens).  Returns
+    first_chunk per request, the chunk count and the slot size."""
+    bs, CT, CL = w["block_size"], w["chunk_tokens"], w["chunk_layers"]
+    per_layer_chunks = w["num_layers"] // CL
+    first, c = [], 0
+    for t0, t1 in w["requests"]:
+        first.append(c)
+        c += per_layer_chunks * -(-(t1 - t0) // CT)
+    slot = CL * w["num_kv"] * CT * token_bytes(w)
+    assert CT % bs == 0
+    return dict(first_chunk=first, n_chunks=c, slot_bytes=slot)
+
+
 def host_fill(nbytes: int, kind: str, seed: int) -> np.ndarray:
     """Seeded random contents as a flat uint8 array.
 

@@ -26,18 +26,27 @@ def slot_capacity(pool: dict, chunks: dict) -> int:
 
 
 def make_case(rng: np.random.Generator, *, tok_multiple: int = 1, max_bytes: int = 1 << 20,
-              layout: int | None = None, n_spans: int | None = None):
-    """A random small case: (pool, spans, chunks) with tables as int32 arrays."""
+              layout: int | None = None, n_spans: int | None = None, medium: bool = False):
+    """A random case: (pool, spans, chunks) with tables as int32 arrays.
+
+    Small cases use tiny heads (tokens of 8-144 bytes, pages of 2-16 tokens);
+    medium cases use model-like heads (tokens of 64 B - 4 KiB, pages of 16-64
+    tokens) so a page spans several 1 KiB wave copies plus a ragged tail."""
     while True:
-        L = int(rng.integers(1, 4))
+        L = int(rng.integers(1, 5 if medium else 4))
         KV = int(rng.integers(1, 3))
-        H = int(rng.integers(1, 4))
-        D = int(rng.choice([8, 16, 24]))
-        E = int(rng.choice([1, 2]))
+        if medium:
+            H = int(rng.choice([1, 2, 8]))
+            D = int(rng.choice([64, 128, 576]))
+            E = int(rng.choice([1, 2]))
+        else:
+            H = int(rng.integers(1, 4))
+            D = int(rng.choice([8, 16, 24]))
+            E = int(rng.choice([1, 2]))
         tok = H * D * E
         if tok % tok_multiple:
             continue
-        bs = int(rng.choice([2, 4, 16]))
+        bs = int(rng.choice([16, 32, 64] if medium else [2, 4, 16]))
         tile = bs * tok
         block_stride = tile + int(rng.choice([0, 0, 16, 48]))
         if block_stride % tok_multiple:

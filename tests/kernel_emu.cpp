@@ -1,0 +1,82 @@
+// kernel_emu.cpp -- CPU walk of the tile-copy kernel's grid-stride loop (test only).
+//
+// Built together with the library's own sources, it runs the library's host
+// preparation (kvx::prepare_call) and, for every (workgroup, wave) of the grid the
+// library would launch, the same span search and tile resolution the kernel
+// runs (kvx::find_span, kvx::resolve_tile), on host buffers.  Every address is
+// checked against the buffers it must stay in before anything is copied, and
+// every tile must be visited exactly once.  With copy != 0 the tile bytes are
+// moved with memcpy so the result can be compared with the oracle.
+#include <cstring>
+#include <vector>
+
+#include "kvxfer_internal.h"
+
+extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span *spans,
+                            int32_t n_spans, const kv_chunk_spec *spec, const int64_t *region_bytes,
+                            int64_t staging_bytes, int32_t copy, int64_t *violations,
+                            int64_t *tiles_out, int64_t *grid_out)
+{
+    static kvx::SpanDev records[KV_MAX_SPANS];
+    uint32_t n_rec = 0;
+    kvx::Launch a;
+    kv_transfer_info info;
+    int rc = kvx::prepare_call(d, spans, n_spans, spec, records, &n_rec, &a, &info);
+    if (rc) return rc;
+    *violations = 0;
+    *tiles_out = info.tiles;
+    if (info.tiles == 0) {
+        *grid_out = 0;
+        return KV_OK;
+    }
+    // table length of each record (records skip empty spans)
+    std::vector<int64_t> tlen;
+    for (int32_t i = 0; i < n_spans; ++i)
+        if (spans[i].t_end > spans[i].t_begin) tlen.push_back(spans[i].table_len);
+
+    uint32_t grid = kvx::default_grid(info.tiles);
+    if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
+        grid = (uint32_t)spec->max_workgroups;
+    *grid_out = grid;
+    std::vector<uint8_t> seen((size_t)info.tiles, 0);
+    const int64_t step = (int64_t)grid * kvx::kWavesPerBlock;
+    const int64_t nreg = (int64_t)d->num_layers * d->num_kv;
+
+    for (uint32_t b = 0; b < grid; ++b) {
+        for (int w = 0; w < kvx::kWavesPerBlock; ++w) {
+            uint32_t s = 0;
+            for (int64_t tile = (int64_t)b * kvx::kWavesPerBlock + w; tile < a.total_tiles;
+                 tile += step) {
+                s = kvx::find_span(records, s, n_rec, tile);
+                const kvx::SpanDev &sp = records[s];
+                if (tile < sp.tile_begin) { ++*violations; continue; }
+                const kvx::TileRef t = (a.layout == KV_LAYER_FIRST)
+                                           ? kvx::resolve_tile<KV_LAYER_FIRST>(a, sp, tile)
+                                           : kvx::resolve_tile<KV_PAGE_FIRST>(a, sp, tile);
+                if (seen[tile]++) { ++*violations; continue; }
+                if ((int64_t)t.page >= tlen[s] || (int64_t)t.region >= nreg || t.nbytes == 0 ||
+                    t.nbytes % 16 != 0 || t.chunk_off < 0 ||
+                    t.chunk_off + (int64_t)t.nbytes > staging_bytes) {
+                    ++*violations;
+                    continue;
+                }
+                const int32_t blk = sp.table[t.page];
+                if (blk < 0 || (uint32_t)blk >= a.num_blocks) continue;  // the kernel skips it too
+                const int64_t poff = (int64_t)blk * a.block_stride;
+                if (poff + (int64_t)t.nbytes > region_bytes[t.region]) {
+                    ++*violations;
+                    continue;
+                }
+                if (copy) {
+                    uint8_t *pool = static_cast<uint8_t *>(d->bases[t.region]) + poff;
+                    uint8_t *chunk = a.chunk_base + t.chunk_off;
+                    if (direction == KV_GATHER) std::memcpy(chunk, pool, t.nbytes);
+                    else std::memcpy(pool, chunk, t.nbytes);
+                }
+            }
+        }
+    }
+    for (int64_t i = 0; i < info.tiles; ++i)
+        if (seen[i] != 1) ++*violations;
+    return KV_OK;
+}

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, byte for byte.
+
+Every case starts from random pool bytes and random staging bytes (so NaN, Inf,
+-0.0 and subnormal fp16/bf16/fp8 patterns all occur), runs one call on the GPU
+and the same call in the oracle, and compares the *whole* pool and the *whole*
+staging buffer: moved bytes must match and every other byte must keep its prior
+value.  Sizes are small enough for the oracle to finish in seconds while still
+spanning many tiles, ragged last pages and short last chunks.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import cases
+import gpu_harness as G
+import oracle
+from paged_layout_transfer_amd import kvxfer as K
+from paged_layout_transfer_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DIRS = (K.KV_GATHER, K.KV_SCATTER)
+
+
+def _oracle(direction, pool, spans, chunks, regions, staging, views=None):
+    regs = regions.copy()
+    stg = staging.copy()
+    if views is None:
+        rows = [regs[i] for i in range(regs.shape[0])]
+    else:
+        need = (pool["num_blocks"] - 1) * pool["block_stride"] + \
+            pool["block_size"] * pool["num_heads"] * pool["head_dim"] * pool["elem_bytes"]
+        rows = [regs[o:o + need] for o in views]
+    oracle.transfer(direction, pool, rows, spans, chunks, stg)
+    return regs, stg
+
+
+def _compare(direction, pool, spans, chunks, regions, staging, label, views=None, **kw):
+    exp_r, exp_s = _oracle(direction, pool, spans, chunks, regions, staging, views)
+    got_r, got_s, bits = G.run_transfer(direction, pool, spans, chunks, regions, staging,
+                                        label=label, region_views=views, **kw)
+    assert bits == 0, "device reported error bits %#x" % bits
+    assert np.array_equal(got_s, exp_s), "staging differs from the oracle"
+    assert np.array_equal(got_r, exp_r), "pool differs from the oracle"
+
+
+def _random(pool, chunks, seed):
+    rng = np.random.default_rng(seed)
+    return cases.regions_for(pool, rng), cases.staging_for(chunks, rng=rng)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_small_random_cases(seed):
+    pool, spans, chunks = cases.make_case(np.random.default_rng(10_000 + seed), tok_multiple=16)
+    regions, staging = _random(pool, chunks, seed)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "small-%d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_medium_random_cases(seed):
+    pool, spans, chunks = cases.make_case(np.random.default_rng(20_000 + seed), tok_multiple=16,
+                                          medium=True, max_bytes=48 << 20)
+    regions, staging = _random(pool, chunks, seed)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "medium-%d" % seed)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pinned_host_ring_cases(seed):
+    """Chunks in pinned host memory, read (scatter) and written (gather) by the kernel."""
+    pool, spans, chunks = cases.make_case(np.random.default_rng(30_000 + seed), tok_multiple=16,
+                                          medium=True, max_bytes=32 << 20)
+    regions, staging = _random(pool, chunks, seed)
+    flags = K.KV_RING_NONCOHERENT if seed % 2 else K.KV_RING_COHERENT
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "ring-%d" % seed, ring=True, ring_flags=flags)
+
+
+@pytest.mark.parametrize("wg", [1, 2, 3, 5])
+def test_capped_grid(wg):
+    """A grid of a few workgroups walks every tile through the grid-stride loop."""
+    pool = dict(num_layers=3, num_kv=2, num_heads=8, head_dim=128, elem_bytes=2, block_size=16,
+                num_blocks=64, block_stride=16 * 2048)
+    rng = np.random.default_rng(40_000 + wg)
+    tables = [rng.permutation(64)[:20].astype(np.int32), rng.permutation(64)[20:40].astype(np.int32)]
+    tables[1] = np.setdiff1d(np.arange(64, dtype=np.int32), tables[0])[:20]
+    spans = [(tables[0], 0, 311, 0), (tables[1], 48, 301, 6)]
+    chunks = dict(layout=0, chunk_layers=3, chunk_tokens=128, layer_begin=0, layer_end=3,
+                  slot_bytes=3 * 2 * 128 * 2048, n_slots=9)
+    regions, staging = _random(pool, chunks, wg)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "grid-%d" % wg, max_workgroups=wg)
+
+
+def test_tiny_workload_gather_then_scatter():
+    w = W.resolve(W.WORKLOADS["tiny"])
+    tok = W.token_bytes(w)
+    pool = {k: w[k] for k in ("num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
+                              "block_size", "num_blocks")}
+    pool["block_stride"] = w["block_size"] * tok
+    plan = W.staging_plan(w)
+    chunks = dict(layout=w["layout"], chunk_layers=w["chunk_layers"], chunk_tokens=w["chunk_tokens"],
+                  layer_begin=0, layer_end=w["num_layers"], slot_bytes=plan["slot_bytes"],
+                  n_slots=plan["n_chunks"])
+    spans = [(w["block_tables"][0], 0, w["tokens"], 0)]
+    n = w["num_layers"] * w["num_kv"]
+    regions = W.host_fill(n * w["num_blocks"] * pool["block_stride"], w["fill"], w["k"]).reshape(n, -1)
+    staging = np.full(plan["slot_bytes"] * plan["n_chunks"], W.SENTINEL, dtype=np.uint8)
+    exp_r, exp_s = _oracle(K.KV_GATHER, pool, spans, chunks, regions, staging)
+    _, got_s, bits = G.run_transfer(K.KV_GATHER, pool, spans, chunks, regions, staging, label="tiny")
+    assert bits == 0 and np.array_equal(got_s, exp_s)
+    fresh = np.full_like(regions, W.SENTINEL)
+    exp_r2, _ = _oracle(K.KV_SCATTER, pool, spans, chunks, fresh, got_s)
+    got_r2, _, bits = G.run_transfer(K.KV_SCATTER, pool, spans, chunks, fresh, got_s, label="tiny")
+    assert bits == 0 and np.array_equal(got_r2, exp_r2)
+    # the round trip restores every referenced token and leaves the rest at the sentinel
+    moved = got_r2 != W.SENTINEL
+    assert np.array_equal(got_r2[moved], regions[moved])
+
+
+REDUCED = {
+    "llama8b": dict(num_layers=4, chunk_layers=4, tokens=2085, num_blocks=200),
+    "llama70b": dict(num_layers=3, chunk_layers=1, tokens=4096 + 21, num_blocks=300),
+    "mixed": dict(num_layers=3, chunk_layers=3, n_requests=6, median=600, min_len=100,
+                  max_len=3000),
+    "mla_fp8": dict(num_layers=5, chunk_layers=5, tokens=64 * 9 + 13, num_blocks=40),
+    "int8_kv": dict(num_layers=3, chunk_layers=3, tokens=64 * 7 + 1, num_blocks=30),
+}
+
+
+def reduced_call(name):
+    w = dict(W.WORKLOADS[name])
+    w.update(REDUCED[name])
+    w = W.resolve(w)
+    tok = W.token_bytes(w)
+    pool = {k: w[k] for k in ("num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
+                              "block_size", "num_blocks")}
+    pool["block_stride"] = w["block_size"] * tok
+    plan = W.staging_plan(w)
+    chunks = dict(layout=w["layout"], chunk_layers=w["chunk_layers"], chunk_tokens=w["chunk_tokens"],
+                  layer_begin=0, layer_end=w["num_layers"], slot_bytes=plan["slot_bytes"],
+                  n_slots=plan["n_chunks"])
+    spans = [(tbl, t0, t1, fc) for tbl, (t0, t1), fc in
+             zip(w["block_tables"], w["requests"], plan["first_chunk"])]
+    return w, pool, spans, chunks
+
+
+@pytest.mark.parametrize("name", sorted(REDUCED))
+def test_reduced_workloads(name):
+    w, pool, spans, chunks = reduced_call(name)
+    n = pool["num_layers"] * pool["num_kv"]
+    regions = W.host_fill(n * pool["num_blocks"] * pool["block_stride"], w["fill"], w["k"]).reshape(n, -1)
+    staging = W.host_fill(chunks["slot_bytes"] * chunks["n_slots"], "bytes", 100 + w["k"])
+    ring = w["staging"] == "host"
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "reduced-" + name, ring=ring)
+
+
+def test_interleaved_kv_pool():
+    """A per-layer [blocks][K/V][page] pool: block_stride = 2 pages, V regions offset by a page."""
+    L, KV, H, D, E, bs, N = 3, 2, 2, 128, 2, 32, 24
+    tile = bs * H * D * E
+    pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
+                num_blocks=N, block_stride=KV * tile)
+    views = [l * N * KV * tile + kv * tile for l in range(L) for kv in range(KV)]
+    rng = np.random.default_rng(50_000)
+    flat = rng.integers(0, 256, size=L * N * KV * tile, dtype=np.uint8)
+    tbl = rng.permutation(N)[:7].astype(np.int32)
+    spans = [(tbl, 32, 32 * 6 + 17, 0)]
+    for layout in (0, 1):
+        chunks = dict(layout=layout, chunk_layers=1, chunk_tokens=64, layer_begin=0, layer_end=L,
+                      slot_bytes=KV * 64 * H * D * E, n_slots=L * 3)
+        staging = cases.staging_for(chunks, rng=rng)
+        for d in DIRS:
+            _compare(d, pool, spans, chunks, flat, staging, "interleaved-%d" % layout, views=views)
+
+
+def test_bad_block_id_is_skipped_and_reported():
+    """A table entry past the pool: that page's tiles are skipped, the sticky error bit is
+    set, and every other tile still moves (page-first, one chunk per page)."""
+    L, KV, H, D, E, bs, N = 2, 2, 1, 64, 2, 16, 32
+    tok = H * D * E
+    pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
+                num_blocks=N, block_stride=bs * tok)
+    rng = np.random.default_rng(60_000)
+    good = rng.permutation(N)[:6].astype(np.int32)
+    bad = good.copy()
+    bad[4] = N + 3                                # page 4 is poisoned
+    chunks = dict(layout=1, chunk_layers=L, chunk_tokens=bs, layer_begin=0, layer_end=L,
+                  slot_bytes=L * KV * bs * tok, n_slots=6)
+    regions, staging = _random(pool, chunks, 7)
+    for d in DIRS:
+        # expected: the oracle without page 4 (chunk 4 keeps its bytes, pool block untouched)
+        part = [(good, 0, 64, 0), (good, 80, 96, 5)]
+        exp_r, exp_s = _oracle(d, pool, part, chunks, regions, staging)
+        got_r, got_s, bits = G.run_transfer(d, pool, [(bad, 0, 96, 0)], chunks, regions, staging,
+                                            label="bad-block")
+        assert bits == K.KV_DEVERR_BLOCK_RANGE
+        assert np.array_equal(got_s, exp_s) and np.array_equal(got_r, exp_r)
+
+
+def test_empty_span_moves_nothing():
+    pool = dict(num_layers=2, num_kv=2, num_heads=1, head_dim=64, elem_bytes=2, block_size=16,
+                num_blocks=8, block_stride=2048)
+    chunks = dict(layout=0, chunk_layers=2, chunk_tokens=16, layer_begin=0, layer_end=2,
+                  slot_bytes=2 * 2 * 16 * 128, n_slots=4)
+    regions, staging = _random(pool, chunks, 3)
+    tbl = np.arange(4, dtype=np.int32)
+    spans = [(tbl, 32, 32, 0), (tbl, 0, 16, 0), (tbl, 64, 64, 3)]   # only the middle span moves
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "empty-spans")
+
+
+def test_validate_flag_rejects_double_write():
+    pool = dict(num_layers=1, num_kv=1, num_heads=1, head_dim=64, elem_bytes=2, block_size=16,
+                num_blocks=8, block_stride=2048)
+    chunks = dict(layout=0, chunk_layers=1, chunk_tokens=16, layer_begin=0, layer_end=1,
+                  slot_bytes=2048, n_slots=4)
+    regions, staging = _random(pool, chunks, 4)
+    tbl = np.array([1, 2, 1, 3], dtype=np.int32)       # block 1 twice
+    spans = [(tbl, 0, 64, 0)]
+    with pytest.raises(K.KvError) as e:
+        G.run_transfer(K.KV_SCATTER, pool, spans, chunks, regions, staging,
+                       flags=K.KV_FLAG_VALIDATE, label="validate-dup")
+    assert e.value.code == K.KV_ERR_DUP
+    # a gather may read one page twice
+    _compare(K.KV_GATHER, pool, spans, chunks, regions, staging, "validate-gather",
+             flags=K.KV_FLAG_VALIDATE)

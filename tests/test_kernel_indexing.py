@@ -1,0 +1,118 @@
+"""CPU check of the kernel's tile indexing (no GPU).
+
+tests/kernel_emu.cpp is compiled here together with the library's sources and
+walks the exact grid-stride loop the kernel runs -- the library's own launch
+preparation, span search and tile resolution -- on host buffers: every address
+must stay inside its buffer and every tile must be visited once.  Small cases
+also copy the bytes and must match the oracle; the workload-sized calls are
+walked without copying (addresses and coverage only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import cases
+import oracle
+from paged_layout_transfer_amd import _build
+from paged_layout_transfer_amd import kvxfer as K
+from paged_layout_transfer_amd import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def emu(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("emu") / "libemu.so")
+    cmd = [_build.HIPCC, *[f for f in _build.FLAGS if f != "-fvisibility=hidden"],
+           "-I", os.path.join(_build.ROOT, "include"), "-I", _build.CSRC,
+           *_build.SOURCES, os.path.join(HERE, "kernel_emu.cpp"), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    lib = ctypes.CDLL(out)
+    lib.emu_transfer.restype = ctypes.c_int
+    lib.emu_transfer.argtypes = [ctypes.c_int, ctypes.POINTER(K.kv_pool_desc), ctypes.POINTER(K.kv_span),
+                                 ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                 ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    return lib
+
+
+def _emulate(lib, direction, pool, spans, chunks, bases, region_bytes, staging_ptr, staging_bytes,
+             copy, max_workgroups=0):
+    desc = K.make_pool_desc(pool["num_layers"], pool["num_kv"], pool["num_heads"], pool["head_dim"],
+                            pool["elem_bytes"], pool["block_size"], pool["num_blocks"],
+                            pool["block_stride"], bases)
+    tabs = [np.ascontiguousarray(t, dtype=np.int32) for t, _, _, _ in spans]
+    sp = K.make_spans([(t.ctypes.data, t.size, t0, t1, fc) for t, (_, t0, t1, fc) in zip(tabs, spans)])
+    spec = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"],
+                             chunks["layer_begin"], chunks["layer_end"], staging_ptr,
+                             chunks["slot_bytes"], chunks["n_slots"], max_workgroups, 0)
+    rb = np.ascontiguousarray(region_bytes, dtype=np.int64)
+    viol, tiles, grid = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = lib.emu_transfer(direction, ctypes.byref(desc), sp, len(spans), ctypes.byref(spec),
+                          rb.ctypes.data, staging_bytes, int(copy), ctypes.byref(viol),
+                          ctypes.byref(tiles), ctypes.byref(grid))
+    assert rc == 0, K.kv_strerror(rc)
+    return viol.value, tiles.value, grid.value
+
+
+def _copy_case(lib, pool, spans, chunks, seed, max_workgroups=0):
+    rng = np.random.default_rng(seed)
+    regions = cases.regions_for(pool, rng)
+    staging = cases.staging_for(chunks, rng=rng)
+    n = regions.shape[0]
+    for d in (K.KV_GATHER, K.KV_SCATTER):
+        r_emu, s_emu = regions.copy(), staging.copy()
+        bases = [r_emu[i].ctypes.data for i in range(n)]
+        viol, _, _ = _emulate(lib, d, pool, spans, chunks, bases, [r_emu.shape[1]] * n,
+                              s_emu.ctypes.data, s_emu.size, True, max_workgroups)
+        assert viol == 0
+        r_or, s_or = regions.copy(), staging.copy()
+        oracle.transfer(d, pool, r_or, spans, chunks, s_or)
+        assert np.array_equal(s_emu, s_or) and np.array_equal(r_emu, r_or)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_emulated_kernel_matches_oracle_small(emu, seed):
+    pool, spans, chunks = cases.make_case(np.random.default_rng(10_000 + seed), tok_multiple=16)
+    _copy_case(emu, pool, spans, chunks, seed)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_emulated_kernel_matches_oracle_medium(emu, seed):
+    pool, spans, chunks = cases.make_case(np.random.default_rng(20_000 + seed), tok_multiple=16,
+                                          medium=True, max_bytes=48 << 20)
+    _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 4))
+
+
+FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_addresses_stay_in_bounds(emu, name):
+    """Full-size calls of every workload, walked without copying: addresses stay inside
+    a pool of exactly num_blocks blocks and a staging buffer of exactly n_slots slots."""
+    w = W.resolve(W.WORKLOADS[name])
+    tok = W.token_bytes(w)
+    pool = {k: w[k] for k in ("num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
+                              "block_size", "num_blocks")}
+    pool["block_stride"] = w["block_size"] * tok
+    plan = W.staging_plan(w)
+    chunks = dict(layout=w["layout"], chunk_layers=w["chunk_layers"], chunk_tokens=w["chunk_tokens"],
+                  layer_begin=0, layer_end=w["num_layers"], slot_bytes=plan["slot_bytes"],
+                  n_slots=plan["n_chunks"])
+    spans = [(t, t0, t1, fc) for t, (t0, t1), fc in zip(w["block_tables"], w["requests"], plan["first_chunk"])]
+    n = pool["num_layers"] * pool["num_kv"]
+    fake = 1 << 44
+    bases = [fake + i * (1 << 38) for i in range(n)]
+    for d in (K.KV_GATHER, K.KV_SCATTER):
+        for wg in (0, 2):
+            viol, tiles, grid = _emulate(emu, d, pool, spans, chunks, bases,
+                                         [pool["num_blocks"] * pool["block_stride"]] * n, 1 << 45,
+                                         plan["slot_bytes"] * plan["n_chunks"], False, wg)
+            assert viol == 0
+            assert tiles == sum(n * -(-(t1 - t0) // w["block_size"]) for t0, t1 in w["requests"])
