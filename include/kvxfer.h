@@ -259,6 +259,11 @@ KV_API const char *kv_strerror(int code);
 /* Library version: major*10000 + minor*100 + patch. */
 KV_API int kv_version(void);
 
+/* The hipError_t of the last HIP runtime call that failed inside the library on
+ * the calling thread (0 if none), and in *where (if not NULL) the call's text.
+ * Lets a caller that got KV_ERR_HIP see which call failed and why. */
+KV_API int kv_last_hip_error(const char **where);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,22 @@ constexpr int kDescSlots = 4;           // descriptor upload buffers in flight p
 constexpr int kMaxTimed = 4096;         // launches one timing window can record
 constexpr int64_t kMaxU31 = 0x7fffffffLL;
 
+// The last HIP failure seen by this thread, reported by kv_last_hip_error.  The
+// runtime's own last-error is consumed on every failure so a stale error never
+// leaks into a later status check.
+thread_local int g_hip_error = 0;
+thread_local const char *g_hip_where = "";
+
+inline bool hip_ok(hipError_t e, const char *where)
+{
+    if (e == hipSuccess) return true;
+    g_hip_error = (int)e;
+    g_hip_where = where;
+    (void)hipGetLastError();
+    return false;
+}
+#define HIP_OK(call) hip_ok((call), #call)
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -274,24 +290,22 @@ void free_device_state(kv_pool *p)
 int device_setup(kv_pool *p)
 {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return KV_ERR_HIP;
+    if (!HIP_OK(hipGetDevice(&dev))) return KV_ERR_HIP;
     if (p->device >= 0) return dev == p->device ? KV_OK : KV_ERR_ARG;
     const int64_t n = (int64_t)p->desc.num_layers * p->desc.num_kv;
     const size_t desc_bytes = sizeof(kvx::SpanDev) * KV_MAX_SPANS * kDescSlots;
-    if (hipMalloc(&p->d_regions, n * sizeof(void *)) != hipSuccess) goto fail;
-    if (hipMemcpy(p->d_regions, p->bases.data(), n * sizeof(void *), hipMemcpyHostToDevice) !=
-        hipSuccess)
+    if (!HIP_OK(hipMalloc(&p->d_regions, n * sizeof(void *)))) goto fail;
+    if (!HIP_OK(hipMemcpy(p->d_regions, p->bases.data(), n * sizeof(void *), hipMemcpyHostToDevice)))
         goto fail;
-    if (hipMalloc(&p->d_err, sizeof(int32_t)) != hipSuccess) goto fail;
-    if (hipMemset(p->d_err, 0, sizeof(int32_t)) != hipSuccess) goto fail;
-    if (hipMalloc(&p->d_desc, desc_bytes) != hipSuccess) goto fail;
-    if (hipHostMalloc((void **)&p->h_desc, desc_bytes, hipHostMallocDefault) != hipSuccess) goto fail;
+    if (!HIP_OK(hipMalloc(&p->d_err, sizeof(int32_t)))) goto fail;
+    if (!HIP_OK(hipMemset(p->d_err, 0, sizeof(int32_t)))) goto fail;
+    if (!HIP_OK(hipMalloc(&p->d_desc, desc_bytes))) goto fail;
+    if (!HIP_OK(hipHostMalloc((void **)&p->h_desc, desc_bytes, hipHostMallocDefault))) goto fail;
     for (int i = 0; i < kDescSlots; ++i)
-        if (hipEventCreateWithFlags(&p->desc_ev[i], hipEventDisableTiming) != hipSuccess) goto fail;
+        if (!HIP_OK(hipEventCreateWithFlags(&p->desc_ev[i], hipEventDisableTiming))) goto fail;
     p->device = dev;
     return KV_OK;
 fail:
-    (void)hipGetLastError();
     free_device_state(p);
     return KV_ERR_HIP;
 }
@@ -308,15 +322,15 @@ int validate_tables(kv_pool *p, const kv_span *spans, int32_t n_spans, int direc
                     hipStream_t stream)
 {
     // Host copies of the device tables (debug path; synchronous by design).
-    if (hipStreamSynchronize(stream) != hipSuccess) return KV_ERR_HIP;
+    if (!HIP_OK(hipStreamSynchronize(stream))) return KV_ERR_HIP;
     std::vector<std::vector<int32_t>> host(n_spans);
     std::vector<const int32_t *> ptrs(n_spans, nullptr);
     for (int32_t i = 0; i < n_spans; ++i) {
         if (spans[i].t_end == spans[i].t_begin) continue;
         const int64_t n = cdiv(spans[i].t_end, p->desc.block_size);
         host[i].resize(n);
-        if (hipMemcpy(host[i].data(), spans[i].block_table, n * sizeof(int32_t),
-                      hipMemcpyDeviceToHost) != hipSuccess)
+        if (!HIP_OK(hipMemcpy(host[i].data(), spans[i].block_table, n * sizeof(int32_t),
+                              hipMemcpyDeviceToHost)))
             return KV_ERR_HIP;
         ptrs[i] = host[i].data();
     }
@@ -346,7 +360,7 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     // then one stream-ordered copy to the matching device buffer.
     const int slot = p->desc_next;
     p->desc_next = (p->desc_next + 1) % kDescSlots;
-    if (hipEventSynchronize(p->desc_ev[slot]) != hipSuccess) return KV_ERR_HIP;
+    if (!HIP_OK(hipEventSynchronize(p->desc_ev[slot]))) return KV_ERR_HIP;
     kvx::SpanDev *h = p->h_desc + (size_t)slot * KV_MAX_SPANS;
     kvx::SpanDev *dd = p->d_desc + (size_t)slot * KV_MAX_SPANS;
     kvx::Launch a;
@@ -354,8 +368,7 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     rc = prepare_with(&p->desc, spans, n_spans, spec, h, &n_rec, &a, &info, p->plans.data(),
                       p->ranges.data());
     if (rc) return rc;
-    if (hipMemcpyAsync(dd, h, n_rec * sizeof(kvx::SpanDev), hipMemcpyHostToDevice, stream) !=
-        hipSuccess)
+    if (!HIP_OK(hipMemcpyAsync(dd, h, n_rec * sizeof(kvx::SpanDev), hipMemcpyHostToDevice, stream)))
         return KV_ERR_HIP;
     a.regions = p->d_regions;
     a.spans = dd;
@@ -365,13 +378,14 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
 
     const bool timed = p->timing && p->n_timed < kMaxTimed;
-    if (timed && hipEventRecord(p->t_ev[2 * p->n_timed], stream) != hipSuccess) return KV_ERR_HIP;
-    if (kvx::launch_tile_copy(direction, a, grid, stream) != (int)hipSuccess) return KV_ERR_HIP;
+    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
+    if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))
+        return KV_ERR_HIP;
     if (timed) {
-        if (hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream) != hipSuccess) return KV_ERR_HIP;
+        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;
         ++p->n_timed;
     }
-    if (hipEventRecord(p->desc_ev[slot], stream) != hipSuccess) return KV_ERR_HIP;
+    if (!HIP_OK(hipEventRecord(p->desc_ev[slot], stream))) return KV_ERR_HIP;
     return KV_OK;
 }
 
@@ -529,10 +543,10 @@ int kv_pool_get_error(kv_pool *p, hipStream_t stream, int32_t *out_bits)
     if (!p || !out_bits) return KV_ERR_ARG;
     *out_bits = 0;
     if (p->device < 0) return KV_OK;
-    if (hipStreamSynchronize(stream) != hipSuccess) return KV_ERR_HIP;
+    if (!HIP_OK(hipStreamSynchronize(stream))) return KV_ERR_HIP;
     int32_t v = 0;
-    if (hipMemcpy(&v, p->d_err, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return KV_ERR_HIP;
-    if (v && hipMemset(p->d_err, 0, sizeof(int32_t)) != hipSuccess) return KV_ERR_HIP;
+    if (!HIP_OK(hipMemcpy(&v, p->d_err, sizeof(v), hipMemcpyDeviceToHost))) return KV_ERR_HIP;
+    if (v && !HIP_OK(hipMemset(p->d_err, 0, sizeof(int32_t)))) return KV_ERR_HIP;
     *out_bits = v;
     return v ? KV_ERR_DEVICE : KV_OK;
 }
@@ -547,7 +561,7 @@ int kv_pool_timing_start(kv_pool *p)
             return KV_ERR_OOM;
         }
         for (auto &e : p->t_ev)
-            if (hipEventCreate(&e) != hipSuccess) return KV_ERR_HIP;
+            if (!HIP_OK(hipEventCreate(&e))) return KV_ERR_HIP;
     }
     p->n_timed = 0;
     p->timing = true;
@@ -559,10 +573,9 @@ int kv_pool_timing_read(kv_pool *p, double *total_ms, int64_t *launches)
     if (!p || !total_ms || !launches) return KV_ERR_ARG;
     double sum = 0.0;
     for (int i = 0; i < p->n_timed; ++i) {
-        if (hipEventSynchronize(p->t_ev[2 * i + 1]) != hipSuccess) return KV_ERR_HIP;
+        if (!HIP_OK(hipEventSynchronize(p->t_ev[2 * i + 1]))) return KV_ERR_HIP;
         float ms = 0.f;
-        if (hipEventElapsedTime(&ms, p->t_ev[2 * i], p->t_ev[2 * i + 1]) != hipSuccess)
-            return KV_ERR_HIP;
+        if (!HIP_OK(hipEventElapsedTime(&ms, p->t_ev[2 * i], p->t_ev[2 * i + 1]))) return KV_ERR_HIP;
         sum += ms;
     }
     *total_ms = sum;
@@ -585,13 +598,11 @@ int kv_ring_create(int64_t slot_bytes, int64_t n_slots, int32_t flags, kv_ring *
     const unsigned hflags = hipHostMallocMapped | hipHostMallocPortable |
                             ((flags & KV_RING_NONCOHERENT) ? hipHostMallocNonCoherent
                                                            : hipHostMallocCoherent);
-    if (hipHostMalloc(&r->host, bytes, hflags) != hipSuccess) {
-        (void)hipGetLastError();
+    if (!HIP_OK(hipHostMalloc(&r->host, bytes, hflags))) {
         delete r;
         return KV_ERR_OOM;
     }
-    if (hipHostGetDevicePointer(&r->dev, r->host, 0) != hipSuccess) {
-        (void)hipGetLastError();
+    if (!HIP_OK(hipHostGetDevicePointer(&r->dev, r->host, 0))) {
         (void)hipHostFree(r->host);
         delete r;
         return KV_ERR_HIP;
@@ -636,5 +647,11 @@ const char *kv_strerror(int code)
 }
 
 int kv_version(void) { return 100; }
+
+int kv_last_hip_error(const char **where)
+{
+    if (where) *where = g_hip_where;
+    return g_hip_error;
+}
 
 }  // extern "C"

@@ -109,16 +109,17 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 
 int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t stream)
 {
-    const dim3 g(grid), b(kThreads);
-    if (direction == KV_GATHER && a.layout == KV_LAYER_FIRST)
-        hipLaunchKernelGGL((tile_copy<KV_GATHER, KV_LAYER_FIRST>), g, b, 0, stream, a);
-    else if (direction == KV_GATHER)
-        hipLaunchKernelGGL((tile_copy<KV_GATHER, KV_PAGE_FIRST>), g, b, 0, stream, a);
-    else if (a.layout == KV_LAYER_FIRST)
-        hipLaunchKernelGGL((tile_copy<KV_SCATTER, KV_LAYER_FIRST>), g, b, 0, stream, a);
+    const void *fn;
+    if (direction == KV_GATHER)
+        fn = a.layout == KV_LAYER_FIRST ? (const void *)&tile_copy<KV_GATHER, KV_LAYER_FIRST>
+                                        : (const void *)&tile_copy<KV_GATHER, KV_PAGE_FIRST>;
     else
-        hipLaunchKernelGGL((tile_copy<KV_SCATTER, KV_PAGE_FIRST>), g, b, 0, stream, a);
-    return (int)hipGetLastError();
+        fn = a.layout == KV_LAYER_FIRST ? (const void *)&tile_copy<KV_SCATTER, KV_LAYER_FIRST>
+                                        : (const void *)&tile_copy<KV_SCATTER, KV_PAGE_FIRST>;
+    Launch arg = a;
+    void *args[] = {&arg};
+    // hipLaunchKernel reports this launch's own status (not a stale runtime error).
+    return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 uint32_t default_grid(int64_t tiles)

@@ -22,6 +22,14 @@ if not os.path.exists(_LIB_PATH):
     raise ImportError(
         "libkvxfer.so is not built (%s); build it with __graft_entry__.build() or "
         "python -m paged_layout_transfer_amd._build" % _LIB_PATH)
+# A process must hold one HIP runtime.  PyTorch ships its own copy and its libraries
+# ask for it under a name that does not match an already loaded /opt/rocm copy, so
+# loading this library first would leave two runtimes, and the second sees no
+# device.  Loading torch first makes this library bind to torch's runtime.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(_LIB_PATH)
 
 # ---- constants (mirror include/kvxfer.h) ---------------------------------------------
@@ -105,19 +113,24 @@ _sig("kv_ring_slot", ctypes.c_int, _P, _I64, ctypes.POINTER(_P), ctypes.POINTER(
 _sig("kv_ring_destroy", ctypes.c_int, _P)
 _sig("kv_strerror", ctypes.c_char_p, ctypes.c_int)
 _sig("kv_version", ctypes.c_int)
+_sig("kv_last_hip_error", ctypes.c_int, ctypes.POINTER(ctypes.c_char_p))
 
 LIBRARY_PATH = _LIB_PATH
 EXPORTED = ("kv_pool_create", "kv_pool_destroy", "kv_pool_alloc_blocks", "kv_pool_free_blocks",
             "kv_pool_free_count", "kv_check_transfer", "kv_chunk_bytes", "kv_validate_targets",
             "kv_gather_chunks", "kv_scatter_chunks", "kv_pool_get_error", "kv_pool_timing_start",
             "kv_pool_timing_read", "kv_ring_create", "kv_ring_slot", "kv_ring_destroy",
-            "kv_strerror", "kv_version")
+            "kv_strerror", "kv_version", "kv_last_hip_error")
 
 
 class KvError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = int(code)
-        super().__init__("%s: %s (%d)" % (where, kv_strerror(code), code))
+        msg = "%s: %s (%d)" % (where, kv_strerror(code), code)
+        if self.code == KV_ERR_HIP:
+            err, call = kv_last_hip_error()
+            msg += "; last failing HIP call: %s -> hipError %d" % (call, err)
+        super().__init__(msg)
 
 
 def _check(rc: int, where: str) -> None:
@@ -279,6 +292,12 @@ def kv_strerror(code: int) -> str:
 
 def kv_version() -> int:
     return int(_lib.kv_version())
+
+
+def kv_last_hip_error() -> tuple[int, str]:
+    where = ctypes.c_char_p()
+    code = _lib.kv_last_hip_error(ctypes.byref(where))
+    return int(code), (where.value or b"").decode()
 
 
 def ring_host_array(ring: int, nbytes: int) -> np.ndarray:
