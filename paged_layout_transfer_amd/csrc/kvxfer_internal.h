@@ -25,7 +25,35 @@
 
 namespace kvx {
 
-constexpr int kWavesPerBlock = 4;  // 256-thread workgroups of four 64-lane wavefronts
+// Launch shape and copy policy; the defaults are the values measured best on MI355X.
+#ifndef KVX_WAVES_PER_BLOCK
+#define KVX_WAVES_PER_BLOCK 4  // 256-thread workgroups of four 64-lane wavefronts
+#endif
+#ifndef KVX_GRID_CAP
+#define KVX_GRID_CAP 32768     // workgroups per launch at most; more tiles loop
+#endif
+#ifndef KVX_GATHER_UNROLL
+#define KVX_GATHER_UNROLL 8    // 16-byte vectors per lane per group, gather
+#endif
+#ifndef KVX_GATHER_PIPELINE
+#define KVX_GATHER_PIPELINE 1  // next group's loads issued before this group's stores
+#endif
+#ifndef KVX_SCATTER_UNROLL
+#define KVX_SCATTER_UNROLL 16  // 16-byte vectors per lane per group, scatter
+#endif
+#ifndef KVX_SCATTER_PIPELINE
+#define KVX_SCATTER_PIPELINE 0
+#endif
+#ifndef KVX_TAIL_GROUP
+#define KVX_TAIL_GROUP 4       // vectors per lane per group after the full groups
+#endif
+#ifndef KVX_NT_LOAD
+#define KVX_NT_LOAD 1          // nontemporal loads
+#endif
+#ifndef KVX_NT_STORE
+#define KVX_NT_STORE 1         // nontemporal stores
+#endif
+constexpr int kWavesPerBlock = KVX_WAVES_PER_BLOCK;
 constexpr int kThreads = 64 * kWavesPerBlock;
 
 // Per-span launch record, uploaded once per call (64 bytes: one scalar 16-dword load).

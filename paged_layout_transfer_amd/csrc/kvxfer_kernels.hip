@@ -62,6 +62,39 @@ __device__ __forceinline__ SpanDev load_span(const KVX_CONST SpanDev *p)
     return r;
 }
 
+__device__ __forceinline__ u32x4 ld(const gvec *p)
+{
+#if KVX_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st(gvec *p, u32x4 v)
+{
+#if KVX_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// The remainder after the full groups, in groups of U vectors per lane; within a
+// group all loads are issued before the stores (lanes past the end are masked off).
+template <int U>
+__device__ __forceinline__ void copy_tail(const gvec *__restrict__ src, gvec *__restrict__ dst,
+                                          uint32_t nvec, uint32_t v)
+{
+    u32x4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (v + 64u * u < nvec) r[u] = ld(src + v + 64u * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (v + 64u * u < nvec) st(dst + v + 64u * u, r[u]);
+}
+
 // Copy nvec 16-byte vectors; lane i handles vectors i, i+64, i+128, ...
 template <int U>
 __device__ __forceinline__ void copy_run(const gvec *__restrict__ src, gvec *__restrict__ dst,
@@ -71,11 +104,70 @@ __device__ __forceinline__ void copy_run(const gvec *__restrict__ src, gvec *__r
     for (; v + 64u * (U - 1) < nvec; v += 64u * U) {
         u32x4 r[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) r[u] = __builtin_nontemporal_load(src + v + 64u * u);
+        for (int u = 0; u < U; ++u) r[u] = ld(src + v + 64u * u);
 #pragma unroll
-        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], dst + v + 64u * u);
+        for (int u = 0; u < U; ++u) st(dst + v + 64u * u, r[u]);
     }
-    for (; v < nvec; v += 64u) __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
+    for (; v < nvec; v += 64u * KVX_TAIL_GROUP) copy_tail<KVX_TAIL_GROUP>(src, dst, nvec, v);
+}
+
+// Software-pipelined variant: the loads of group k+1 are issued before the stores
+// of group k, so each lane keeps 2U vectors in flight.
+template <int U>
+__device__ __forceinline__ void copy_run_pipelined(const gvec *__restrict__ src,
+                                                   gvec *__restrict__ dst, uint32_t nvec,
+                                                   uint32_t lane)
+{
+    constexpr uint32_t G = 64u * U;
+    uint32_t v = lane;
+    if (v + G - 64u < nvec) {
+        u32x4 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = ld(src + v + 64u * u);
+        for (;;) {
+            if (v + 2 * G - 64u >= nvec) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) b[u] = ld(src + v + G + 64u * u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) st(dst + v + 64u * u, a[u]);
+            v += G;
+            if (v + 2 * G - 64u >= nvec) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) a[u] = b[u];
+                break;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) a[u] = ld(src + v + G + 64u * u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) st(dst + v + 64u * u, b[u]);
+            v += G;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) st(dst + v + 64u * u, a[u]);
+        v += G;
+    }
+    for (; v < nvec; v += 64u * KVX_TAIL_GROUP) copy_tail<KVX_TAIL_GROUP>(src, dst, nvec, v);
+}
+
+// Copy loop per direction.  Gather reads scattered pool pages and writes the chunk
+// sequentially; scatter reads the chunk sequentially and writes scattered pages.
+template <int DIR>
+__device__ __forceinline__ void copy_tile(const gvec *__restrict__ src, gvec *__restrict__ dst,
+                                          uint32_t nvec, uint32_t lane)
+{
+    if (DIR == KV_GATHER) {
+#if KVX_GATHER_PIPELINE
+        copy_run_pipelined<KVX_GATHER_UNROLL>(src, dst, nvec, lane);
+#else
+        copy_run<KVX_GATHER_UNROLL>(src, dst, nvec, lane);
+#endif
+    } else {
+#if KVX_SCATTER_PIPELINE
+        copy_run_pipelined<KVX_SCATTER_UNROLL>(src, dst, nvec, lane);
+#else
+        copy_run<KVX_SCATTER_UNROLL>(src, dst, nvec, lane);
+#endif
+    }
 }
 
 template <int DIR, int LAYOUT>
@@ -102,8 +194,8 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         uint8_t *pool = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
         uint8_t *chunk = a.chunk_base + t.chunk_off;
         const uint32_t nvec = t.nbytes >> 4;
-        if (DIR == KV_GATHER) copy_run<8>(as_global(pool), as_global(chunk), nvec, lane);
-        else copy_run<8>(as_global(chunk), as_global(pool), nvec, lane);
+        if (DIR == KV_GATHER) copy_tile<DIR>(as_global(pool), as_global(chunk), nvec, lane);
+        else copy_tile<DIR>(as_global(chunk), as_global(pool), nvec, lane);
     }
 }
 
@@ -124,11 +216,8 @@ int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t 
 
 uint32_t default_grid(int64_t tiles)
 {
-    // 256 CUs x 8 resident 4-wave workgroups = 2048; twice that keeps the queue fed
-    // while the first wave of workgroups drains.
-    const int64_t cap = 4096;
     const int64_t need = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    return (uint32_t)(need < cap ? need : cap);
+    return (uint32_t)(need < KVX_GRID_CAP ? need : KVX_GRID_CAP);
 }
 
 }  // namespace kvx
