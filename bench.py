@@ -212,27 +212,71 @@ def hbm_leg(args, dev):
 
 
 def cpu_baseline(res, budget_s):
-    """The oracle, as it is, on the first layers of the same gather."""
+    """The oracle, as it is, on the same step (gather then scatter of the whole
+    request), layer by layer until the time budget is spent."""
     import numpy as np
     import oracle
+    from paged_layout_transfer_amd import workloads as W
     w, pool, chunks = res["w"], res["pool"], res["chunks_spec"]
     regions = res["host_sample"]
-    from paged_layout_transfer_amd import workloads as W
     spans = [(t, t0, t1, fc) for t, (t0, t1), fc in
              zip(w["block_tables"], w["requests"], W.staging_plan(w)["first_chunk"])]
     buf = np.zeros(chunks["slot_bytes"] * chunks["n_slots"], dtype=np.uint8)
-    moved, spent, layers = 0, 0.0, 0
-    for l in range(res["host_sample_layers"]):
-        t0 = time.perf_counter()
-        moved += oracle.gather(pool, regions, spans, chunks, buf, only_layers=(l, l + 1))
-        spent += time.perf_counter() - t0
-        layers += 1
-        if spent >= budget_s:
-            break
+    moved, spent, done = 0, 0.0, []
+    for name, fn in (("gather", oracle.gather), ("scatter", oracle.scatter)):
+        n = 0
+        for l in range(res["host_sample_layers"]):
+            if spent >= budget_s:
+                break
+            t0 = time.perf_counter()
+            moved += fn(pool, regions, spans, chunks, buf, only_layers=(l, l + 1))
+            spent += time.perf_counter() - t0
+            n += 1
+        done.append("%s of %d/%d layers" % (name, n, pool["num_layers"]))
     return dict(value=round(moved / spent / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample="gather of layers 0..%d of the %s workload (%d of %d layers, %.3f GB moved), "
-                       "single-threaded C oracle, %.1f s" % (layers - 1, res["name"], layers,
-                                                            pool["num_layers"], moved / 1e9, spent))
+                sample="%s of the %s workload (%.3f GB moved), single-threaded C oracle, %.1f s" % (
+                    " then ".join(done), res["name"], moved / 1e9, spent))
+
+
+def other_workloads(dev, names, reps):
+    """Kernel-time throughput of the other HBM-staged workloads (parity for them is
+    covered by the test suite); each payload byte is read once and written once."""
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    from paged_layout_transfer_amd import workloads as W
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name in names:
+        w, pool = resolve(name)
+        plan = W.staging_plan(w)
+        L, KV = pool["num_layers"], pool["num_kv"]
+        P = DevicePool(pool, dev)
+        S = torch.empty(plan["slot_bytes"] * plan["n_chunks"], dtype=torch.uint8, device=dev)
+        tabs = [torch.from_numpy(t).to(dev) for t in w["block_tables"]]
+        spans = K.make_spans([(tb, tb.numel(), t0, t1, fc) for tb, (t0, t1), fc in
+                              zip(tabs, w["requests"], plan["first_chunk"])])
+        spec = K.make_chunk_spec(w["layout"], w["chunk_layers"], w["chunk_tokens"], 0, L, S,
+                                 plan["slot_bytes"], plan["n_chunks"])
+        info = K.kv_check_transfer(P.desc, spans, spec)
+        row = dict(payload_bytes=info.payload_bytes, requests=len(w["requests"]), tiles=info.tiles)
+        for dn, fn in (("gather", K.kv_gather_chunks), ("scatter", K.kv_scatter_chunks)):
+            fn(P.h, spans, spec, stream)
+            torch.cuda.synchronize()
+            K.kv_pool_timing_start(P.h)
+            for _ in range(reps):
+                fn(P.h, spans, spec, stream)
+            ms, n = K.kv_pool_timing_read(P.h)
+            assert K.kv_pool_get_error(P.h, stream) == 0
+            t = ms / n * 1e-3
+            row[dn] = dict(kernel_ms=round(ms / n, 4), gbs=round(info.payload_bytes / t / 1e9, 1),
+                           hbm_frac=round(2 * info.payload_bytes / t / 1e9 / HBM_PEAK_GBS, 4))
+        out[name] = row
+        log("%s: gather %.1f%%, scatter %.1f%% of HBM peak" % (
+            name, 100 * row["gather"]["hbm_frac"], 100 * row["scatter"]["hbm_frac"]))
+        P.close()
+        del P, S, tabs
+        torch.cuda.empty_cache()
+    return out
 
 
 def host_leg(args, dev):
@@ -366,10 +410,11 @@ def main():
     ap.add_argument("--no-host-path", dest="host_path", action="store_false")
     ap.add_argument("--host-windows", type=int, default=0, help="0 = the whole 80-layer context")
     ap.add_argument("--ring-layers", type=int, default=4, help="layers per ring window")
-    ap.add_argument("--sweep", action="store_true", help="sweep max_workgroups on the host path")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
-    ap.add_argument("--cpu-layers", type=int, default=8)
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-layers", type=int, default=32)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-other-workloads", dest="others", action="store_false")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -390,6 +435,7 @@ def main():
     cpu = cpu_baseline(res, args.cpu_budget) if args.cpu_baseline else None
     res.pop("host_sample", None)
     host = host_leg(args, dev) if args.host_path else None
+    others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv"], 5) if args.others else None
 
     w = res["w"]
     traffic = traffic_for(2 * res["payload"])
@@ -428,6 +474,7 @@ def main():
         "d2d_memcpy_gbs": round(res["d2d_copy_gbs"], 1),
         "parity": res["parity"],
         "host_path": host,
+        "other_workloads": others,
     }
     print(json.dumps(out), flush=True)
 
