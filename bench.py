@@ -371,15 +371,16 @@ def host_leg(args, dev):
                              bytes=moved, kernel_ms=ms, launches=n)
         sweep = {}
         if args.sweep:
-            for wg in (1, 2, 4, 8, 16, 32, 0):
+            for wg in (1, 2, 4, 8, 16, 32, 64, 32768):
                 row = {}
                 for name, fn in (("scatter", K.kv_scatter_chunks), ("gather", K.kv_gather_chunks)):
                     ms, n = run_pass(fn, 1, wg)
-                    row[name] = payload_layer * win_layers / (ms * 1e-3) / 1e9
-                sweep[str(wg) if wg else "full"] = row
+                    row[name] = round(payload_layer * win_layers / (ms * 1e-3) / 1e9, 2)
+                sweep[str(wg)] = row
         return dict(workload="llama70b: 80 layers x K/V x 8 x 128 bf16, 16-token pages, one 131072-token "
                              "request, 2 MiB chunks (1 layer x 512 tokens) through a pinned host ring of "
-                             "%d slots (%d layers per window)" % (n_slots, win_layers),
+                             "%d slots (%d layers per window); library default grid for host staging "
+                             "(16 workgroups); sweep_gbs keys are max_workgroups" % (n_slots, win_layers),
                     payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep, **out)
     finally:
         K.kv_ring_destroy(ring)

@@ -151,9 +151,10 @@ typedef struct {
     void *base;            /* device-visible staging: HBM or mapped pinned host memory */
     int64_t slot_bytes;    /* bytes per staging slot, >= the largest chunk of the call */
     int64_t n_slots;       /* slots at base; chunk c uses slot c mod n_slots */
-    int32_t max_workgroups;/* 0 = library default grid; > 0 caps the grid to that many
-                              workgroups (host-link paths need few: Strata guide,
-                              "Non-Intrusive Resource Sizing") */
+    int32_t max_workgroups;/* 0 = library default grid: the whole chip when base is device
+                              memory, 16 workgroups of 256 threads when it is host memory
+                              (a host-link-bound copy needs few: Strata guide,
+                              "Non-Intrusive Resource Sizing"); > 0 caps the grid */
     int32_t flags;         /* KV_FLAG_* */
 } kv_chunk_spec;
 

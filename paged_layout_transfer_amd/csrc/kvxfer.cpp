@@ -262,6 +262,9 @@ struct kv_pool {
     kvx::SpanDev *h_desc = nullptr;   // pinned host mirror
     hipEvent_t desc_ev[kDescSlots] = {};
     int desc_next = 0;
+    // staging-memory kind of the last staging base seen
+    const void *last_base = nullptr;
+    bool last_base_host = false;
     // timing
     bool timing = false;
     int n_timed = 0;
@@ -340,6 +343,24 @@ int validate_tables(kv_pool *p, const kv_span *spans, int32_t n_spans, int direc
     return kv_validate_targets(&p->desc, local.data(), n_spans, ptrs.data(), direction);
 }
 
+// Whether the staging memory is host memory (pinned, mapped): those transfers are
+// bound by the host link, which a few workgroups saturate, so by default they get a
+// small grid and leave the rest of the chip to compute (Strata guide,
+// "Non-Intrusive Resource Sizing").  The answer is cached per staging address.
+bool staging_in_host_memory(kv_pool *p, const void *base)
+{
+    if (base != p->last_base) {
+        hipPointerAttribute_t attr;
+        p->last_base_host = false;
+        if (hipPointerGetAttributes(&attr, base) == hipSuccess)
+            p->last_base_host = attr.type == hipMemoryTypeHost;
+        else
+            (void)hipGetLastError();  // unknown to the runtime: treat as device memory
+        p->last_base = base;
+    }
+    return p->last_base_host;
+}
+
 int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
              hipStream_t stream, int direction)
 {
@@ -376,6 +397,7 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
 
     uint32_t grid = kvx::default_grid(info.tiles);
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
+    else if (staging_in_host_memory(p, spec->base)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
 
     const bool timed = p->timing && p->n_timed < kMaxTimed;
     if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;

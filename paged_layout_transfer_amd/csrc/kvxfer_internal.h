@@ -32,6 +32,9 @@ namespace kvx {
 #ifndef KVX_GRID_CAP
 #define KVX_GRID_CAP 32768     // workgroups per launch at most; more tiles loop
 #endif
+#ifndef KVX_HOST_GRID_CAP
+#define KVX_HOST_GRID_CAP 16   // default workgroups when the staging is host memory
+#endif
 #ifndef KVX_GATHER_UNROLL
 #define KVX_GATHER_UNROLL 8    // 16-byte vectors per lane per group, gather
 #endif
