@@ -395,7 +395,8 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     a.spans = dd;
     a.err = p->d_err;
 
-    uint32_t grid = kvx::default_grid(info.tiles);
+    a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
+    uint32_t grid = kvx::default_grid(info.tiles << a.split_shift);
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
     else if (staging_in_host_memory(p, spec->base)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
 

@@ -179,8 +179,12 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     const KVX_CONST SpanDev *spans = as_const(a.spans);
     uint32_t s = 0;
 
-    for (int64_t tile = (int64_t)blockIdx.x * kWavesPerBlock + wave; tile < a.total_tiles;
-         tile += step) {
+    // Work item = one of a tile's 2^split_shift parts; the waves of a workgroup take
+    // consecutive items, so a split tile is copied by neighbouring waves.
+    const uint32_t shift = a.split_shift;
+    const int64_t items = a.total_tiles << shift;
+    for (int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wave; item < items; item += step) {
+        const int64_t tile = item >> shift;
         // tiles only grow along the loop, so the span search starts at the last span
         s = find_span(spans, s, a.n_spans, tile);
         const SpanDev sp = load_span(spans + s);
@@ -191,11 +195,12 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
             if (lane == 0) atomicOr(a.err, KV_DEVERR_BLOCK_RANGE);
             continue;
         }
-        uint8_t *pool = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
-        uint8_t *chunk = a.chunk_base + t.chunk_off;
-        const uint32_t nvec = t.nbytes >> 4;
-        if (DIR == KV_GATHER) copy_tile<DIR>(as_global(pool), as_global(chunk), nvec, lane);
-        else copy_tile<DIR>(as_global(chunk), as_global(pool), nvec, lane);
+        uint32_t first, count;
+        part_range(t.nbytes >> 4, (uint32_t)(item & ((1 << shift) - 1)), 1u << shift, &first, &count);
+        uint8_t *pool = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride + first * 16ll;
+        uint8_t *chunk = a.chunk_base + t.chunk_off + first * 16ll;
+        if (DIR == KV_GATHER) copy_tile<DIR>(as_global(pool), as_global(chunk), count, lane);
+        else copy_tile<DIR>(as_global(chunk), as_global(pool), count, lane);
     }
 }
 
@@ -214,9 +219,9 @@ int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t 
     return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
-uint32_t default_grid(int64_t tiles)
+uint32_t default_grid(int64_t items)
 {
-    const int64_t need = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t need = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     return (uint32_t)(need < KVX_GRID_CAP ? need : KVX_GRID_CAP);
 }
 

@@ -34,26 +34,29 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     for (int32_t i = 0; i < n_spans; ++i)
         if (spans[i].t_end > spans[i].t_begin) tlen.push_back(spans[i].table_len);
 
-    uint32_t grid = kvx::default_grid(info.tiles);
+    a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
+    uint32_t grid = kvx::default_grid(info.tiles << a.split_shift);
     if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
         grid = (uint32_t)spec->max_workgroups;
     *grid_out = grid;
-    std::vector<uint8_t> seen((size_t)info.tiles, 0);
+    const uint32_t split = 1u << a.split_shift;
+    const int64_t items = info.tiles * split;
+    std::vector<uint8_t> seen((size_t)items, 0);
     const int64_t step = (int64_t)grid * kvx::kWavesPerBlock;
     const int64_t nreg = (int64_t)d->num_layers * d->num_kv;
 
     for (uint32_t b = 0; b < grid; ++b) {
         for (int w = 0; w < kvx::kWavesPerBlock; ++w) {
             uint32_t s = 0;
-            for (int64_t tile = (int64_t)b * kvx::kWavesPerBlock + w; tile < a.total_tiles;
-                 tile += step) {
+            for (int64_t item = (int64_t)b * kvx::kWavesPerBlock + w; item < items; item += step) {
+                const int64_t tile = item / split;
                 s = kvx::find_span(records, s, n_rec, tile);
                 const kvx::SpanDev &sp = records[s];
                 if (tile < sp.tile_begin) { ++*violations; continue; }
                 const kvx::TileRef t = (a.layout == KV_LAYER_FIRST)
                                            ? kvx::resolve_tile<KV_LAYER_FIRST>(a, sp, tile)
                                            : kvx::resolve_tile<KV_PAGE_FIRST>(a, sp, tile);
-                if (seen[tile]++) { ++*violations; continue; }
+                if (seen[item]++) { ++*violations; continue; }
                 if ((int64_t)t.page >= tlen[s] || (int64_t)t.region >= nreg || t.nbytes == 0 ||
                     t.nbytes % 16 != 0 || t.chunk_off < 0 ||
                     t.chunk_off + (int64_t)t.nbytes > staging_bytes) {
@@ -67,16 +70,18 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
                     ++*violations;
                     continue;
                 }
-                if (copy) {
-                    uint8_t *pool = static_cast<uint8_t *>(d->bases[t.region]) + poff;
-                    uint8_t *chunk = a.chunk_base + t.chunk_off;
-                    if (direction == KV_GATHER) std::memcpy(chunk, pool, t.nbytes);
-                    else std::memcpy(pool, chunk, t.nbytes);
+                uint32_t first, count;
+                kvx::part_range(t.nbytes >> 4, (uint32_t)(item % split), split, &first, &count);
+                if (copy && count) {
+                    uint8_t *pool = static_cast<uint8_t *>(d->bases[t.region]) + poff + first * 16ll;
+                    uint8_t *chunk = a.chunk_base + t.chunk_off + first * 16ll;
+                    if (direction == KV_GATHER) std::memcpy(chunk, pool, count * 16ull);
+                    else std::memcpy(pool, chunk, count * 16ull);
                 }
             }
         }
     }
-    for (int64_t i = 0; i < info.tiles; ++i)
+    for (int64_t i = 0; i < items; ++i)
         if (seen[i] != 1) ++*violations;
     return KV_OK;
 }

@@ -25,10 +25,9 @@ from paged_layout_transfer_amd import workloads as W
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-@pytest.fixture(scope="module")
-def emu(tmp_path_factory):
+def _build_emu(tmp_path_factory, defines=()):
     out = str(tmp_path_factory.mktemp("emu") / "libemu.so")
-    cmd = [_build.HIPCC, *[f for f in _build.FLAGS if f != "-fvisibility=hidden"],
+    cmd = [_build.HIPCC, *[f for f in _build.FLAGS if f != "-fvisibility=hidden"], *defines,
            "-I", os.path.join(_build.ROOT, "include"), "-I", _build.CSRC,
            *_build.SOURCES, os.path.join(HERE, "kernel_emu.cpp"), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
@@ -39,6 +38,18 @@ def emu(tmp_path_factory):
                                  ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     return lib
+
+
+@pytest.fixture(scope="module")
+def emu(tmp_path_factory):
+    return _build_emu(tmp_path_factory)
+
+
+@pytest.fixture(scope="module")
+def emu_split(tmp_path_factory):
+    """The same walk with small parts, so tiles are split between 2-4 waves in both directions."""
+    return _build_emu(tmp_path_factory, ("-DKVX_GATHER_PART_BYTES=256", "-DKVX_SCATTER_PART_BYTES=128",
+                                         "-DKVX_GATHER_SPLIT_MIN=512", "-DKVX_SCATTER_SPLIT_MIN=256"))
 
 
 def _emulate(lib, direction, pool, spans, chunks, bases, region_bytes, staging_ptr, staging_bytes,
@@ -87,6 +98,13 @@ def test_emulated_kernel_matches_oracle_medium(emu, seed):
     pool, spans, chunks = cases.make_case(np.random.default_rng(20_000 + seed), tok_multiple=16,
                                           medium=True, max_bytes=48 << 20)
     _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 4))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_emulated_split_tiles_match_oracle(emu_split, seed):
+    pool, spans, chunks = cases.make_case(np.random.default_rng(25_000 + seed), tok_multiple=16,
+                                          medium=True, max_bytes=48 << 20)
+    _copy_case(emu_split, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
 
 
 FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv"]
