@@ -176,6 +176,25 @@ def hbm_leg(args, dev):
         per_dir[name] = dict(kernel_ms=ms / n, gbs=payload / (ms / n * 1e-3) / 1e9,
                              hbm_frac=2 * payload / (ms / n * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
+    # the conventional engine on the same call: one hipMemcpyAsync per tile
+    dma = {}
+    if args.dma_baseline:
+        tabs_h = [np.ascontiguousarray(t, dtype=np.int32) for t in w["block_tables"]]
+        spans_dma = K.make_spans([(t.ctypes.data, t.size, t0, t1, fc) for t, (t0, t1), fc in
+                                  zip(tabs_h, w["requests"], plan["first_chunk"])])
+        for name, fn in (("gather", K.kv_gather_chunks_dma), ("scatter", K.kv_scatter_chunks_dma)):
+            torch.cuda.synchronize()
+            K.kv_pool_timing_start(P.h)
+            t0 = time.perf_counter()
+            fn(P.h, spans_dma, spec, stream)
+            submit = time.perf_counter() - t0
+            ms, n = K.kv_pool_timing_read(P.h)
+            dma[name] = dict(gbs=round(payload / (ms * 1e-3) / 1e9, 2), ms=round(ms, 2),
+                             copies=info.tiles, host_submit_ms=round(submit * 1e3, 2),
+                             hbm_frac=round(2 * payload / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        log("per-tile hipMemcpyAsync: gather %.1f GB/s, scatter %.1f GB/s" % (
+            dma["gather"]["gbs"], dma["scatter"]["gbs"]))
+
     # device-to-device memcpy of the same payload, for context
     import torch as _t
     a = S
@@ -197,7 +216,7 @@ def hbm_leg(args, dev):
         payload=payload, ms_per_step=ms_per_step, kernel_ms_avg=kern_ms / launches, launches=launches,
         value=2 * payload / (ms_per_step * 1e-3) / 1e9,
         achieved=2 * payload / avg_kernel_s / 1e9, per_dir=per_dir, parity=parity,
-        d2d_copy_gbs=d2d_gbs, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
+        d2d_copy_gbs=d2d_gbs, dma=dma, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
         name=args.workload)
     # keep host copies for the CPU baseline (first layers), then free the device
     res["host_sample"] = None
@@ -360,6 +379,25 @@ def host_leg(args, dev):
             assert K.kv_pool_get_error(P.h, stream) == 0
             return ms, n
 
+        dma = {}
+        if args.dma_baseline:
+            tab_h = np.ascontiguousarray(w["block_tables"][0], dtype=np.int32)
+            spans_dma = K.make_spans([(tab_h.ctypes.data, tab_h.size, 0, T, 0)])
+            for name, fn, ref in (("scatter", K.kv_scatter_chunks_dma, "h2d"),
+                                  ("gather", K.kv_gather_chunks_dma, "d2h")):
+                torch.cuda.synchronize()
+                K.kv_pool_timing_start(P.h)
+                t0 = time.perf_counter()
+                fn(P.h, spans_dma, spec_for(0), stream)
+                submit = time.perf_counter() - t0
+                ms, n = K.kv_pool_timing_read(P.h)
+                moved = payload_layer * win_layers
+                dma[name] = dict(gbs=round(moved / (ms * 1e-3) / 1e9, 2), link_frac=round(moved / (ms * 1e-3) / 1e9 / link[ref], 4),
+                                 ms=round(ms, 2), copies=win_layers * KV * (T // w["block_size"]),
+                                 host_submit_ms=round(submit * 1e3, 2), bytes=moved)
+            log("per-tile hipMemcpyAsync over the host link: scatter %.1f GB/s, gather %.1f GB/s" % (
+                dma["scatter"]["gbs"], dma["gather"]["gbs"]))
+
         windows = L // win_layers if args.host_windows <= 0 else args.host_windows
         out = {}
         for name, fn, ref in (("scatter", K.kv_scatter_chunks, "h2d"), ("gather", K.kv_gather_chunks, "d2h")):
@@ -381,7 +419,8 @@ def host_leg(args, dev):
                              "request, 2 MiB chunks (1 layer x 512 tokens) through a pinned host ring of "
                              "%d slots (%d layers per window); library default grid for host staging "
                              "(16 workgroups); sweep_gbs keys are max_workgroups" % (n_slots, win_layers),
-                    payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep, **out)
+                    payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep,
+                    per_tile_dma=dma, **out)
     finally:
         K.kv_ring_destroy(ring)
         P.close()
@@ -416,6 +455,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-other-workloads", dest="others", action="store_false")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
+    ap.add_argument("--no-dma-baseline", dest="dma_baseline", action="store_false",
+                    help="skip the per-tile hipMemcpyAsync comparison")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -473,6 +514,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res["per_dir"].items()},
         "d2d_memcpy_gbs": round(res["d2d_copy_gbs"], 1),
+        "per_tile_dma": res["dma"],
         "parity": res["parity"],
         "host_path": host,
         "other_workloads": others,

@@ -223,6 +223,21 @@ KV_API int kv_gather_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans
 KV_API int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                       const kv_chunk_spec *spec, hipStream_t stream);
 
+/* The conventional engine, for comparison: the same transfer done by the copy
+ * engine as one hipMemcpyAsync per (layer, kv, page) tile, issued from the host on
+ * `stream` -- the per-page DMA loop whose submission overhead the Strata guide
+ * measures ("The Conflict Between PagedAttention and Transfer Efficiency",
+ * paged-fragmentation figure, and the framework comparison table).  Same data
+ * model, validation and results as kv_gather_chunks / kv_scatter_chunks, except
+ * that each spans[i].block_table is a HOST array (the host issues the copies), and
+ * every block id of the call is checked on the host before any copy is issued
+ * (KV_ERR_RANGE; for scatter also KV_ERR_DUP).  Host work is O(tiles).  The tables
+ * are read during the call only. */
+KV_API int kv_gather_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                                const kv_chunk_spec *spec, hipStream_t stream);
+KV_API int kv_scatter_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                                 const kv_chunk_spec *spec, hipStream_t stream);
+
 /* Synchronizes `stream`, then reads and clears the pool's sticky device error
  * word.  *out_bits receives KV_DEVERR_* bits (0 if none); the return value is
  * KV_ERR_DEVICE when any bit was set, else KV_OK. */

@@ -412,6 +412,48 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     return KV_OK;
 }
 
+// One hipMemcpyAsync per tile, addresses from the same tile resolution the kernel
+// uses, block ids from host tables.
+int transfer_dma(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
+                 hipStream_t stream, int direction)
+{
+    if (!p) return KV_ERR_ARG;
+    kv_transfer_info info;
+    int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
+    if (rc) return rc;
+    if (info.tiles == 0) return KV_OK;
+    std::vector<const int32_t *> tables(n_spans);
+    for (int32_t i = 0; i < n_spans; ++i) tables[i] = spans[i].block_table;
+    rc = kv_validate_targets(&p->desc, spans, n_spans, tables.data(), direction);
+    if (rc) return rc;
+    kvx::Launch a;
+    uint32_t n_rec = 0;
+    std::vector<kvx::SpanDev> rec(KV_MAX_SPANS);
+    rc = prepare_with(&p->desc, spans, n_spans, spec, rec.data(), &n_rec, &a, &info, p->plans.data(),
+                      p->ranges.data());
+    if (rc) return rc;
+    const bool timed = p->timing && p->n_timed < kMaxTimed;
+    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
+    uint32_t s = 0;
+    for (int64_t tile = 0; tile < a.total_tiles; ++tile) {
+        s = kvx::find_span(rec.data(), s, n_rec, tile);
+        const kvx::SpanDev &sp = rec[s];
+        const kvx::TileRef t = a.layout == KV_LAYER_FIRST
+                                   ? kvx::resolve_tile<KV_LAYER_FIRST>(a, sp, tile)
+                                   : kvx::resolve_tile<KV_PAGE_FIRST>(a, sp, tile);
+        uint8_t *pool = static_cast<uint8_t *>(p->bases[t.region]) + (int64_t)sp.table[t.page] * a.block_stride;
+        uint8_t *chunk = a.chunk_base + t.chunk_off;
+        void *dst = direction == KV_GATHER ? (void *)chunk : (void *)pool;
+        const void *src = direction == KV_GATHER ? (const void *)pool : (const void *)chunk;
+        if (!HIP_OK(hipMemcpyAsync(dst, src, t.nbytes, hipMemcpyDefault, stream))) return KV_ERR_HIP;
+    }
+    if (timed) {
+        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;
+        ++p->n_timed;
+    }
+    return KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -559,6 +601,18 @@ int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                       const kv_chunk_spec *spec, hipStream_t stream)
 {
     return transfer(pool, spans, n_spans, spec, stream, KV_SCATTER);
+}
+
+int kv_gather_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                         const kv_chunk_spec *spec, hipStream_t stream)
+{
+    return transfer_dma(pool, spans, n_spans, spec, stream, KV_GATHER);
+}
+
+int kv_scatter_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,
+                          const kv_chunk_spec *spec, hipStream_t stream)
+{
+    return transfer_dma(pool, spans, n_spans, spec, stream, KV_SCATTER);
 }
 
 int kv_pool_get_error(kv_pool *p, hipStream_t stream, int32_t *out_bits)

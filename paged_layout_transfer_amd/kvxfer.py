@@ -105,6 +105,8 @@ _sig("kv_validate_targets", ctypes.c_int, ctypes.POINTER(kv_pool_desc), ctypes.P
      ctypes.POINTER(_P), _I32)
 _sig("kv_gather_chunks", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
 _sig("kv_scatter_chunks", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
+_sig("kv_gather_chunks_dma", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
+_sig("kv_scatter_chunks_dma", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
 _sig("kv_pool_get_error", ctypes.c_int, _P, _P, ctypes.POINTER(_I32))
 _sig("kv_pool_timing_start", ctypes.c_int, _P)
 _sig("kv_pool_timing_read", ctypes.c_int, _P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64))
@@ -118,7 +120,8 @@ _sig("kv_last_hip_error", ctypes.c_int, ctypes.POINTER(ctypes.c_char_p))
 LIBRARY_PATH = _LIB_PATH
 EXPORTED = ("kv_pool_create", "kv_pool_destroy", "kv_pool_alloc_blocks", "kv_pool_free_blocks",
             "kv_pool_free_count", "kv_check_transfer", "kv_chunk_bytes", "kv_validate_targets",
-            "kv_gather_chunks", "kv_scatter_chunks", "kv_pool_get_error", "kv_pool_timing_start",
+            "kv_gather_chunks", "kv_scatter_chunks", "kv_gather_chunks_dma", "kv_scatter_chunks_dma",
+            "kv_pool_get_error", "kv_pool_timing_start",
             "kv_pool_timing_read", "kv_ring_create", "kv_ring_slot", "kv_ring_destroy",
             "kv_strerror", "kv_version", "kv_last_hip_error")
 
@@ -248,6 +251,18 @@ def kv_gather_chunks(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None
 def kv_scatter_chunks(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
     _check(_lib.kv_scatter_chunks(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
            "kv_scatter_chunks")
+
+
+def kv_gather_chunks_dma(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
+    """Per-tile hipMemcpyAsync gather; the spans' block tables are host arrays."""
+    _check(_lib.kv_gather_chunks_dma(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
+           "kv_gather_chunks_dma")
+
+
+def kv_scatter_chunks_dma(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
+    """Per-tile hipMemcpyAsync scatter; the spans' block tables are host arrays."""
+    _check(_lib.kv_scatter_chunks_dma(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
+           "kv_scatter_chunks_dma")
 
 
 def kv_pool_get_error(pool: int, stream=None) -> int:

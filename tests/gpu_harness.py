@@ -26,11 +26,12 @@ def describe(label, direction, pool, spans, chunks, extra=""):
 def run_transfer(direction: int, pool: dict, spans, chunks: dict, regions_np: np.ndarray,
                  staging_np: np.ndarray, *, ring: bool = False, ring_flags: int = K.KV_RING_COHERENT,
                  max_workgroups: int = 0, flags: int = 0, label: str = "",
-                 region_views=None):
+                 region_views=None, dma: bool = False):
     """One gather or scatter.  regions_np is [L*KV, bytes] (rows are the regions) or,
     with region_views=(offsets, buffer_bytes), a flat buffer whose regions start at
     the given byte offsets (interleaved pools).  Returns (regions_after,
-    staging_after, device_error_bits)."""
+    staging_after, device_error_bits).  dma=True runs the per-tile copy-engine entry
+    points, which take host block tables."""
     dev = device()
     L, KV = pool["num_layers"], pool["num_kv"]
     buf = torch.from_numpy(np.ascontiguousarray(regions_np)).to(dev)
@@ -53,8 +54,13 @@ def run_transfer(direction: int, pool: dict, spans, chunks: dict, regions_np: np
         base = stg.data_ptr()
     desc = K.make_pool_desc(L, KV, pool["num_heads"], pool["head_dim"], pool["elem_bytes"],
                             pool["block_size"], pool["num_blocks"], pool["block_stride"], bases)
-    sp = K.make_spans([(tb.data_ptr(), tb.numel(), t0, t1, fc)
-                       for tb, (_, t0, t1, fc) in zip(tabs, spans)])
+    host_tabs = [np.ascontiguousarray(t, dtype=np.int32) for t, _, _, _ in spans]
+    if dma:
+        sp = K.make_spans([(ht.ctypes.data, ht.size, t0, t1, fc)
+                           for ht, (_, t0, t1, fc) in zip(host_tabs, spans)])
+    else:
+        sp = K.make_spans([(tb.data_ptr(), tb.numel(), t0, t1, fc)
+                           for tb, (_, t0, t1, fc) in zip(tabs, spans)])
     spec = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"],
                              chunks["layer_begin"], chunks["layer_end"], base,
                              chunks["slot_bytes"], chunks["n_slots"], max_workgroups, flags)
@@ -62,9 +68,12 @@ def run_transfer(direction: int, pool: dict, spans, chunks: dict, regions_np: np
     try:
         torch.cuda.synchronize()
         print(describe(label, direction, pool, spans, chunks,
-                       "ring=%s wg=%d" % (ring, max_workgroups)), flush=True)
+                       "ring=%s wg=%d dma=%s" % (ring, max_workgroups, dma)), flush=True)
         stream = torch.cuda.current_stream()
-        fn = K.kv_gather_chunks if direction == K.KV_GATHER else K.kv_scatter_chunks
+        if dma:
+            fn = K.kv_gather_chunks_dma if direction == K.KV_GATHER else K.kv_scatter_chunks_dma
+        else:
+            fn = K.kv_gather_chunks if direction == K.KV_GATHER else K.kv_scatter_chunks
         fn(h, sp, spec, stream)
         bits = K.kv_pool_get_error(h, stream)
         torch.cuda.synchronize()

@@ -264,3 +264,23 @@ def test_validate_targets():
     # only the pages a span touches are checked: the prefix page before t_begin may be anything
     tail = K.make_spans([(0, 4, 8, 16, 0)])
     K.kv_validate_targets(d, tail, [np.array([-5, 99, 6, 7], dtype=np.int32)], K.KV_SCATTER)
+
+
+def test_per_tile_dma_validates_host_tables_before_any_hip_call():
+    d = _desc(N=8, bs=4, D=8, H=1, E=2)  # 16-byte tokens
+    pool = K.kv_pool_create(d)
+    try:
+        bad = np.array([0, 1, 8, 3], dtype=np.int32)
+        dup = np.array([0, 1, 1, 3], dtype=np.int32)
+        spec = _spec(chunk_layers=2, chunk_tokens=16, slot_bytes=2 * 2 * 16 * 16, n_slots=1)
+        for tbl, fn, code in ((bad, K.kv_gather_chunks_dma, K.KV_ERR_RANGE),
+                              (dup, K.kv_scatter_chunks_dma, K.KV_ERR_DUP)):
+            with pytest.raises(K.KvError) as e:
+                fn(pool, K.make_spans([(tbl.ctypes.data, 4, 0, 16, 0)]), spec)
+            assert e.value.code == code
+        good = np.array([0, 1, 2, 3], dtype=np.int32)
+        with pytest.raises(K.KvError) as e:   # valid: gets as far as the first copy, no device here
+            K.kv_gather_chunks_dma(pool, K.make_spans([(good.ctypes.data, 4, 0, 16, 0)]), spec)
+        assert e.value.code == K.KV_ERR_HIP
+    finally:
+        K.kv_pool_destroy(pool)

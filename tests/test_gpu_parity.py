@@ -228,3 +228,28 @@ def test_validate_flag_rejects_double_write():
     # a gather may read one page twice
     _compare(K.KV_GATHER, pool, spans, chunks, regions, staging, "validate-gather",
              flags=K.KV_FLAG_VALIDATE)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_per_tile_dma_baseline_matches_oracle(seed):
+    """The copy-engine comparison path (one hipMemcpyAsync per tile, host block tables)
+    gives the same bytes as the oracle, in HBM and, for odd seeds, in pinned host memory."""
+    pool, spans, chunks = cases.make_case(np.random.default_rng(70_000 + seed), tok_multiple=16,
+                                          medium=bool(seed % 3), max_bytes=24 << 20)
+    regions, staging = _random(pool, chunks, seed)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "dma-%d" % seed, dma=True, ring=bool(seed % 2))
+
+
+def test_per_tile_dma_rejects_bad_ids_before_copying():
+    pool = dict(num_layers=1, num_kv=1, num_heads=1, head_dim=64, elem_bytes=2, block_size=16,
+                num_blocks=8, block_stride=2048)
+    chunks = dict(layout=0, chunk_layers=1, chunk_tokens=16, layer_begin=0, layer_end=1,
+                  slot_bytes=2048, n_slots=4)
+    regions, staging = _random(pool, chunks, 5)
+    for tbl, code in ((np.array([1, 2, 9, 3], dtype=np.int32), K.KV_ERR_RANGE),
+                      (np.array([1, 2, 1, 3], dtype=np.int32), K.KV_ERR_DUP)):
+        with pytest.raises(K.KvError) as e:
+            G.run_transfer(K.KV_SCATTER, pool, [(tbl, 0, 64, 0)], chunks, regions, staging,
+                           label="dma-bad", dma=True)
+        assert e.value.code == code
