@@ -415,17 +415,117 @@ def host_leg(args, dev):
                     ms, n = run_pass(fn, 1, wg)
                     row[name] = round(payload_layer * win_layers / (ms * 1e-3) / 1e9, 2)
                 sweep[str(wg)] = row
+        interference = interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_layer) \
+            if args.interference else None
         return dict(workload="llama70b: 80 layers x K/V x 8 x 128 bf16, 16-token pages, one 131072-token "
                              "request, 2 MiB chunks (1 layer x 512 tokens) through a pinned host ring of "
                              "%d slots (%d layers per window); library default grid for host staging "
                              "(16 workgroups); sweep_gbs keys are max_workgroups" % (n_slots, win_layers),
                     payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep,
-                    per_tile_dma=dma, **out)
+                    per_tile_dma=dma, interference=interference, **out)
     finally:
         K.kv_ring_destroy(ring)
         P.close()
         del P
         torch.cuda.empty_cache()
+
+
+def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_layer):
+    """Slowdown of compute running beside a pinned-host reload (Strata guide,
+    "Non-Intrusive Resource Sizing"; the Tutti summary partitions SMs between
+    compute and I/O).  A bf16 GEMM and a bandwidth-bound elementwise kernel are
+    timed alone, then while scatter windows stream from the host ring on a second
+    stream: first with both streams on the whole chip at three transfer grid sizes,
+    then with CU-masked streams (the transfer on 8 CUs, compute on the other 248)."""
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    words = (n_cu + 31) // 32
+
+    def masked(cus):
+        m = (ctypes.c_uint32 * words)()
+        for c in cus:
+            m[c // 32] |= 1 << (c % 32)
+        h = ctypes.c_void_p()
+        rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), words, m)
+        if rc != 0:
+            raise RuntimeError("hipExtStreamCreateWithCUMask failed: %d" % rc)
+        return h.value, torch.cuda.ExternalStream(h.value)
+
+    # square 8192^3 GEMM; a prefill-chunk MLP GEMM (4096 tokens x 4096 -> 14336);
+    # a bandwidth-bound elementwise pass over 4 GiB standing in for decode
+    mats = {"gemm_8192": (8192, 8192, 8192), "gemm_prefill": (4096, 4096, 14336)}
+    ops = {}
+    for name, (mm, kk, nn) in mats.items():
+        ops[name] = (torch.randn(mm, kk, dtype=torch.bfloat16, device=dev),
+                     torch.randn(kk, nn, dtype=torch.bfloat16, device=dev),
+                     torch.empty(mm, nn, dtype=torch.bfloat16, device=dev))
+    x = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
+
+    def work(kind, n, stream):
+        with torch.cuda.stream(stream):
+            for _ in range(n):
+                if kind in ops:
+                    a_, b_, c_ = ops[kind]
+                    torch.mm(a_, b_, out=c_)
+                else:
+                    x.mul_(1.0001)
+
+    def timed(kind, n, stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        work(kind, n, stream)
+        e1.record(stream)
+        return e0, e1
+
+    def measure(kind, n, compute, transfer=None, wg=0):
+        if transfer is not None:
+            K.kv_pool_timing_start(P.h)
+            for i in range(4):
+                K.kv_scatter_chunks(P.h, spans_d, spec_for((i * win_layers) % L, wg), transfer)
+        e0, e1 = timed(kind, n, compute)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / n
+        if transfer is None:
+            return t, None
+        ms, _ = K.kv_pool_timing_read(P.h)
+        return t, 4 * win_layers * payload_layer / (ms * 1e-3) / 1e9
+
+    reps = {"gemm_8192": 100, "gemm_prefill": 150, "elementwise": 60}
+    whole_c, whole_t = torch.cuda.Stream(), torch.cuda.Stream()
+    io_cus = list(range(8))
+    h_io, io = masked(io_cus)
+    h_cmp, cmp = masked([i for i in range(n_cu) if i not in io_cus])
+    out = {"cus": n_cu, "io_cus": io_cus}
+    try:
+        for kind, n in reps.items():
+            work(kind, 3, whole_c)
+            work(kind, 3, cmp)
+            torch.cuda.synchronize()
+            alone, _ = measure(kind, n, whole_c)
+            row = {"alone_ms": round(alone, 4)}
+            for wg in (2, 0, 32768):
+                t, gbs = measure(kind, n, whole_c, whole_t, wg)
+                row["shared_grid_%s" % (wg if wg else "default16")] = {
+                    "ms": round(t, 4), "slowdown": round(t / alone - 1, 4), "transfer_gbs": round(gbs, 2)}
+            t_alone_masked, _ = measure(kind, n, cmp)
+            t, gbs = measure(kind, n, cmp, io, 0)
+            row["partitioned"] = {"compute_alone_ms": round(t_alone_masked, 4),
+                                  "ms": round(t, 4), "slowdown_vs_whole_chip": round(t / alone - 1, 4),
+                                  "transfer_gbs": round(gbs, 2)}
+            out[kind] = row
+        assert K.kv_pool_get_error(P.h, whole_t) == 0
+    finally:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(h_io)
+        hip.hipStreamDestroy(h_cmp)
+    log("interference: " + json.dumps(out))
+    del ops, x
+    return out
 
 
 def traffic_for(achieved_bytes_per_launch):
@@ -455,6 +555,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-other-workloads", dest="others", action="store_false")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
+    ap.add_argument("--no-interference", dest="interference", action="store_false",
+                    help="skip the compute-beside-transfer measurement")
     ap.add_argument("--no-dma-baseline", dest="dma_baseline", action="store_false",
                     help="skip the per-tile hipMemcpyAsync comparison")
     args = ap.parse_args()

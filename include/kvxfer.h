@@ -267,6 +267,19 @@ KV_API int kv_ring_slot(const kv_ring *ring, int64_t i, void **host_ptr, void **
  * that uses it.  NULL is accepted. */
 KV_API int kv_ring_destroy(kv_ring *ring);
 
+/* Slot fencing, for using the ring as a queue between the GPU and the host (slot
+ * reuse across calls is fenced by events, as the Tutti summary's GPU io_uring
+ * orders its I/O with events, Figure 5).  kv_ring_record marks slots
+ * [first, first+count) (taken mod n_slots) as used by the work enqueued so far on
+ * `stream` (one event per call).  kv_ring_wait blocks the host until the last work
+ * recorded on every slot of the range has finished -- e.g. before the host reads
+ * slots an offload wrote, or refills slots a reload read.  kv_ring_stream_wait
+ * makes `stream` wait for that work instead.  A slot never recorded is free.
+ * 1 <= count <= n_slots, 0 <= first < n_slots, else KV_ERR_ARG.  Not thread-safe. */
+KV_API int kv_ring_record(kv_ring *ring, int64_t first, int64_t count, hipStream_t stream);
+KV_API int kv_ring_wait(kv_ring *ring, int64_t first, int64_t count);
+KV_API int kv_ring_stream_wait(kv_ring *ring, int64_t first, int64_t count, hipStream_t stream);
+
 /* ---- misc ------------------------------------------------------------------------ */
 
 /* Static description of a KV_* return code. */

@@ -275,6 +275,14 @@ struct kv_ring {
     void *host = nullptr;
     void *dev = nullptr;
     int64_t slot_bytes = 0, n_slots = 0;
+    // slot fencing: a small pool of events reused round-robin; each slot remembers
+    // the event (and that event's generation) of the last work recorded on it.  An
+    // event is synchronized before reuse, so a slot whose generation is stale is free.
+    std::vector<hipEvent_t> ev;
+    std::vector<uint64_t> ev_gen;
+    std::vector<int32_t> slot_ev;
+    std::vector<uint64_t> slot_gen;
+    int next_ev = 0;
 };
 
 namespace {
@@ -455,6 +463,30 @@ int transfer_dma(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chu
 }
 
 }  // namespace
+
+static constexpr int kRingEvents = 64;
+
+static bool ring_range_ok(const kv_ring *r, int64_t first, int64_t count)
+{
+    return r && first >= 0 && first < r->n_slots && count >= 1 && count <= r->n_slots;
+}
+
+template <typename F>
+static int ring_for_events(kv_ring *r, int64_t first, int64_t count, F fn)
+{
+    if (!ring_range_ok(r, first, count)) return KV_ERR_ARG;
+    if (r->ev.empty()) return KV_OK;  // nothing recorded yet
+    int last = -1;
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t sl = (first + i) % r->n_slots;
+        const int e = r->slot_ev[sl];
+        if (e < 0 || e == last || r->slot_gen[sl] != r->ev_gen[e]) continue;
+        int rc = fn(r->ev[e]);
+        if (rc) return rc;
+        last = e;
+    }
+    return KV_OK;
+}
 
 extern "C" {
 
@@ -702,9 +734,53 @@ int kv_ring_slot(const kv_ring *r, int64_t i, void **host_ptr, void **dev_ptr)
 int kv_ring_destroy(kv_ring *r)
 {
     if (!r) return KV_OK;
+    for (hipEvent_t e : r->ev)
+        if (e) (void)hipEventDestroy(e);
     if (r->host) (void)hipHostFree(r->host);
     delete r;
     return KV_OK;
+}
+
+int kv_ring_record(kv_ring *r, int64_t first, int64_t count, hipStream_t stream)
+{
+    if (!ring_range_ok(r, first, count)) return KV_ERR_ARG;
+    if (r->ev.empty()) {
+        try {
+            r->ev.assign(kRingEvents, nullptr);
+            r->ev_gen.assign(kRingEvents, 0);
+            r->slot_ev.assign(r->n_slots, -1);
+            r->slot_gen.assign(r->n_slots, 0);
+        } catch (...) {
+            return KV_ERR_OOM;
+        }
+        for (hipEvent_t &e : r->ev)
+            if (!HIP_OK(hipEventCreateWithFlags(&e, hipEventDisableTiming))) return KV_ERR_HIP;
+    }
+    const int e = r->next_ev;
+    if (!HIP_OK(hipEventSynchronize(r->ev[e]))) return KV_ERR_HIP;  // its earlier work is done
+    if (!HIP_OK(hipEventRecord(r->ev[e], stream))) return KV_ERR_HIP;
+    r->next_ev = (e + 1) % kRingEvents;
+    const uint64_t g = ++r->ev_gen[e];
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t sl = (first + i) % r->n_slots;
+        r->slot_ev[sl] = e;
+        r->slot_gen[sl] = g;
+    }
+    return KV_OK;
+}
+
+int kv_ring_wait(kv_ring *r, int64_t first, int64_t count)
+{
+    return ring_for_events(r, first, count, [](hipEvent_t e) {
+        return HIP_OK(hipEventSynchronize(e)) ? KV_OK : KV_ERR_HIP;
+    });
+}
+
+int kv_ring_stream_wait(kv_ring *r, int64_t first, int64_t count, hipStream_t stream)
+{
+    return ring_for_events(r, first, count, [stream](hipEvent_t e) {
+        return HIP_OK(hipStreamWaitEvent(stream, e, 0)) ? KV_OK : KV_ERR_HIP;
+    });
 }
 
 const char *kv_strerror(int code)

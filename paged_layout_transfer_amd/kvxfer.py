@@ -113,6 +113,9 @@ _sig("kv_pool_timing_read", ctypes.c_int, _P, ctypes.POINTER(ctypes.c_double), c
 _sig("kv_ring_create", ctypes.c_int, _I64, _I64, _I32, ctypes.POINTER(_P))
 _sig("kv_ring_slot", ctypes.c_int, _P, _I64, ctypes.POINTER(_P), ctypes.POINTER(_P))
 _sig("kv_ring_destroy", ctypes.c_int, _P)
+_sig("kv_ring_record", ctypes.c_int, _P, _I64, _I64, _P)
+_sig("kv_ring_wait", ctypes.c_int, _P, _I64, _I64)
+_sig("kv_ring_stream_wait", ctypes.c_int, _P, _I64, _I64, _P)
 _sig("kv_strerror", ctypes.c_char_p, ctypes.c_int)
 _sig("kv_version", ctypes.c_int)
 _sig("kv_last_hip_error", ctypes.c_int, ctypes.POINTER(ctypes.c_char_p))
@@ -123,6 +126,7 @@ EXPORTED = ("kv_pool_create", "kv_pool_destroy", "kv_pool_alloc_blocks", "kv_poo
             "kv_gather_chunks", "kv_scatter_chunks", "kv_gather_chunks_dma", "kv_scatter_chunks_dma",
             "kv_pool_get_error", "kv_pool_timing_start",
             "kv_pool_timing_read", "kv_ring_create", "kv_ring_slot", "kv_ring_destroy",
+            "kv_ring_record", "kv_ring_wait", "kv_ring_stream_wait",
             "kv_strerror", "kv_version", "kv_last_hip_error")
 
 
@@ -299,6 +303,18 @@ def kv_ring_slot(ring: int, i: int) -> tuple[int, int]:
 
 def kv_ring_destroy(ring: int) -> None:
     _check(_lib.kv_ring_destroy(ring), "kv_ring_destroy")
+
+
+def kv_ring_record(ring: int, first: int, count: int, stream=None) -> None:
+    _check(_lib.kv_ring_record(ring, first, count, _stream(stream)), "kv_ring_record")
+
+
+def kv_ring_wait(ring: int, first: int, count: int) -> None:
+    _check(_lib.kv_ring_wait(ring, first, count), "kv_ring_wait")
+
+
+def kv_ring_stream_wait(ring: int, first: int, count: int, stream=None) -> None:
+    _check(_lib.kv_ring_stream_wait(ring, first, count, _stream(stream)), "kv_ring_stream_wait")
 
 
 def kv_strerror(code: int) -> str:

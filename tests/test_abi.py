@@ -284,3 +284,11 @@ def test_per_tile_dma_validates_host_tables_before_any_hip_call():
         assert e.value.code == K.KV_ERR_HIP
     finally:
         K.kv_pool_destroy(pool)
+
+
+def test_ring_functions_reject_null_handles():
+    for fn, args in ((K._lib.kv_ring_record, (None, 0, 1, None)), (K._lib.kv_ring_wait, (None, 0, 1)),
+                     (K._lib.kv_ring_stream_wait, (None, 0, 1, None)), (K._lib.kv_ring_slot, (None, 0, None, None))):
+        assert fn(*args) == K.KV_ERR_ARG
+    assert K._lib.kv_ring_destroy(None) == K.KV_OK
+    assert K._lib.kv_pool_destroy(None) == K.KV_OK
