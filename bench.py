@@ -430,6 +430,34 @@ def host_leg(args, dev):
         torch.cuda.empty_cache()
 
 
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    lib.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    lib.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def cu_masked_stream(dev, cus):
+    """A default-priority stream restricted to the given CUs (hipExtStreamCreateWithCUMask),
+    wrapped for torch; returns (handle, torch stream)."""
+    import torch
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    words = (n_cu + 31) // 32
+    m = (ctypes.c_uint32 * words)()
+    for c in cus:
+        m[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    rc = _hip().hipExtStreamCreateWithCUMask(ctypes.byref(h), words, m)
+    if rc != 0:
+        raise RuntimeError("hipExtStreamCreateWithCUMask failed: %d" % rc)
+    return h.value, torch.cuda.ExternalStream(h.value)
+
+
+def destroy_stream(handle):
+    _hip().hipStreamDestroy(handle)
+
+
 def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_layer):
     """Slowdown of compute running beside a pinned-host reload (Strata guide,
     "Non-Intrusive Resource Sizing"; the Tutti summary partitions SMs between
@@ -439,23 +467,8 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
     then with CU-masked streams (the transfer on 8 CUs, compute on the other 248)."""
     import torch
     from paged_layout_transfer_amd import kvxfer as K
-    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
-    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
-                                                 ctypes.POINTER(ctypes.c_uint32)]
-    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    words = (n_cu + 31) // 32
-
-    def masked(cus):
-        m = (ctypes.c_uint32 * words)()
-        for c in cus:
-            m[c // 32] |= 1 << (c % 32)
-        h = ctypes.c_void_p()
-        rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), words, m)
-        if rc != 0:
-            raise RuntimeError("hipExtStreamCreateWithCUMask failed: %d" % rc)
-        return h.value, torch.cuda.ExternalStream(h.value)
-
+    masked = cu_masked_stream
     # square 8192^3 GEMM; a prefill-chunk MLP GEMM (4096 tokens x 4096 -> 14336);
     # a bandwidth-bound elementwise pass over 4 GiB standing in for decode
     mats = {"gemm_8192": (8192, 8192, 8192), "gemm_prefill": (4096, 4096, 14336)}
@@ -498,8 +511,8 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
     reps = {"gemm_8192": 100, "gemm_prefill": 150, "elementwise": 60}
     whole_c, whole_t = torch.cuda.Stream(), torch.cuda.Stream()
     io_cus = list(range(8))
-    h_io, io = masked(io_cus)
-    h_cmp, cmp = masked([i for i in range(n_cu) if i not in io_cus])
+    h_io, io = masked(dev, io_cus)
+    h_cmp, cmp = masked(dev, [i for i in range(n_cu) if i not in io_cus])
     out = {"cus": n_cu, "io_cus": io_cus}
     try:
         for kind, n in reps.items():
@@ -521,11 +534,133 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
         assert K.kv_pool_get_error(P.h, whole_t) == 0
     finally:
         torch.cuda.synchronize()
-        hip.hipStreamDestroy(h_io)
-        hip.hipStreamDestroy(h_cmp)
+        destroy_stream(h_io)
+        destroy_stream(h_cmp)
     log("interference: " + json.dumps(out))
     del ops, x
     return out
+
+
+def pipeline_leg(args, dev):
+    """Layer-wise reload overlapped with per-layer compute (the Strata guide's
+    layer-overlapped prefill, "Implementation" lifecycle step 5; the Tutti summary's
+    layer-granular retrieve, section 7): a 70B-shaped context (80 layers x K/V x 8 x
+    128 bf16, 16-token pages) cached in pinned host memory is reloaded one layer per
+    call on a transfer stream; the compute stream waits for layer l's event and runs
+    that layer's prefill MLP GEMMs for a chunk of new tokens.  Compared with reload
+    then compute on one stream."""
+    import numpy as np
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    from paged_layout_transfer_amd import workloads as W
+    L, KV, H, D, E, bs = 80, 2, 8, 128, 2, 16
+    T, new_tok, hidden, ffn = args.pipeline_tokens, args.pipeline_new_tokens, 8192, 28672
+    tok = H * D * E
+    n_pages = T // bs
+    N = n_pages + 64
+    pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
+                num_blocks=N, block_stride=bs * tok)
+    P = DevicePool(pool, dev)
+    table = np.random.default_rng(1003).permutation(N)[:n_pages].astype(np.int32)
+    tab = torch.from_numpy(table).to(dev)
+    spans = K.make_spans([(tab, n_pages, 0, T, 0)])
+    slot = KV * T * tok                                      # one layer of the context per slot
+    ring = K.kv_ring_create(slot, L)
+    ring_dev = K.kv_ring_slot(ring, 0)[1]
+    x = torch.randn(new_tok, hidden, dtype=torch.bfloat16, device=dev)
+    w_up = torch.randn(hidden, 2 * ffn, dtype=torch.bfloat16, device=dev)
+    w_down = torch.randn(ffn, hidden, dtype=torch.bfloat16, device=dev)
+    h_up = torch.empty(new_tok, 2 * ffn, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(new_tok, hidden, dtype=torch.bfloat16, device=dev)
+    shared_streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    h_io, io = cu_masked_stream(dev, range(8))
+    h_cmp, cmp = cu_masked_stream(dev, range(8, n_cu))
+    compute, transfer = shared_streams
+
+    def spec_layer(l, whole=False):
+        lb, le = (0, L) if whole else (l, l + 1)
+        return K.make_chunk_spec(K.KV_LAYER_FIRST, 1, T, lb, le, ring_dev + (0 if whole else l * slot),
+                                 slot, L if whole else 1)
+
+    def layer_compute():
+        torch.mm(x, w_up, out=h_up)
+        torch.mm(h_up[:, :ffn], w_down, out=y)
+
+    try:
+        W.device_fill_(P.t.view(-1), "bf16_uniform", 3)
+        K.kv_gather_chunks(P.h, spans, spec_layer(0, whole=True), transfer)   # the host cache
+        torch.cuda.synchronize()
+        assert K.kv_pool_get_error(P.h, transfer) == 0
+
+        def reload_all(stream):
+            for l in range(L):
+                K.kv_scatter_chunks(P.h, spans, spec_layer(l), stream)
+
+        def run(mode):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if mode == "transfer":
+                e0.record(transfer)
+                reload_all(transfer)
+                e1.record(transfer)
+            elif mode == "compute":
+                e0.record(compute)
+                with torch.cuda.stream(compute):
+                    for _ in range(L):
+                        layer_compute()
+                e1.record(compute)
+            elif mode == "serial":
+                e0.record(compute)
+                reload_all(compute)
+                with torch.cuda.stream(compute):
+                    for _ in range(L):
+                        layer_compute()
+                e1.record(compute)
+            else:  # pipelined: layer l's compute waits for layer l's reload
+                e0.record(transfer)
+                compute.wait_event(e0)
+                for l in range(L):
+                    K.kv_scatter_chunks(P.h, spans, spec_layer(l), transfer)
+                    ev = torch.cuda.Event()
+                    ev.record(transfer)
+                    with torch.cuda.stream(compute):
+                        compute.wait_event(ev)
+                        layer_compute()
+                e1.record(compute)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        modes = ("transfer", "compute", "serial", "pipelined")
+        res = {}
+        for tag, (c_s, t_s) in (("shared", shared_streams), ("partitioned", (cmp, io))):
+            compute, transfer = c_s, t_s
+            for mode in modes:
+                run(mode)                               # warm-up
+            res[tag] = {m: round(min(run(m) for _ in range(3)), 3) for m in modes}
+            r = res[tag]
+            r["overlap_of_shorter"] = round((r["transfer"] + r["compute"] - r["pipelined"]) /
+                                            min(r["transfer"], r["compute"]), 3)
+        assert K.kv_pool_get_error(P.h, transfer) == 0
+        res["speedup_vs_serial_on_whole_chip"] = round(res["shared"]["serial"] / min(
+            res["shared"]["pipelined"], res["partitioned"]["pipelined"]), 3)
+        res.update(
+            workload="70B-shaped context of %d cached tokens (%.2f GB) reloaded layer by layer from pinned "
+                     "host memory; per layer, %d new tokens through a %dx%d up/gate and %dx%d down GEMM" % (
+                         T, L * slot / 1e9, new_tok, hidden, 2 * ffn, ffn, hidden),
+            reload_gbs=round(L * slot / (res["shared"]["transfer"] * 1e-3) / 1e9, 2),
+            partition="transfer stream on CUs 0-7, compute stream on the other %d" % (n_cu - 8))
+        log("layer pipeline: " + json.dumps(res))
+        return res
+    finally:
+        torch.cuda.synchronize()
+        destroy_stream(h_io)
+        destroy_stream(h_cmp)
+        K.kv_ring_destroy(ring)
+        P.close()
+        del P
+        torch.cuda.empty_cache()
 
 
 def traffic_for(achieved_bytes_per_launch):
@@ -555,6 +690,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-other-workloads", dest="others", action="store_false")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
+    ap.add_argument("--no-pipeline", dest="pipeline", action="store_false",
+                    help="skip the layer-pipelined reload measurement")
+    ap.add_argument("--pipeline-tokens", type=int, default=16384)
+    ap.add_argument("--pipeline-new-tokens", type=int, default=512)
     ap.add_argument("--no-interference", dest="interference", action="store_false",
                     help="skip the compute-beside-transfer measurement")
     ap.add_argument("--no-dma-baseline", dest="dma_baseline", action="store_false",
@@ -580,6 +719,7 @@ def main():
     res.pop("host_sample", None)
     host = host_leg(args, dev) if args.host_path else None
     others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv"], 5) if args.others else None
+    pipeline = pipeline_leg(args, dev) if args.pipeline else None
 
     w = res["w"]
     traffic = traffic_for(2 * res["payload"])
@@ -620,6 +760,7 @@ def main():
         "parity": res["parity"],
         "host_path": host,
         "other_workloads": others,
+        "layer_pipeline": pipeline,
     }
     print(json.dumps(out), flush=True)
 

@@ -22,7 +22,8 @@
 
 namespace {
 
-constexpr int kDescSlots = 4;           // descriptor upload buffers in flight per pool
+constexpr int64_t kArenaBytes = 4 << 20; // span records of the calls in flight, per pool
+constexpr int kInflight = 256;           // calls in flight per pool before the host waits
 constexpr int kMaxTimed = 4096;         // launches one timing window can record
 constexpr int64_t kMaxU31 = 0x7fffffffLL;
 
@@ -258,10 +259,17 @@ struct kv_pool {
     int device = -1;
     uint8_t **d_regions = nullptr;
     int32_t *d_err = nullptr;
-    kvx::SpanDev *d_desc = nullptr;   // kDescSlots x KV_MAX_SPANS records
-    kvx::SpanDev *h_desc = nullptr;   // pinned host mirror
-    hipEvent_t desc_ev[kDescSlots] = {};
-    int desc_next = 0;
+    // Span-record arena: each call takes the next free stretch of a circular buffer
+    // (pinned host mirror + device copy) and records an event after its kernel; a
+    // stretch is reused once that event has passed.  Allocation is sequential, so
+    // the oldest call in flight is always the next one in the way.
+    uint8_t *d_arena = nullptr;
+    uint8_t *h_arena = nullptr;
+    hipEvent_t fl_ev[kInflight] = {};
+    int64_t fl_off[kInflight] = {};
+    int64_t fl_bytes[kInflight] = {};
+    int fl_first = 0, fl_count = 0;
+    int64_t arena_head = 0;
     // staging-memory kind of the last staging base seen
     const void *last_base = nullptr;
     bool last_base_host = false;
@@ -289,13 +297,49 @@ namespace {
 
 void free_device_state(kv_pool *p)
 {
-    for (int i = 0; i < kDescSlots; ++i)
-        if (p->desc_ev[i]) (void)hipEventDestroy(p->desc_ev[i]), p->desc_ev[i] = nullptr;
-    if (p->h_desc) (void)hipHostFree(p->h_desc), p->h_desc = nullptr;
-    if (p->d_desc) (void)hipFree(p->d_desc), p->d_desc = nullptr;
+    for (int i = 0; i < kInflight; ++i)
+        if (p->fl_ev[i]) (void)hipEventDestroy(p->fl_ev[i]), p->fl_ev[i] = nullptr;
+    if (p->h_arena) (void)hipHostFree(p->h_arena), p->h_arena = nullptr;
+    if (p->d_arena) (void)hipFree(p->d_arena), p->d_arena = nullptr;
+    p->fl_first = p->fl_count = 0;
+    p->arena_head = 0;
     if (p->d_err) (void)hipFree(p->d_err), p->d_err = nullptr;
     if (p->d_regions) (void)hipFree(p->d_regions), p->d_regions = nullptr;
     p->device = -1;
+}
+
+// Reserve `bytes` of the span-record arena for one call.  The host waits only for
+// calls still using that stretch, or for the oldest call when kInflight are queued.
+int arena_take(kv_pool *p, int64_t bytes, int64_t *off)
+{
+    int64_t start = p->arena_head;
+    if (start + bytes > kArenaBytes) start = 0;
+    while (p->fl_count > 0) {
+        const int i = p->fl_first;
+        const bool overlap = p->fl_off[i] < start + bytes && start < p->fl_off[i] + p->fl_bytes[i];
+        if (!overlap && p->fl_count < kInflight) break;
+        if (!HIP_OK(hipEventSynchronize(p->fl_ev[i]))) return KV_ERR_HIP;
+        p->fl_first = (i + 1) % kInflight;
+        --p->fl_count;
+    }
+    *off = start;
+    return KV_OK;
+}
+
+// Mark the stretch as used by the work just queued on `stream`.
+int arena_commit(kv_pool *p, int64_t off, int64_t bytes, hipStream_t stream)
+{
+    const int i = (p->fl_first + p->fl_count) % kInflight;
+    if (!HIP_OK(hipEventRecord(p->fl_ev[i], stream))) {
+        // cannot fence the stretch: wait for the work instead so it is free again
+        (void)hipStreamSynchronize(stream);
+        return KV_ERR_HIP;
+    }
+    p->fl_off[i] = off;
+    p->fl_bytes[i] = bytes;
+    ++p->fl_count;
+    p->arena_head = off + bytes;
+    return KV_OK;
 }
 
 int device_setup(kv_pool *p)
@@ -304,16 +348,16 @@ int device_setup(kv_pool *p)
     if (!HIP_OK(hipGetDevice(&dev))) return KV_ERR_HIP;
     if (p->device >= 0) return dev == p->device ? KV_OK : KV_ERR_ARG;
     const int64_t n = (int64_t)p->desc.num_layers * p->desc.num_kv;
-    const size_t desc_bytes = sizeof(kvx::SpanDev) * KV_MAX_SPANS * kDescSlots;
+
     if (!HIP_OK(hipMalloc(&p->d_regions, n * sizeof(void *)))) goto fail;
     if (!HIP_OK(hipMemcpy(p->d_regions, p->bases.data(), n * sizeof(void *), hipMemcpyHostToDevice)))
         goto fail;
     if (!HIP_OK(hipMalloc(&p->d_err, sizeof(int32_t)))) goto fail;
     if (!HIP_OK(hipMemset(p->d_err, 0, sizeof(int32_t)))) goto fail;
-    if (!HIP_OK(hipMalloc(&p->d_desc, desc_bytes))) goto fail;
-    if (!HIP_OK(hipHostMalloc((void **)&p->h_desc, desc_bytes, hipHostMallocDefault))) goto fail;
-    for (int i = 0; i < kDescSlots; ++i)
-        if (!HIP_OK(hipEventCreateWithFlags(&p->desc_ev[i], hipEventDisableTiming))) goto fail;
+    if (!HIP_OK(hipMalloc(&p->d_arena, kArenaBytes))) goto fail;
+    if (!HIP_OK(hipHostMalloc((void **)&p->h_arena, kArenaBytes, hipHostMallocDefault))) goto fail;
+    for (int i = 0; i < kInflight; ++i)
+        if (!HIP_OK(hipEventCreateWithFlags(&p->fl_ev[i], hipEventDisableTiming))) goto fail;
     p->device = dev;
     return KV_OK;
 fail:
@@ -385,13 +429,14 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
         if (rc) return rc;
     }
 
-    // Span records go to a pinned host buffer whose previous upload has finished,
-    // then one stream-ordered copy to the matching device buffer.
-    const int slot = p->desc_next;
-    p->desc_next = (p->desc_next + 1) % kDescSlots;
-    if (!HIP_OK(hipEventSynchronize(p->desc_ev[slot]))) return KV_ERR_HIP;
-    kvx::SpanDev *h = p->h_desc + (size_t)slot * KV_MAX_SPANS;
-    kvx::SpanDev *dd = p->d_desc + (size_t)slot * KV_MAX_SPANS;
+    // Span records go to a free stretch of the pinned arena, then one stream-ordered
+    // copy to the same stretch of the device arena.
+    const int64_t rec_bytes = ((int64_t)std::max(1, (int)n_spans) * (int64_t)sizeof(kvx::SpanDev) + 255) & ~255LL;
+    int64_t off = 0;
+    rc = arena_take(p, rec_bytes, &off);
+    if (rc) return rc;
+    kvx::SpanDev *h = reinterpret_cast<kvx::SpanDev *>(p->h_arena + off);
+    kvx::SpanDev *dd = reinterpret_cast<kvx::SpanDev *>(p->d_arena + off);
     kvx::Launch a;
     uint32_t n_rec = 0;
     rc = prepare_with(&p->desc, spans, n_spans, spec, h, &n_rec, &a, &info, p->plans.data(),
@@ -399,6 +444,12 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     if (rc) return rc;
     if (!HIP_OK(hipMemcpyAsync(dd, h, n_rec * sizeof(kvx::SpanDev), hipMemcpyHostToDevice, stream)))
         return KV_ERR_HIP;
+    // From here the copy may be in flight: a failure waits for the stream before
+    // returning, so the uncommitted arena stretch is free again.
+    auto fail = [stream]() {
+        (void)hipStreamSynchronize(stream);
+        return KV_ERR_HIP;
+    };
     a.regions = p->d_regions;
     a.spans = dd;
     a.err = p->d_err;
@@ -409,15 +460,14 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     else if (staging_in_host_memory(p, spec->base)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
 
     const bool timed = p->timing && p->n_timed < kMaxTimed;
-    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
+    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return fail();
     if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))
-        return KV_ERR_HIP;
+        return fail();
     if (timed) {
-        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;
+        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return fail();
         ++p->n_timed;
     }
-    if (!HIP_OK(hipEventRecord(p->desc_ev[slot], stream))) return KV_ERR_HIP;
-    return KV_OK;
+    return arena_commit(p, off, rec_bytes, stream);
 }
 
 // One hipMemcpyAsync per tile, addresses from the same tile resolution the kernel
