@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
 class _Pool(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
-        "block_size", "num_blocks", "block_stride")]
+        "block_size", "num_blocks", "block_stride", "page_layout")]
 
 
 class _Span(ctypes.Structure):
@@ -83,7 +83,8 @@ def transfer(direction: int, pool: dict, regions, spans, chunks: dict, chunk_buf
     """Run the oracle in place.
 
     pool     : dict with num_layers, num_kv, num_heads, head_dim, elem_bytes,
-               block_size, num_blocks, block_stride
+               block_size, num_blocks, block_stride and optionally page_layout
+               (0 token-major pages, the default; 1 head-major)
     regions  : sequence of L*KV writable uint8 numpy arrays (one per (layer, kv),
                index l*KV+kv), each covering every block it addresses, or a
                2-D uint8 array whose rows are the regions; with only_layers, the
@@ -95,7 +96,7 @@ def transfer(direction: int, pool: dict, regions, spans, chunks: dict, chunk_buf
     Returns the number of bytes copied; raises ValueError on a broken precondition.
     """
     lib = lib or _load()
-    p = _Pool(**{k: int(pool[k]) for k, _ in _Pool._fields_})
+    p = _Pool(**{k: int(pool.get(k, 0)) for k, _ in _Pool._fields_})
     c = _Chunks(**{k: int(chunks[k]) for k, _ in _Chunks._fields_})
     nreg = p.num_layers * p.num_kv
     if len(regions) != nreg:

@@ -11,7 +11,9 @@
  *
  *   Pool. For every layer l and K/V index kv there is one pool region; block b
  *   of it starts at bases[l*KV + kv] + b*block_stride and holds the page's
- *   tokens token-major, each token as [H][D] elements of E bytes.  A block id
+ *   tokens token-major, each token as [H][D] elements of E bytes -- or, for a
+ *   head-major pool, the page as [H][bs][D] (chunks stay token-major, so such a
+ *   pool is transposed on the way in and out).  A block id
  *   names the same page in every (layer, K/V) region, as the page index array
  *   does for all layers in the transfer kernel of the Strata guide
  *   ("Step 1: High-Performance GPU-Assisted I/O CUDA Kernel"); the HBM side is
@@ -56,6 +58,7 @@
 typedef struct {
     int64_t num_layers, num_kv, num_heads, head_dim, elem_bytes;
     int64_t block_size, num_blocks, block_stride;
+    int64_t page_layout; /* 0 = token-major pages [bs][H][D], 1 = head-major [H][bs][D] */
 } orc_pool;
 
 typedef struct {
@@ -78,6 +81,8 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 /* Byte offset, inside its pool region, of element (block b, slot j, head h, dim d). */
 static int64_t pool_offset(const orc_pool *P, int64_t b, int64_t j, int64_t h, int64_t d)
 {
+    if (P->page_layout == 1)
+        return b * P->block_stride + ((h * P->block_size + j) * P->head_dim + d) * P->elem_bytes;
     return b * P->block_stride + ((j * P->num_heads + h) * P->head_dim + d) * P->elem_bytes;
 }
 
@@ -110,6 +115,7 @@ int64_t orc_transfer(int dir, const orc_pool *P, uint8_t *const *bases, const or
     int64_t copied = 0;
 
     if (dir != ORC_GATHER && dir != ORC_SCATTER) return -1;
+    if (P->page_layout != 0 && P->page_layout != 1) return -1;
     if (CL <= 0 || CT <= 0 || CT % bs != 0 || C->n_slots <= 0) return -1;
     if (C->layer_begin < 0 || C->layer_end > P->num_layers || C->layer_end <= C->layer_begin)
         return -1;

@@ -67,7 +67,10 @@ def slot_map(pool: dict, spans, chunks: dict):
                 p = np.where(ok, t // bs, 0)
                 blk = tbl[p]
                 jj = t % bs
-                off = blk * stride + ((jj * H + h) * D + d) * E + e
+                if pool.get("page_layout", 0) == 1:   # [H][bs][D] pages
+                    off = blk * stride + ((h * bs + jj) * D + d) * E + e
+                else:                                 # [bs][H][D] pages
+                    off = blk * stride + ((jj * H + h) * D + d) * E + e
                 base = s * SB
                 region[base:base + SB] = np.where(ok, l * KV + kv, -1)
                 offset[base:base + SB] = np.where(ok, off, 0)

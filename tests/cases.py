@@ -26,12 +26,14 @@ def slot_capacity(pool: dict, chunks: dict) -> int:
 
 
 def make_case(rng: np.random.Generator, *, tok_multiple: int = 1, max_bytes: int = 1 << 20,
-              layout: int | None = None, n_spans: int | None = None, medium: bool = False):
+              layout: int | None = None, n_spans: int | None = None, medium: bool = False,
+              head_major: bool | None = False):
     """A random case: (pool, spans, chunks) with tables as int32 arrays.
 
     Small cases use tiny heads (tokens of 8-144 bytes, pages of 2-16 tokens);
     medium cases use model-like heads (tokens of 64 B - 4 KiB, pages of 16-64
-    tokens) so a page spans several 1 KiB wave copies plus a ragged tail."""
+    tokens) so a page spans several 1 KiB wave copies plus a ragged tail.
+    head_major: False = token-major pages, True = head-major, None = either."""
     while True:
         L = int(rng.integers(1, 5 if medium else 4))
         KV = int(rng.integers(1, 3))
@@ -72,8 +74,11 @@ def make_case(rng: np.random.Generator, *, tok_multiple: int = 1, max_bytes: int
         CL = int(rng.choice(divs))
         CT = bs * int(rng.integers(1, 4))
         lay = int(rng.integers(0, 2)) if layout is None else layout
+        page_layout = int(rng.integers(0, 2)) if head_major is None else int(head_major)
+        if page_layout == 1 and (D * E) % tok_multiple:
+            page_layout = 0
         pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E,
-                    block_size=bs, num_blocks=N, block_stride=block_stride)
+                    block_size=bs, num_blocks=N, block_stride=block_stride, page_layout=page_layout)
         chunks = dict(layout=lay, chunk_layers=CL, chunk_tokens=CT, layer_begin=lb,
                       layer_end=le, slot_bytes=0, n_slots=0)
         n_chunks = [((le - lb) // CL) * cdiv(t1 - t0, CT) for t0, t1 in spans_tok]

@@ -56,7 +56,7 @@ def _run_pair(direction, pool, spans, chunks, seed, lib=None):
 @pytest.mark.parametrize("seed", range(120))
 def test_oracle_matches_brute_force(seed):
     rng = np.random.default_rng(seed)
-    pool, spans, chunks = cases.make_case(rng)
+    pool, spans, chunks = cases.make_case(rng, head_major=None)
     for direction in (oracle.GATHER, oracle.SCATTER):
         got, exp = _run_pair(direction, pool, spans, chunks, seed * 7 + direction)
         assert np.array_equal(got, exp), (direction, pool, chunks)
@@ -94,22 +94,26 @@ def _referenced_mask(pool, spans, chunks):
     """Pool bytes the call touches, written from the page-table definition alone."""
     n = pool["num_layers"] * pool["num_kv"]
     mask = np.zeros((n, pool["num_blocks"] * pool["block_stride"]), dtype=bool)
-    tok = pool["num_heads"] * pool["head_dim"] * pool["elem_bytes"]
+    H, R = pool["num_heads"], pool["head_dim"] * pool["elem_bytes"]
     bs = pool["block_size"]
     for tbl, t0, t1, _ in spans:
         for t in range(t0, t1):
-            b = int(tbl[t // bs])
-            o = b * pool["block_stride"] + (t % bs) * tok
-            for l in range(chunks["layer_begin"], chunks["layer_end"]):
-                for kv in range(pool["num_kv"]):
-                    mask[l * pool["num_kv"] + kv, o:o + tok] = True
+            b, j = int(tbl[t // bs]), t % bs
+            for h in range(H):
+                if pool.get("page_layout", 0) == 1:      # [H][bs][D]
+                    o = b * pool["block_stride"] + (h * bs + j) * R
+                else:                                    # [bs][H][D]
+                    o = b * pool["block_stride"] + (j * H + h) * R
+                for l in range(chunks["layer_begin"], chunks["layer_end"]):
+                    for kv in range(pool["num_kv"]):
+                        mask[l * pool["num_kv"] + kv, o:o + R] = True
     return mask
 
 
 @pytest.mark.parametrize("seed", range(40))
 def test_roundtrip_identity_and_sentinel(seed):
     rng = np.random.default_rng(1000 + seed)
-    pool, spans, chunks = cases.make_case(rng)
+    pool, spans, chunks = cases.make_case(rng, head_major=None)
     regions = cases.regions_for(pool, rng)
     buf = cases.staging_for(chunks)
     oracle.gather(pool, regions, spans, chunks, buf)
@@ -123,8 +127,10 @@ def test_roundtrip_identity_and_sentinel(seed):
 @pytest.mark.parametrize("seed", range(12))
 def test_layer_first_equals_torch_indexing(seed):
     """One span of whole pages, layer-first, page-sized pool strides: each chunk is
-    pool[l, kv][table[pages]] flattened to tokens, stacked over (layer, kv)."""
+    pool[l, kv][table[pages]] flattened to tokens, stacked over (layer, kv); for a
+    head-major pool, with each page's [H][bs] axes permuted to [bs][H] first."""
     rng = np.random.default_rng(2000 + seed)
+    head_major = seed % 2 == 1
     L, KV, H, D, E, bs = 3, 2, int(rng.integers(1, 4)), 16, 2, int(rng.choice([4, 16]))
     N, n_pages = 40, int(rng.integers(2, 9))
     CT = bs * int(rng.integers(1, 4))
@@ -132,7 +138,7 @@ def test_layer_first_equals_torch_indexing(seed):
     pad = int(rng.choice([0, 32]))
     tok = H * D * E
     pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
-                num_blocks=N, block_stride=bs * tok + pad)
+                num_blocks=N, block_stride=bs * tok + pad, page_layout=int(head_major))
     tbl = rng.permutation(N)[:n_pages].astype(np.int32)
     T = n_pages * bs
     n_tc = cases.cdiv(T, CT)
@@ -143,6 +149,8 @@ def test_layer_first_equals_torch_indexing(seed):
     oracle.gather(pool, regions, [(tbl, 0, T, 0)], chunks, buf)
 
     t_regions = torch.from_numpy(regions).view(L, KV, N, -1)[:, :, :, :bs * tok]
+    if head_major:
+        t_regions = t_regions.reshape(L, KV, N, H, bs, D * E).permute(0, 1, 2, 4, 3, 5)
     t_regions = t_regions.reshape(L, KV, N, bs, tok)
     idx = torch.from_numpy(tbl.astype(np.int64))
     per_lkv = t_regions[:, :, idx].reshape(L, KV, T, tok)       # [L][KV][T][tok]
@@ -223,7 +231,7 @@ def test_page_first_is_transpose_of_layer_first(seed):
 @pytest.mark.parametrize("seed", range(10))
 def test_byte_histogram_is_conserved(seed):
     rng = np.random.default_rng(5000 + seed)
-    pool, spans, chunks = cases.make_case(rng)
+    pool, spans, chunks = cases.make_case(rng, head_major=None)
     regions = cases.regions_for(pool, rng)
     buf = cases.staging_for(chunks)
     written = oracle.gather(pool, regions, spans, chunks, buf)
@@ -295,8 +303,13 @@ MUTANTS = [
     ("ring modulo dropped", "(c % C->n_slots) * C->slot_bytes", "c * C->slot_bytes"),
     ("layer range offset dropped (li)", "li = (l - C->layer_begin) % CL", "li = l % CL"),
     ("layer range offset dropped (lc)", "lc = (l - C->layer_begin) / CL", "lc = l / CL"),
-    ("block stride taken as the page size", "b * P->block_stride",
-     "b * P->block_size * P->num_heads * P->head_dim * P->elem_bytes"),
+    ("block stride taken as the page size",
+     "return b * P->block_stride + ((j * P->num_heads",
+     "return b * P->block_size * P->num_heads * P->head_dim * P->elem_bytes + ((j * P->num_heads"),
+    ("head-major page read token-major", "((h * P->block_size + j) * P->head_dim",
+     "((j * P->num_heads + h) * P->head_dim"),
+    ("head-major head stride wrong", "((h * P->block_size + j) * P->head_dim",
+     "((h * P->block_size + j) * P->num_heads"),
     ("region index transposed", "bases[l * KV + kv]", "bases[kv * P->num_layers + l]"),
     ("head stride wrong", "* P->head_dim + d) * P->elem_bytes;\n}", "* P->head_dim + d);\n}"),
 ]
@@ -306,7 +319,7 @@ def _pins_pass(lib) -> bool:
     """Run a compact battery of the pins above against an oracle build."""
     for seed in range(60):
         rng = np.random.default_rng(seed)
-        pool, spans, chunks = cases.make_case(rng)
+        pool, spans, chunks = cases.make_case(rng, head_major=None)
         for direction in (oracle.GATHER, oracle.SCATTER):
             try:
                 got, exp = _run_pair(direction, pool, spans, chunks, seed * 7 + direction, lib=lib)
