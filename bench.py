@@ -52,6 +52,7 @@ def resolve(name):
     pool = {k: w[k] for k in ("num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
                               "block_size", "num_blocks")}
     pool["block_stride"] = w["block_size"] * tok
+    pool["page_layout"] = w.get("page_layout", 0)
     return w, pool
 
 
@@ -67,7 +68,8 @@ class DevicePool:
         bases = [self.t.data_ptr() + i * self.t.stride(0) for i in range(n)]
         self.desc = K.make_pool_desc(pool["num_layers"], pool["num_kv"], pool["num_heads"],
                                      pool["head_dim"], pool["elem_bytes"], pool["block_size"],
-                                     pool["num_blocks"], pool["block_stride"], bases)
+                                     pool["num_blocks"], pool["block_stride"], bases,
+                                     pool.get("page_layout", 0))
         self.h = K.kv_pool_create(self.desc)
 
     def close(self):
@@ -718,7 +720,8 @@ def main():
     cpu = cpu_baseline(res, args.cpu_budget) if args.cpu_baseline else None
     res.pop("host_sample", None)
     host = host_leg(args, dev) if args.host_path else None
-    others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv"], 5) if args.others else None
+    others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64"], 5) \
+        if args.others else None
     pipeline = pipeline_leg(args, dev) if args.pipeline else None
 
     w = res["w"]

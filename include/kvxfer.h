@@ -26,8 +26,9 @@
  * Pool.  For layer l < num_layers and kv < num_kv (2 = K and V, 1 = a single
  * latent) the caller provides one device region, bases[l*num_kv + kv].  Block
  * b of that region starts at bases[l*num_kv+kv] + b*block_stride and holds
- * block_size tokens, token-major, each token num_heads x head_dim elements of
- * elem_bytes bytes: tok = num_heads*head_dim*elem_bytes bytes per token.  One
+ * block_size tokens, token-major ([block_size][H][D]) or, with page_layout
+ * KV_PAGE_HEAD_MAJOR, head-major ([H][block_size][D]); a token is num_heads x
+ * head_dim elements of elem_bytes bytes: tok = num_heads*head_dim*elem_bytes.  One
  * block id names the same page in every (layer, kv) region.  K and V are
  * separate objects per layer, as in the Tutti summary's Figure 4 (2L objects
  * per block).  block_stride >= block_size*tok; block_stride == block_size*tok
@@ -55,7 +56,8 @@
  *                     are neither written (gather) nor read (scatter).
  * The page-first order is the Strata guide's host-side [P, L, H, D] tensor
  * ("Two-Dimensional Memory Layout Decoupling", item 2); layer-first matches its
- * HBM-side [L, P, H, D] tensor (item 1).
+ * HBM-side [L, P, H, D] tensor (item 1).  Chunks are token-major in both; a
+ * head-major pool is transposed to token-major on the way out and back on the way in.
  *
  * Nothing outside the referenced pool tokens and the chunk bytes is written.
  *
@@ -96,9 +98,13 @@ extern "C" {
 #define KV_ERR_DEVICE (-7) /* kv_pool_get_error: the device reported a bad block id */
 #define KV_ERR_DUP (-8)    /* KV_FLAG_VALIDATE: a scatter writes one pool page twice */
 
-/* ---- chunk layouts, directions, flags ---------------------------------- */
+/* ---- chunk layouts, in-page layouts, directions, flags ----------------- */
 #define KV_LAYER_FIRST 0
 #define KV_PAGE_FIRST 1
+
+/* kv_pool_desc.page_layout: how a pool block orders its tokens and heads */
+#define KV_PAGE_TOKEN_MAJOR 0 /* [block_size][H][D] (vLLM-style NHD) */
+#define KV_PAGE_HEAD_MAJOR 1  /* [H][block_size][D] (HND); chunks stay token-major */
 
 #define KV_GATHER 0  /* pool -> chunks (offload) */
 #define KV_SCATTER 1 /* chunks -> pool (reload)  */
@@ -128,6 +134,8 @@ typedef struct {
     int32_t head_dim;     /* D >= 1 */
     int32_t elem_bytes;   /* 1, 2, 4 or 8 (the payload is moved as opaque bytes) */
     int32_t block_size;   /* tokens per page, >= 1 */
+    int32_t page_layout;  /* KV_PAGE_TOKEN_MAJOR or KV_PAGE_HEAD_MAJOR; head-major needs
+                             head_dim*elem_bytes to be a multiple of 16 */
     int64_t num_blocks;   /* blocks per (layer, kv) region, 1 .. 2^31-1 */
     int64_t block_stride; /* bytes between consecutive blocks of one region */
     void *const *bases;   /* host array of num_layers*num_kv device pointers; the
@@ -232,7 +240,8 @@ KV_API int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_span
  * that each spans[i].block_table is a HOST array (the host issues the copies), and
  * every block id of the call is checked on the host before any copy is issued
  * (KV_ERR_RANGE; for scatter also KV_ERR_DUP).  Host work is O(tiles).  The tables
- * are read during the call only. */
+ * are read during the call only.  A head-major pool takes one hipMemcpy2DAsync per
+ * (tile, head) instead. */
 KV_API int kv_gather_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                                 const kv_chunk_spec *spec, hipStream_t stream);
 KV_API int kv_scatter_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,

@@ -65,6 +65,10 @@ int check_desc(const kv_pool_desc *d)
     if (d->elem_bytes != 1 && d->elem_bytes != 2 && d->elem_bytes != 4 && d->elem_bytes != 8)
         return KV_ERR_ARG;
     if (d->num_blocks < 1 || d->num_blocks > kMaxU31) return KV_ERR_ARG;
+    if (d->page_layout != KV_PAGE_TOKEN_MAJOR && d->page_layout != KV_PAGE_HEAD_MAJOR)
+        return KV_ERR_ARG;
+    if (d->page_layout == KV_PAGE_HEAD_MAJOR && ((int64_t)d->head_dim * d->elem_bytes) % 16 != 0)
+        return KV_ERR_ALIGN;
     const int64_t tok = (int64_t)d->num_heads * d->head_dim * d->elem_bytes;
     if (tok > kMaxU31 || tok * d->block_size > kMaxU31) return KV_ERR_ARG;
     if (tok % 16 != 0) return KV_ERR_ALIGN;
@@ -220,6 +224,17 @@ int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
     a->tok = (uint32_t)tok_bytes(d);
     a->block_size = (uint32_t)d->block_size;
     a->layout = (uint32_t)spec->layout;
+    a->page_layout = (uint32_t)d->page_layout;
+    if (d->page_layout == KV_PAGE_HEAD_MAJOR) {
+        const uint32_t r16 = (uint32_t)((int64_t)d->head_dim * d->elem_bytes / 16);
+        const uint32_t H = (uint32_t)d->num_heads;
+        a->hm_heads = H;
+        a->hm_r16 = r16;
+        a->hm_bs_r16 = (uint32_t)d->block_size * r16;
+        a->hm_dq = 64u % r16;
+        a->hm_dh = (64u / r16) % H;
+        a->hm_dj = (64u / r16) / H;
+    }
     if (info) *info = inf;
     return KV_OK;
 }
@@ -501,9 +516,23 @@ int transfer_dma(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chu
                                    : kvx::resolve_tile<KV_PAGE_FIRST>(a, sp, tile);
         uint8_t *pool = static_cast<uint8_t *>(p->bases[t.region]) + (int64_t)sp.table[t.page] * a.block_stride;
         uint8_t *chunk = a.chunk_base + t.chunk_off;
-        void *dst = direction == KV_GATHER ? (void *)chunk : (void *)pool;
-        const void *src = direction == KV_GATHER ? (const void *)pool : (const void *)chunk;
-        if (!HIP_OK(hipMemcpyAsync(dst, src, t.nbytes, hipMemcpyDefault, stream))) return KV_ERR_HIP;
+        if (a.page_layout == KV_PAGE_TOKEN_MAJOR) {
+            void *dst = direction == KV_GATHER ? (void *)chunk : (void *)pool;
+            const void *src = direction == KV_GATHER ? (const void *)pool : (const void *)chunk;
+            if (!HIP_OK(hipMemcpyAsync(dst, src, t.nbytes, hipMemcpyDefault, stream))) return KV_ERR_HIP;
+            continue;
+        }
+        // head-major: one strided copy per head, n_tok rows of D*E bytes
+        const size_t row = (size_t)a.hm_r16 * 16, n_tok = t.nbytes / a.tok;
+        for (uint32_t h = 0; h < a.hm_heads; ++h) {
+            uint8_t *ph = pool + (size_t)h * a.hm_bs_r16 * 16;
+            uint8_t *ch = chunk + (size_t)h * row;
+            const size_t cp = (size_t)a.hm_heads * row;
+            hipError_t e = direction == KV_GATHER
+                               ? hipMemcpy2DAsync(ch, cp, ph, row, row, n_tok, hipMemcpyDefault, stream)
+                               : hipMemcpy2DAsync(ph, row, ch, cp, row, n_tok, hipMemcpyDefault, stream);
+            if (!hip_ok(e, "hipMemcpy2DAsync")) return KV_ERR_HIP;
+        }
     }
     if (timed) {
         if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;

@@ -66,6 +66,12 @@ namespace kvx {
 #ifndef KVX_SCATTER_PIPELINE
 #define KVX_SCATTER_PIPELINE 0
 #endif
+#ifndef KVX_HM_UNROLL
+#define KVX_HM_UNROLL 8        // vectors per lane per group, head-major pools
+#endif
+#ifndef KVX_HM_POOL_NT
+#define KVX_HM_POOL_NT 1       // nontemporal accesses on the pool side of head-major tiles
+#endif
 #ifndef KVX_TAIL_GROUP
 #define KVX_TAIL_GROUP 4       // vectors per lane per group after the full groups
 #endif
@@ -113,7 +119,49 @@ struct Launch {
     uint32_t block_size;
     uint32_t layout;          // KV_LAYER_FIRST or KV_PAGE_FIRST
     uint32_t split_shift;     // each tile is copied as 2^split_shift parts by as many waves
-    uint32_t pad_[3];
+    // head-major pools ([H][block_size][D] pages): 16-byte vectors per head row
+    // (r16 = D*E/16), per block head (bs_r16 = block_size*r16), and the cursor step
+    // for 64 vectors of token-major order (see HmCursor)
+    uint32_t page_layout;
+    uint32_t hm_heads;
+    uint32_t hm_r16;
+    uint32_t hm_bs_r16;
+    uint32_t hm_dq, hm_dh, hm_dj;
+    uint32_t pad_;
+};
+
+// Position of a 16-byte vector of a tile in token-major order -- token j, head h,
+// vector q of that head's row -- and its offset (in vectors) inside a head-major
+// pool block, [H][block_size][r16].  advance() moves 64 vectors on (one wave
+// instruction's worth); each of q and h carries at most once.
+struct HmCursor {
+    uint32_t j, h, q;
+    __host__ __device__ void init(uint32_t v, const Launch &a)
+    {
+        const uint32_t per_tok = a.hm_heads * a.hm_r16;
+        j = v / per_tok;
+        const uint32_t rem = v - j * per_tok;
+        h = rem / a.hm_r16;
+        q = rem - h * a.hm_r16;
+    }
+    __host__ __device__ uint32_t pool_vec(const Launch &a) const
+    {
+        return h * a.hm_bs_r16 + j * a.hm_r16 + q;
+    }
+    __host__ __device__ void advance(const Launch &a)
+    {
+        q += a.hm_dq;
+        if (q >= a.hm_r16) {
+            q -= a.hm_r16;
+            ++h;
+        }
+        h += a.hm_dh;
+        if (h >= a.hm_heads) {
+            h -= a.hm_heads;
+            ++j;
+        }
+        j += a.hm_dj;
+    }
 };
 
 // Where one tile's bytes live, before the block-table lookup.

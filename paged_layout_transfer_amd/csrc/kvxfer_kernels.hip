@@ -170,7 +170,60 @@ __device__ __forceinline__ void copy_tile(const gvec *__restrict__ src, gvec *__
     }
 }
 
-template <int DIR, int LAYOUT>
+// The permuted (pool) side of a head-major tile touches each cache line of the block
+// from several wave instructions (one per token whose head row shares the line), so
+// whether those accesses bypass the caches is a separate choice.
+__device__ __forceinline__ u32x4 ld_hm_pool(const gvec *p)
+{
+#if KVX_HM_POOL_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st_hm_pool(gvec *p, u32x4 v)
+{
+#if KVX_HM_POOL_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// Head-major pool block against a token-major chunk tile: vectors [first, end) of
+// the tile in token-major order.  The chunk side is contiguous; on the pool side each
+// lane follows a cursor to its vector's place in the block's [H][bs][r16] order, so a
+// wave's 1 KiB touches whole D*E-byte head rows.
+template <int DIR, int U>
+__device__ __forceinline__ void copy_head_major(gvec *__restrict__ block, gvec *__restrict__ tile,
+                                                uint32_t first, uint32_t end, uint32_t lane,
+                                                const Launch &a)
+{
+    HmCursor c;
+    c.init(first + lane, a);
+    for (uint32_t v = first + lane; v < end; v += 64u * U) {
+        uint32_t pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            pv[u] = c.pool_vec(a);
+            c.advance(a);
+        }
+        u32x4 r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (v + 64u * u < end)
+                r[u] = DIR == KV_GATHER ? ld_hm_pool(block + pv[u]) : ld(tile + v + 64u * u);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (v + 64u * u < end) {
+                if (DIR == KV_GATHER) st(tile + v + 64u * u, r[u]);
+                else st_hm_pool(block + pv[u], r[u]);
+            }
+    }
+}
+
+template <int DIR, int LAYOUT, int PAGE>
 __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -197,22 +250,37 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         }
         uint32_t first, count;
         part_range(t.nbytes >> 4, (uint32_t)(item & ((1 << shift) - 1)), 1u << shift, &first, &count);
-        uint8_t *pool = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride + first * 16ll;
-        uint8_t *chunk = a.chunk_base + t.chunk_off + first * 16ll;
-        if (DIR == KV_GATHER) copy_tile<DIR>(as_global(pool), as_global(chunk), count, lane);
-        else copy_tile<DIR>(as_global(chunk), as_global(pool), count, lane);
+        uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
+        uint8_t *chunk_tile = a.chunk_base + t.chunk_off;
+        if (PAGE == KV_PAGE_HEAD_MAJOR) {
+            copy_head_major<DIR, KVX_HM_UNROLL>(as_global(block), as_global(chunk_tile), first,
+                                                first + count, lane, a);
+        } else {
+            uint8_t *pool = block + first * 16ll;
+            uint8_t *chunk = chunk_tile + first * 16ll;
+            if (DIR == KV_GATHER) copy_tile<DIR>(as_global(pool), as_global(chunk), count, lane);
+            else copy_tile<DIR>(as_global(chunk), as_global(pool), count, lane);
+        }
     }
+}
+
+template <int DIR, int LAYOUT>
+static const void *pick_page(const Launch &a)
+{
+    return a.page_layout == KV_PAGE_HEAD_MAJOR
+               ? (const void *)&tile_copy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>
+               : (const void *)&tile_copy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>;
 }
 
 int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t stream)
 {
     const void *fn;
     if (direction == KV_GATHER)
-        fn = a.layout == KV_LAYER_FIRST ? (const void *)&tile_copy<KV_GATHER, KV_LAYER_FIRST>
-                                        : (const void *)&tile_copy<KV_GATHER, KV_PAGE_FIRST>;
+        fn = a.layout == KV_LAYER_FIRST ? pick_page<KV_GATHER, KV_LAYER_FIRST>(a)
+                                        : pick_page<KV_GATHER, KV_PAGE_FIRST>(a);
     else
-        fn = a.layout == KV_LAYER_FIRST ? (const void *)&tile_copy<KV_SCATTER, KV_LAYER_FIRST>
-                                        : (const void *)&tile_copy<KV_SCATTER, KV_PAGE_FIRST>;
+        fn = a.layout == KV_LAYER_FIRST ? pick_page<KV_SCATTER, KV_LAYER_FIRST>(a)
+                                        : pick_page<KV_SCATTER, KV_PAGE_FIRST>(a);
     Launch arg = a;
     void *args[] = {&arg};
     // hipLaunchKernel reports this launch's own status (not a stale runtime error).

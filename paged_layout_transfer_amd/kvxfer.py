@@ -44,6 +44,8 @@ KV_ERR_DEVICE = -7
 KV_ERR_DUP = -8
 KV_LAYER_FIRST = 0
 KV_PAGE_FIRST = 1
+KV_PAGE_TOKEN_MAJOR = 0
+KV_PAGE_HEAD_MAJOR = 1
 KV_GATHER = 0
 KV_SCATTER = 1
 KV_FLAG_VALIDATE = 0x1
@@ -57,6 +59,7 @@ class kv_pool_desc(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("num_kv", ctypes.c_int32),
                 ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("elem_bytes", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("page_layout", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64), ("block_stride", ctypes.c_int64),
                 ("bases", ctypes.POINTER(ctypes.c_void_p))]
 
@@ -165,10 +168,10 @@ def _stream(s) -> int:
 
 def make_pool_desc(num_layers: int, num_kv: int, num_heads: int, head_dim: int, elem_bytes: int,
                    block_size: int, num_blocks: int, block_stride: int,
-                   bases: Sequence) -> kv_pool_desc:
+                   bases: Sequence, page_layout: int = KV_PAGE_TOKEN_MAJOR) -> kv_pool_desc:
     """A kv_pool_desc; bases holds num_layers*num_kv device addresses (index l*num_kv+kv)."""
     arr = (ctypes.c_void_p * len(bases))(*[_addr(b) for b in bases])
-    d = kv_pool_desc(num_layers, num_kv, num_heads, head_dim, elem_bytes, block_size,
+    d = kv_pool_desc(num_layers, num_kv, num_heads, head_dim, elem_bytes, block_size, page_layout,
                      num_blocks, block_stride, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
     d._bases_keepalive = arr
     return d

@@ -12,7 +12,9 @@ contexts, 16-64-token pages) is taken.  A copy's result does not depend on the
 values, so random bytes of the stated element width are used.
 
 Seeds: table/length seed 1000 + k and data seed k for workload k
-(tiny 1, llama8b 2, llama70b 3, mixed 4, mla_fp8 5, int8_kv 6).
+(tiny 1, llama8b 2, llama70b 3, mixed 4, mla_fp8 5, int8_kv 6, llama8b_hnd 7,
+fp8_hnd_d64 8).  page_layout (default 0) is the pool's in-page order: 0 token-major
+[block_size][H][D], 1 head-major [H][block_size][D].
 """
 from __future__ import annotations
 
@@ -53,6 +55,16 @@ WORKLOADS: dict[str, dict] = {
     "int8_kv": dict(k=6, num_layers=61, num_kv=2, num_heads=8, head_dim=128, elem_bytes=1,
                     block_size=64, num_blocks=2048, tokens=65536, fill="bytes",
                     layout=PAGE_FIRST, chunk_layers=61, chunk_tokens=64, staging="hbm"),
+    # The llama8b shape with head-major pages ([H][16][128] bf16: 256-byte head rows).
+    "llama8b_hnd": dict(k=7, num_layers=32, num_kv=2, num_heads=8, head_dim=128, elem_bytes=2,
+                        block_size=16, num_blocks=16384, tokens=32768, fill="bf16_uniform",
+                        layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm",
+                        page_layout=1),
+    # Head-major fp8 pages with short rows: 8 heads x 64 dims x 1 byte = 64-byte head rows.
+    "fp8_hnd_d64": dict(k=8, num_layers=32, num_kv=2, num_heads=8, head_dim=64, elem_bytes=1,
+                        block_size=16, num_blocks=16384, tokens=32768, fill="bytes",
+                        layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm",
+                        page_layout=1),
 }
 
 

@@ -76,6 +76,8 @@ def make_case(rng: np.random.Generator, *, tok_multiple: int = 1, max_bytes: int
         lay = int(rng.integers(0, 2)) if layout is None else layout
         page_layout = int(rng.integers(0, 2)) if head_major is None else int(head_major)
         if page_layout == 1 and (D * E) % tok_multiple:
+            if head_major:
+                continue            # head rows must be whole 16-byte vectors: draw again
             page_layout = 0
         pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E,
                     block_size=bs, num_blocks=N, block_stride=block_stride, page_layout=page_layout)

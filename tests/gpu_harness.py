@@ -53,7 +53,8 @@ def run_transfer(direction: int, pool: dict, spans, chunks: dict, regions_np: np
         stg = torch.from_numpy(np.ascontiguousarray(staging_np)).to(dev)
         base = stg.data_ptr()
     desc = K.make_pool_desc(L, KV, pool["num_heads"], pool["head_dim"], pool["elem_bytes"],
-                            pool["block_size"], pool["num_blocks"], pool["block_stride"], bases)
+                            pool["block_size"], pool["num_blocks"], pool["block_stride"], bases,
+                            pool.get("page_layout", 0))
     host_tabs = [np.ascontiguousarray(t, dtype=np.int32) for t, _, _, _ in spans]
     if dma:
         sp = K.make_spans([(ht.ctypes.data, ht.size, t0, t1, fc)

@@ -72,7 +72,26 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
                 }
                 uint32_t first, count;
                 kvx::part_range(t.nbytes >> 4, (uint32_t)(item % split), split, &first, &count);
-                if (copy && count) {
+                if (a.page_layout == KV_PAGE_HEAD_MAJOR) {
+                    // each lane's cursor, as the kernel advances it, 64 vectors at a time
+                    uint8_t *block = static_cast<uint8_t *>(d->bases[t.region]) + poff;
+                    uint8_t *tile = a.chunk_base + t.chunk_off;
+                    for (uint32_t lane = 0; lane < 64; ++lane) {
+                        kvx::HmCursor c;
+                        c.init(first + lane, a);
+                        for (uint32_t v = first + lane; v < first + count; v += 64) {
+                            const uint32_t pv = c.pool_vec(a);
+                            c.advance(a);
+                            if ((int64_t)pv * 16 + 16 > (int64_t)a.hm_bs_r16 * a.hm_heads * 16) {
+                                ++*violations;  // outside the block's [H][bs][D] page
+                                continue;
+                            }
+                            if (!copy) continue;
+                            if (direction == KV_GATHER) std::memcpy(tile + v * 16ull, block + pv * 16ull, 16);
+                            else std::memcpy(block + pv * 16ull, tile + v * 16ull, 16);
+                        }
+                    }
+                } else if (copy && count) {
                     uint8_t *pool = static_cast<uint8_t *>(d->bases[t.region]) + poff + first * 16ll;
                     uint8_t *chunk = a.chunk_base + t.chunk_off + first * 16ll;
                     if (direction == KV_GATHER) std::memcpy(chunk, pool, count * 16ull);

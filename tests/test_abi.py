@@ -19,13 +19,13 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 FAKE = 0x7F0000000000  # 16-byte aligned stand-in device addresses, never dereferenced
 
 
-def _desc(L=2, KV=2, H=2, D=64, E=2, bs=16, N=64, stride=None, bases=None):
+def _desc(L=2, KV=2, H=2, D=64, E=2, bs=16, N=64, stride=None, bases=None, page_layout=0):
     tok = H * D * E
     if stride is None:
         stride = bs * tok
     if bases is None:
         bases = [FAKE + i * (1 << 30) for i in range(L * KV)]
-    return K.make_pool_desc(L, KV, H, D, E, bs, N, stride, bases)
+    return K.make_pool_desc(L, KV, H, D, E, bs, N, stride, bases, page_layout)
 
 
 def _spec(**kw):
@@ -114,6 +114,8 @@ POOL_CASES = [
     (dict(stride=4096 + 8), K.KV_ERR_ALIGN),
     (dict(bases=[FAKE, FAKE + 8, FAKE, FAKE]), K.KV_ERR_ALIGN),
     (dict(bases=[FAKE, 0, FAKE, FAKE]), K.KV_ERR_ARG),
+    (dict(page_layout=2), K.KV_ERR_ARG),
+    (dict(H=2, D=8, E=1, page_layout=1), K.KV_ERR_ALIGN),   # 8-byte head rows
 ]
 
 

@@ -31,6 +31,7 @@ def resolve(name):
     pool = {k: w[k] for k in ("num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
                               "block_size", "num_blocks")}
     pool["block_stride"] = w["block_size"] * tok
+    pool["page_layout"] = w.get("page_layout", 0)
     return w, pool
 
 
@@ -50,7 +51,8 @@ class Setup:
         self.P = torch.empty((L * KV, self.row), dtype=torch.uint8, device=self.dev)
         bases = [self.P.data_ptr() + i * self.row for i in range(L * KV)]
         self.desc = K.make_pool_desc(L, KV, pool["num_heads"], pool["head_dim"], pool["elem_bytes"],
-                                     pool["block_size"], pool["num_blocks"], pool["block_stride"], bases)
+                                     pool["block_size"], pool["num_blocks"], pool["block_stride"], bases,
+                                     pool["page_layout"])
         self.h = K.kv_pool_create(self.desc)
         self.tabs = [torch.from_numpy(t).to(self.dev) for t in w["block_tables"]]
         self.spans_h = [(t, t0, t1, fc) for t, (t0, t1), fc in
@@ -134,6 +136,8 @@ HBM_CASES = {
     "mixed": dict(layers=[0, 31], requests=[0, 21, 42, 63]),
     "mla_fp8": dict(layers=[0, 60], requests=[0]),
     "int8_kv": dict(layers=[0, 60], requests=[0]),
+    "llama8b_hnd": dict(layers=[0, 31], requests=[0]),
+    "fp8_hnd_d64": dict(layers=[0, 31], requests=[0]),
 }
 
 

@@ -253,3 +253,15 @@ def test_per_tile_dma_rejects_bad_ids_before_copying():
             G.run_transfer(K.KV_SCATTER, pool, [(tbl, 0, 64, 0)], chunks, regions, staging,
                            label="dma-bad", dma=True)
         assert e.value.code == code
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_head_major_pool_cases(seed):
+    """Head-major pages ([H][bs][D]) against token-major chunks; odd seeds stage in
+    pinned host memory, every fourth uses the per-tile copy-engine path."""
+    pool, spans, chunks = cases.make_case(np.random.default_rng(85_000 + seed), tok_multiple=16,
+                                          medium=bool(seed % 3), max_bytes=24 << 20, head_major=True)
+    regions, staging = _random(pool, chunks, seed)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "head-major-%d" % seed, ring=bool(seed % 2),
+                 dma=seed % 4 == 0)

@@ -56,7 +56,7 @@ def _emulate(lib, direction, pool, spans, chunks, bases, region_bytes, staging_p
              copy, max_workgroups=0):
     desc = K.make_pool_desc(pool["num_layers"], pool["num_kv"], pool["num_heads"], pool["head_dim"],
                             pool["elem_bytes"], pool["block_size"], pool["num_blocks"],
-                            pool["block_stride"], bases)
+                            pool["block_stride"], bases, pool.get("page_layout", 0))
     tabs = [np.ascontiguousarray(t, dtype=np.int32) for t, _, _, _ in spans]
     sp = K.make_spans([(t.ctypes.data, t.size, t0, t1, fc) for t, (_, t0, t1, fc) in zip(tabs, spans)])
     spec = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"],
@@ -100,14 +100,22 @@ def test_emulated_kernel_matches_oracle_medium(emu, seed):
     _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 4))
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_emulated_head_major_matches_oracle(emu, seed):
+    pool, spans, chunks = cases.make_case(np.random.default_rng(27_000 + seed), tok_multiple=16,
+                                          medium=bool(seed % 2), max_bytes=24 << 20, head_major=True)
+    assert pool["page_layout"] == 1
+    _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
+
+
 @pytest.mark.parametrize("seed", range(20))
 def test_emulated_split_tiles_match_oracle(emu_split, seed):
     pool, spans, chunks = cases.make_case(np.random.default_rng(25_000 + seed), tok_multiple=16,
-                                          medium=True, max_bytes=48 << 20)
+                                          medium=True, max_bytes=48 << 20, head_major=None)
     _copy_case(emu_split, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
 
 
-FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv"]
+FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -119,6 +127,7 @@ def test_workload_addresses_stay_in_bounds(emu, name):
     pool = {k: w[k] for k in ("num_layers", "num_kv", "num_heads", "head_dim", "elem_bytes",
                               "block_size", "num_blocks")}
     pool["block_stride"] = w["block_size"] * tok
+    pool["page_layout"] = w.get("page_layout", 0)
     plan = W.staging_plan(w)
     chunks = dict(layout=w["layout"], chunk_layers=w["chunk_layers"], chunk_tokens=w["chunk_tokens"],
                   layer_begin=0, layer_end=w["num_layers"], slot_bytes=plan["slot_bytes"],
@@ -127,8 +136,9 @@ def test_workload_addresses_stay_in_bounds(emu, name):
     n = pool["num_layers"] * pool["num_kv"]
     fake = 1 << 44
     bases = [fake + i * (1 << 38) for i in range(n)]
+    grids = (0,) if pool["page_layout"] else (0, 2)   # a head-major walk visits every vector
     for d in (K.KV_GATHER, K.KV_SCATTER):
-        for wg in (0, 2):
+        for wg in grids:
             viol, tiles, grid = _emulate(emu, d, pool, spans, chunks, bases,
                                          [pool["num_blocks"] * pool["block_stride"]] * n, 1 << 45,
                                          plan["slot_bytes"] * plan["n_chunks"], False, wg)
