@@ -265,3 +265,37 @@ def test_head_major_pool_cases(seed):
     for d in DIRS:
         _compare(d, pool, spans, chunks, regions, staging, "head-major-%d" % seed, ring=bool(seed % 2),
                  dma=seed % 4 == 0)
+
+
+EXTREMES = {
+    # 1-token pages of 16-byte tokens: every tile is one vector
+    "one_token_pages": dict(L=3, KV=2, H=1, D=16, E=1, bs=1, N=900, spans=[(0, 500), (0, 77)], CT=64, CL=3),
+    # 512-token pages of 2 KiB tokens: 1 MiB tiles, split between waves in both directions
+    "huge_pages": dict(L=2, KV=2, H=8, D=128, E=2, bs=512, N=8, spans=[(0, 1500), (512, 1100)], CT=1024, CL=1),
+    # a span that starts 300 pages into its table
+    "deep_start": dict(L=2, KV=1, H=2, D=64, E=2, bs=16, N=400, spans=[(300 * 16, 300 * 16 + 70)], CT=32, CL=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXTREMES))
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("page_layout", [0, 1])
+def test_extreme_shapes(name, layout, page_layout):
+    c = EXTREMES[name]
+    tok = c["H"] * c["D"] * c["E"]
+    pool = dict(num_layers=c["L"], num_kv=c["KV"], num_heads=c["H"], head_dim=c["D"], elem_bytes=c["E"],
+                block_size=c["bs"], num_blocks=c["N"], block_stride=c["bs"] * tok, page_layout=page_layout)
+    rng = np.random.default_rng(95_000 + 7 * layout + page_layout)
+    perm = rng.permutation(c["N"]).astype(np.int32)
+    spans, used, fc = [], 0, 0
+    for t0, t1 in c["spans"]:
+        n_pages = cases.cdiv(t1, c["bs"])
+        tbl = np.concatenate([np.full(t0 // c["bs"], -1, np.int32), perm[used:used + n_pages - t0 // c["bs"]]])
+        used += n_pages - t0 // c["bs"]
+        spans.append((tbl, t0, t1, fc))
+        fc += (c["L"] // c["CL"]) * cases.cdiv(t1 - t0, c["CT"])
+    chunks = dict(layout=layout, chunk_layers=c["CL"], chunk_tokens=c["CT"], layer_begin=0, layer_end=c["L"],
+                  slot_bytes=c["CL"] * c["KV"] * c["CT"] * tok, n_slots=fc)
+    regions, staging = _random(pool, chunks, 3)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "extreme-%s-%d-%d" % (name, layout, page_layout))

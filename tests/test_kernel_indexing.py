@@ -144,3 +144,33 @@ def test_workload_addresses_stay_in_bounds(emu, name):
                                          plan["slot_bytes"] * plan["n_chunks"], False, wg)
             assert viol == 0
             assert tiles == sum(n * -(-(t1 - t0) // w["block_size"]) for t0, t1 in w["requests"])
+
+
+def _extreme_case(name, layout, page_layout):
+    from test_gpu_parity import EXTREMES
+    c = EXTREMES[name]
+    tok = c["H"] * c["D"] * c["E"]
+    pool = dict(num_layers=c["L"], num_kv=c["KV"], num_heads=c["H"], head_dim=c["D"], elem_bytes=c["E"],
+                block_size=c["bs"], num_blocks=c["N"], block_stride=c["bs"] * tok, page_layout=page_layout)
+    rng = np.random.default_rng(95_000 + 7 * layout + page_layout)
+    perm = rng.permutation(c["N"]).astype(np.int32)
+    spans, used, fc = [], 0, 0
+    for t0, t1 in c["spans"]:
+        n_pages = cases.cdiv(t1, c["bs"])
+        tbl = np.concatenate([np.full(t0 // c["bs"], -1, np.int32), perm[used:used + n_pages - t0 // c["bs"]]])
+        used += n_pages - t0 // c["bs"]
+        spans.append((tbl, t0, t1, fc))
+        fc += (c["L"] // c["CL"]) * cases.cdiv(t1 - t0, c["CT"])
+    chunks = dict(layout=layout, chunk_layers=c["CL"], chunk_tokens=c["CT"], layer_begin=0, layer_end=c["L"],
+                  slot_bytes=c["CL"] * c["KV"] * c["CT"] * tok, n_slots=fc)
+    return pool, spans, chunks
+
+
+@pytest.mark.parametrize("name", ["one_token_pages", "huge_pages", "deep_start"])
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("page_layout", [0, 1])
+def test_emulated_extreme_shapes(emu, name, layout, page_layout):
+    """The GPU extreme-shape cases, walked on the CPU first (prefix table entries are -1
+    and must never be read)."""
+    pool, spans, chunks = _extreme_case(name, layout, page_layout)
+    _copy_case(emu, pool, spans, chunks, 3)
