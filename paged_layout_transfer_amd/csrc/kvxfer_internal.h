@@ -81,6 +81,19 @@ namespace kvx {
 #ifndef KVX_NT_STORE
 #define KVX_NT_STORE 1         // nontemporal stores
 #endif
+// Cache-policy bits of a gfx950 buffer load/store (the builtin's last argument).
+#define KVX_POL_SC0 1
+#define KVX_POL_NT 2
+#define KVX_POL_SC1 16
+#ifndef KVX_GATHER_POOL_POL
+#define KVX_GATHER_POOL_POL KVX_POL_NT                   // gather's loads of pool pages
+#endif
+#ifndef KVX_GATHER_CHUNK_POL
+#define KVX_GATHER_CHUNK_POL (KVX_POL_NT | KVX_POL_SC1)  // gather's stores into the chunk
+#endif
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle, no per-lane index
+// (the setting untyped dword accesses use on gfx9-family parts).
+#define KVX_BUF_WORD3 0x00020000
 constexpr int kWavesPerBlock = KVX_WAVES_PER_BLOCK;
 constexpr int kThreads = 64 * kWavesPerBlock;
 
