@@ -56,6 +56,24 @@ def resolve(name):
     return w, pool
 
 
+DTYPE_NAMES = {"bf16_uniform": "bf16", "u16_bits": "fp16 bit patterns", "bytes": "1-byte"}
+
+
+def describe(name, w):
+    """The workload as one line: shape, pool, requests, chunks."""
+    tile_kib = w["block_size"] * w["num_heads"] * w["head_dim"] * w["elem_bytes"] / 1024
+    lens = sorted(t1 - t0 for t0, t1 in w["requests"])
+    reqs = ("one %d-token request" % lens[0] if len(lens) == 1 else
+            "%d requests of %d-%d tokens" % (len(lens), lens[0], lens[-1]))
+    return ("%s: %d layers x %s x %d heads x %d dims %s, %d-token %s pages (%g KiB per layer-page), "
+            "%d-block pool, %s with a shuffled block table, %d-token %s chunks of %d layers in HBM; "
+            "step = gather + scatter" % (
+                name, w["num_layers"], "K/V" if w["num_kv"] == 2 else "1 latent", w["num_heads"],
+                w["head_dim"], DTYPE_NAMES.get(w["fill"], w["fill"]), w["block_size"],
+                "head-major" if w.get("page_layout", 0) else "token-major", tile_kib, w["num_blocks"], reqs,
+                w["chunk_tokens"], "layer-first" if w["layout"] == 0 else "page-first", w["chunk_layers"]))
+
+
 class DevicePool:
     """A pool of num_layers*num_kv regions in one device tensor, with its handle."""
 
@@ -184,18 +202,24 @@ def hbm_leg(args, dev):
         tabs_h = [np.ascontiguousarray(t, dtype=np.int32) for t in w["block_tables"]]
         spans_dma = K.make_spans([(t.ctypes.data, t.size, t0, t1, fc) for t, (t0, t1), fc in
                                   zip(tabs_h, w["requests"], plan["first_chunk"])])
-        for name, fn in (("gather", K.kv_gather_chunks_dma), ("scatter", K.kv_scatter_chunks_dma)):
-            torch.cuda.synchronize()
-            K.kv_pool_timing_start(P.h)
-            t0 = time.perf_counter()
-            fn(P.h, spans_dma, spec, stream)
-            submit = time.perf_counter() - t0
-            ms, n = K.kv_pool_timing_read(P.h)
-            dma[name] = dict(gbs=round(payload / (ms * 1e-3) / 1e9, 2), ms=round(ms, 2),
-                             copies=info.tiles, host_submit_ms=round(submit * 1e3, 2),
-                             hbm_frac=round(2 * payload / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
-        log("per-tile hipMemcpyAsync: gather %.1f GB/s, scatter %.1f GB/s" % (
-            dma["gather"]["gbs"], dma["scatter"]["gbs"]))
+        # per tile, then with one strided copy per (chunk, page) over its (layer, kv) tiles
+        group = w["chunk_layers"] * w["num_kv"]
+        for mode, flags, copies in (("per_tile", 0, info.tiles), ("strided", K.KV_FLAG_DMA_STRIDED, info.tiles // group)):
+            spec_dma = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"], 0, L,
+                                         S, plan["slot_bytes"], plan["n_chunks"], 0, flags)
+            out_dma = dma if mode == "per_tile" else dma.setdefault("strided", {})
+            for name, fn in (("gather", K.kv_gather_chunks_dma), ("scatter", K.kv_scatter_chunks_dma)):
+                torch.cuda.synchronize()
+                K.kv_pool_timing_start(P.h)
+                t0 = time.perf_counter()
+                fn(P.h, spans_dma, spec_dma, stream)
+                submit = time.perf_counter() - t0
+                ms, n = K.kv_pool_timing_read(P.h)
+                out_dma[name] = dict(gbs=round(payload / (ms * 1e-3) / 1e9, 2), ms=round(ms, 2),
+                                     copies=copies, host_submit_ms=round(submit * 1e3, 2),
+                                     hbm_frac=round(2 * payload / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+            log("%s hipMemcpy(2D)Async: gather %.1f GB/s, scatter %.1f GB/s" % (
+                mode, out_dma["gather"]["gbs"], out_dma["scatter"]["gbs"]))
 
     # device-to-device memcpy of the same payload, for context
     import torch as _t
@@ -325,9 +349,9 @@ def host_leg(args, dev):
     ring_host = K.ring_host_array(ring, slot * n_slots)
     stream = torch.cuda.current_stream()
 
-    def spec_for(l0, wg=0):
+    def spec_for(l0, wg=0, flags=0):
         return K.make_chunk_spec(K.KV_LAYER_FIRST, w["chunk_layers"], w["chunk_tokens"], l0,
-                                 l0 + win_layers, ring_dev, slot, n_slots, wg, 0)
+                                 l0 + win_layers, ring_dev, slot, n_slots, wg, flags)
 
     parity = {}
     try:
@@ -385,20 +409,26 @@ def host_leg(args, dev):
         if args.dma_baseline:
             tab_h = np.ascontiguousarray(w["block_tables"][0], dtype=np.int32)
             spans_dma = K.make_spans([(tab_h.ctypes.data, tab_h.size, 0, T, 0)])
-            for name, fn, ref in (("scatter", K.kv_scatter_chunks_dma, "h2d"),
-                                  ("gather", K.kv_gather_chunks_dma, "d2h")):
-                torch.cuda.synchronize()
-                K.kv_pool_timing_start(P.h)
-                t0 = time.perf_counter()
-                fn(P.h, spans_dma, spec_for(0), stream)
-                submit = time.perf_counter() - t0
-                ms, n = K.kv_pool_timing_read(P.h)
-                moved = payload_layer * win_layers
-                dma[name] = dict(gbs=round(moved / (ms * 1e-3) / 1e9, 2), link_frac=round(moved / (ms * 1e-3) / 1e9 / link[ref], 4),
-                                 ms=round(ms, 2), copies=win_layers * KV * (T // w["block_size"]),
-                                 host_submit_ms=round(submit * 1e3, 2), bytes=moved)
-            log("per-tile hipMemcpyAsync over the host link: scatter %.1f GB/s, gather %.1f GB/s" % (
-                dma["scatter"]["gbs"], dma["gather"]["gbs"]))
+            tiles_win = win_layers * KV * (T // w["block_size"])
+            group = w["chunk_layers"] * KV
+            for mode, flags, copies in (("per_tile", 0, tiles_win),
+                                        ("strided", K.KV_FLAG_DMA_STRIDED, tiles_win // group)):
+                out_dma = dma if mode == "per_tile" else dma.setdefault("strided", {})
+                for name, fn, ref in (("scatter", K.kv_scatter_chunks_dma, "h2d"),
+                                      ("gather", K.kv_gather_chunks_dma, "d2h")):
+                    torch.cuda.synchronize()
+                    K.kv_pool_timing_start(P.h)
+                    t0 = time.perf_counter()
+                    fn(P.h, spans_dma, spec_for(0, 0, flags), stream)
+                    submit = time.perf_counter() - t0
+                    ms, n = K.kv_pool_timing_read(P.h)
+                    moved = payload_layer * win_layers
+                    out_dma[name] = dict(gbs=round(moved / (ms * 1e-3) / 1e9, 2),
+                                         link_frac=round(moved / (ms * 1e-3) / 1e9 / link[ref], 4),
+                                         ms=round(ms, 2), copies=copies,
+                                         host_submit_ms=round(submit * 1e3, 2), bytes=moved)
+                log("%s hipMemcpy(2D)Async over the host link: scatter %.1f GB/s, gather %.1f GB/s" % (
+                    mode, out_dma["scatter"]["gbs"], out_dma["gather"]["gbs"]))
 
         windows = L // win_layers if args.host_windows <= 0 else args.host_windows
         out = {}
@@ -720,12 +750,13 @@ def main():
     cpu = cpu_baseline(res, args.cpu_budget) if args.cpu_baseline else None
     res.pop("host_sample", None)
     host = host_leg(args, dev) if args.host_path else None
-    others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64"], 5) \
+    others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8"], 5) \
         if args.others else None
     pipeline = pipeline_leg(args, dev) if args.pipeline else None
 
     w = res["w"]
-    traffic = traffic_for(2 * res["payload"])
+    # the committed counter summary covers the default workload only
+    traffic = traffic_for(2 * res["payload"]) if args.workload == "llama8b" else None
     out = {
         "metric": METRIC,
         "value": round(res["value"], 2),
@@ -740,10 +771,9 @@ def main():
         "dtype": "u8",
         "data": "synthetic",
         "config": {
-            "workload": "llama8b: 32 layers x K/V x 8 heads x 128 dims bf16, 16-token pages (32 KiB "
-                        "per layer-page), 16384-block pool, one 32768-token request with a shuffled "
-                        "block table, 256-token layer-first chunks in HBM; step = gather + scatter",
-            "global_batch": 1, "seq_len": w["tokens"], "parallelism": "none",
+            "workload": describe(args.workload, w),
+            "global_batch": len(w["requests"]), "seq_len": max(t1 - t0 for t0, t1 in w["requests"]),
+            "parallelism": "none",
             "payload_bytes_each_way": res["payload"], "tiles_per_launch": res["tiles"],
             "chunks": res["chunks"],
         },
@@ -754,7 +784,8 @@ def main():
             "unit": "GB/s",
             "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "kvx::tile_copy (gather and scatter, layer-first), %d launches averaged" % res["launches"],
+            "kernel": "kvx::tile_copy (gather and scatter, %s), %d launches averaged" % (
+                "layer-first" if w["layout"] == 0 else "page-first", res["launches"]),
         },
         "cpu_baseline": cpu,
         "breakdown": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res["per_dir"].items()},

@@ -112,6 +112,9 @@ extern "C" {
 /* kv_chunk_spec.flags */
 #define KV_FLAG_VALIDATE 0x1 /* copy the block tables to the host (synchronously) and check
                                 ids in range and, for scatter, one writer per pool page */
+#define KV_FLAG_DMA_STRIDED 0x2 /* read by the _dma entry points only: where the regions are
+                                   evenly spaced, one strided copy per (chunk, page) covers
+                                   the page's chunk_layers*num_kv tiles */
 
 /* device error bits reported through kv_pool_get_error */
 #define KV_DEVERR_BLOCK_RANGE 0x1 /* a block table held an id outside [0, num_blocks); that
@@ -241,7 +244,11 @@ KV_API int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_span
  * every block id of the call is checked on the host before any copy is issued
  * (KV_ERR_RANGE; for scatter also KV_ERR_DUP).  Host work is O(tiles).  The tables
  * are read during the call only.  A head-major pool takes one hipMemcpy2DAsync per
- * (tile, head) instead. */
+ * (tile, head) instead.  With KV_FLAG_DMA_STRIDED and token-major pages whose
+ * regions are evenly spaced (bases[i+1] - bases[i] the same positive value for all
+ * i), the tiles of one page in one chunk -- one per (layer, kv) of the chunk --
+ * go as one hipMemcpy2DAsync of chunk_layers*num_kv rows (the "where strides allow"
+ * variant of the conventional engine); otherwise the flag changes nothing. */
 KV_API int kv_gather_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                                 const kv_chunk_spec *spec, hipStream_t stream);
 KV_API int kv_scatter_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,

@@ -105,7 +105,7 @@ int check_spec(const kv_pool_desc *d, const kv_chunk_spec *s)
     if (s->slot_bytes % 16 != 0) return KV_ERR_ALIGN;
     if (s->n_slots > INT64_MAX / s->slot_bytes) return KV_ERR_ARG;
     if (s->max_workgroups < 0) return KV_ERR_ARG;
-    if (s->flags & ~KV_FLAG_VALIDATE) return KV_ERR_ARG;
+    if (s->flags & ~(KV_FLAG_VALIDATE | KV_FLAG_DMA_STRIDED)) return KV_ERR_ARG;
     return KV_OK;
 }
 
@@ -507,33 +507,33 @@ int transfer_dma(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chu
     if (rc) return rc;
     const bool timed = p->timing && p->n_timed < kMaxTimed;
     if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
-    uint32_t s = 0;
-    for (int64_t tile = 0; tile < a.total_tiles; ++tile) {
-        s = kvx::find_span(rec.data(), s, n_rec, tile);
-        const kvx::SpanDev &sp = rec[s];
-        const kvx::TileRef t = a.layout == KV_LAYER_FIRST
-                                   ? kvx::resolve_tile<KV_LAYER_FIRST>(a, sp, tile)
-                                   : kvx::resolve_tile<KV_PAGE_FIRST>(a, sp, tile);
-        uint8_t *pool = static_cast<uint8_t *>(p->bases[t.region]) + (int64_t)sp.table[t.page] * a.block_stride;
-        uint8_t *chunk = a.chunk_base + t.chunk_off;
-        if (a.page_layout == KV_PAGE_TOKEN_MAJOR) {
-            void *dst = direction == KV_GATHER ? (void *)chunk : (void *)pool;
-            const void *src = direction == KV_GATHER ? (const void *)pool : (const void *)chunk;
-            if (!HIP_OK(hipMemcpyAsync(dst, src, t.nbytes, hipMemcpyDefault, stream))) return KV_ERR_HIP;
-            continue;
-        }
-        // head-major: one strided copy per head, n_tok rows of D*E bytes
-        const size_t row = (size_t)a.hm_r16 * 16, n_tok = t.nbytes / a.tok;
-        for (uint32_t h = 0; h < a.hm_heads; ++h) {
-            uint8_t *ph = pool + (size_t)h * a.hm_bs_r16 * 16;
-            uint8_t *ch = chunk + (size_t)h * row;
-            const size_t cp = (size_t)a.hm_heads * row;
-            hipError_t e = direction == KV_GATHER
-                               ? hipMemcpy2DAsync(ch, cp, ph, row, row, n_tok, hipMemcpyDefault, stream)
-                               : hipMemcpy2DAsync(ph, row, ch, cp, row, n_tok, hipMemcpyDefault, stream);
-            if (!hip_ok(e, "hipMemcpy2DAsync")) return KV_ERR_HIP;
-        }
-    }
+    // host block table of each record (records skip empty spans)
+    std::vector<const int32_t *> rec_tables;
+    rec_tables.reserve(n_rec);
+    for (int32_t i = 0; i < n_spans; ++i)
+        if (spans[i].t_end > spans[i].t_begin) rec_tables.push_back(spans[i].block_table);
+    const int64_t n_regions = (int64_t)p->desc.num_layers * p->desc.num_kv;
+    const bool strided = (spec->flags & KV_FLAG_DMA_STRIDED) != 0;
+    const int64_t pitch = strided ? kvx::uniform_region_pitch(p->bases.data(), n_regions) : 0;
+    const bool gather = direction == KV_GATHER;
+    rc = kvx::dma_walk(a, rec.data(), n_rec, rec_tables.data(), p->bases.data(), pitch, strided,
+                       [&](const kvx::DmaCopy &c) -> int {
+                           void *dst = gather ? (void *)c.chunk : (void *)c.pool;
+                           const void *src = gather ? (const void *)c.pool : (const void *)c.chunk;
+                           if (c.rows == 1)
+                               return HIP_OK(hipMemcpyAsync(dst, src, (size_t)c.width, hipMemcpyDefault,
+                                                            stream))
+                                          ? 0
+                                          : KV_ERR_HIP;
+                           const size_t dp = (size_t)(gather ? c.chunk_pitch : c.pool_pitch);
+                           const size_t sp = (size_t)(gather ? c.pool_pitch : c.chunk_pitch);
+                           return hip_ok(hipMemcpy2DAsync(dst, dp, src, sp, (size_t)c.width,
+                                                          (size_t)c.rows, hipMemcpyDefault, stream),
+                                         "hipMemcpy2DAsync")
+                                      ? 0
+                                      : KV_ERR_HIP;
+                       });
+    if (rc) return rc;
     if (timed) {
         if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;
         ++p->n_timed;

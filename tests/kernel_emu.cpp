@@ -104,3 +104,48 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
         if (seen[i] != 1) ++*violations;
     return KV_OK;
 }
+
+// The copy-engine path's plan (kvx::dma_walk, as kv_*_chunks_dma issue it), carried
+// out with memcpy on host buffers.  Every row of every copy is checked against the
+// region it must lie in and the staging buffer first.  spans[i].block_table are host
+// arrays here, as for the _dma entry points.
+extern "C" int emu_dma(int direction, const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
+                       const kv_chunk_spec *spec, const int64_t *region_bytes, int64_t staging_bytes,
+                       int32_t strided, int64_t *violations, int64_t *copies_out, int64_t *rows_out)
+{
+    static kvx::SpanDev records[KV_MAX_SPANS];
+    uint32_t n_rec = 0;
+    kvx::Launch a;
+    kv_transfer_info info;
+    int rc = kvx::prepare_call(d, spans, n_spans, spec, records, &n_rec, &a, &info);
+    if (rc) return rc;
+    std::vector<const int32_t *> tables;
+    for (int32_t i = 0; i < n_spans; ++i)
+        if (spans[i].t_end > spans[i].t_begin) tables.push_back(spans[i].block_table);
+    const int64_t nreg = (int64_t)d->num_layers * d->num_kv;
+    const int64_t pitch = strided ? kvx::uniform_region_pitch(d->bases, nreg) : 0;
+    *violations = 0;
+    *copies_out = 0;
+    *rows_out = 0;
+    uint8_t *stg = static_cast<uint8_t *>(spec->base);
+    return kvx::dma_walk(a, records, n_rec, tables.data(), d->bases, pitch, strided != 0,
+                         [&](const kvx::DmaCopy &c) -> int {
+                             ++*copies_out;
+                             for (int64_t i = 0; i < c.rows; ++i) {
+                                 const int64_t r = c.region + i * c.region_step;
+                                 uint8_t *pool = c.pool + i * c.pool_pitch;
+                                 uint8_t *chunk = c.chunk + i * c.chunk_pitch;
+                                 uint8_t *rb = static_cast<uint8_t *>(d->bases[r]);
+                                 ++*rows_out;
+                                 if (r < 0 || r >= nreg || c.width <= 0 || pool < rb ||
+                                     pool + c.width > rb + region_bytes[r] || chunk < stg ||
+                                     chunk + c.width > stg + staging_bytes) {
+                                     ++*violations;
+                                     continue;
+                                 }
+                                 if (direction == KV_GATHER) std::memcpy(chunk, pool, (size_t)c.width);
+                                 else std::memcpy(pool, chunk, (size_t)c.width);
+                             }
+                             return 0;
+                         });
+}

@@ -127,6 +127,7 @@ REDUCED = {
                   max_len=3000),
     "mla_fp8": dict(num_layers=5, chunk_layers=5, tokens=64 * 9 + 13, num_blocks=40),
     "int8_kv": dict(num_layers=3, chunk_layers=3, tokens=64 * 7 + 1, num_blocks=30),
+    "llama8b_tp8": dict(num_layers=4, chunk_layers=2, tokens=16 * 37 + 9, num_blocks=80),
 }
 
 
@@ -239,6 +240,19 @@ def test_per_tile_dma_baseline_matches_oracle(seed):
     regions, staging = _random(pool, chunks, seed)
     for d in DIRS:
         _compare(d, pool, spans, chunks, regions, staging, "dma-%d" % seed, dma=True, ring=bool(seed % 2))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_strided_dma_matches_oracle(seed):
+    """KV_FLAG_DMA_STRIDED: one hipMemcpy2DAsync per (chunk, page) over the page's
+    (layer, kv) tiles (the regions are rows of one tensor, so evenly spaced); head-major
+    cases keep their per-head copies."""
+    pool, spans, chunks = cases.make_case(np.random.default_rng(72_000 + seed), tok_multiple=16,
+                                          medium=bool(seed % 3), max_bytes=24 << 20, head_major=None)
+    regions, staging = _random(pool, chunks, seed)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "dma-strided-%d" % seed, dma=True,
+                 ring=bool(seed % 2), flags=K.KV_FLAG_DMA_STRIDED)
 
 
 def test_per_tile_dma_rejects_bad_ids_before_copying():

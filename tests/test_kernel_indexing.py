@@ -37,6 +37,11 @@ def _build_emu(tmp_path_factory, defines=()):
                                  ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.c_void_p,
                                  ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.emu_dma.restype = ctypes.c_int
+    lib.emu_dma.argtypes = [ctypes.c_int, ctypes.POINTER(K.kv_pool_desc), ctypes.POINTER(K.kv_span),
+                            ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.c_void_p, ctypes.c_int64,
+                            ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                            ctypes.POINTER(ctypes.c_int64)]
     return lib
 
 
@@ -115,7 +120,7 @@ def test_emulated_split_tiles_match_oracle(emu_split, seed):
     _copy_case(emu_split, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
 
 
-FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64"]
+FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -174,3 +179,66 @@ def test_emulated_extreme_shapes(emu, name, layout, page_layout):
     and must never be read)."""
     pool, spans, chunks = _extreme_case(name, layout, page_layout)
     _copy_case(emu, pool, spans, chunks, 3)
+
+
+def _dma_case(lib, pool, spans, chunks, seed, strided, even_regions=True):
+    """The copy-engine plan carried out on host buffers must equal the oracle; returns
+    (copies, rows) of the gather."""
+    rng = np.random.default_rng(seed)
+    regions = cases.regions_for(pool, rng)
+    staging = cases.staging_for(chunks, rng=rng)
+    n = regions.shape[0]
+    tabs = [np.ascontiguousarray(t, dtype=np.int32) for t, _, _, _ in spans]
+    sp = K.make_spans([(t.ctypes.data, t.size, t0, t1, fc) for t, (_, t0, t1, fc) in zip(tabs, spans)])
+    counts = None
+    for d in (K.KV_GATHER, K.KV_SCATTER):
+        # region i lives in row order[i]; reversed rows are not evenly spaced in ascending order
+        order = list(range(n)) if even_regions else list(range(n))[::-1]
+        r_emu, s_emu = regions[order].copy(), staging.copy()
+        bases = [r_emu[order[i]].ctypes.data for i in range(n)]
+        desc = K.make_pool_desc(pool["num_layers"], pool["num_kv"], pool["num_heads"], pool["head_dim"],
+                                pool["elem_bytes"], pool["block_size"], pool["num_blocks"],
+                                pool["block_stride"], bases, pool.get("page_layout", 0))
+        spec = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"],
+                                 chunks["layer_begin"], chunks["layer_end"], s_emu.ctypes.data,
+                                 chunks["slot_bytes"], chunks["n_slots"], 0, K.KV_FLAG_DMA_STRIDED if strided else 0)
+        rb = np.full(n, r_emu.shape[1], dtype=np.int64)
+        viol, copies, rows = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        rc = lib.emu_dma(d, ctypes.byref(desc), sp, len(spans), ctypes.byref(spec), rb.ctypes.data,
+                         s_emu.size, int(strided), ctypes.byref(viol), ctypes.byref(copies), ctypes.byref(rows))
+        assert rc == 0, K.kv_strerror(rc)
+        assert viol.value == 0
+        r_emu = r_emu[order]          # back to region order (order is its own inverse)
+        r_or, s_or = regions.copy(), staging.copy()
+        oracle.transfer(d, pool, r_or, spans, chunks, s_or)
+        assert np.array_equal(s_emu, s_or) and np.array_equal(r_emu, r_or)
+        if counts is None:
+            counts = (copies.value, rows.value)
+    return counts
+
+
+@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("strided", [False, True])
+def test_dma_plan_matches_oracle(emu, seed, strided):
+    """Per-tile and strided copy-engine plans, both chunk layouts, both page layouts."""
+    pool, spans, chunks = cases.make_case(np.random.default_rng(29_000 + seed), tok_multiple=16,
+                                          medium=bool(seed % 2), max_bytes=24 << 20, head_major=None)
+    copies, rows = _dma_case(emu, pool, spans, chunks, seed, strided)
+    tiles = sum((chunks["layer_end"] - chunks["layer_begin"]) * pool["num_kv"] * cases.cdiv(t1 - t0, pool["block_size"])
+                for _, t0, t1, _ in spans)
+    per_tile = tiles * (pool["num_heads"] if pool.get("page_layout", 0) else 1)
+    group = chunks["chunk_layers"] * pool["num_kv"]
+    if strided and not pool.get("page_layout", 0) and group > 1:
+        assert copies * group == tiles
+    else:
+        assert copies == per_tile
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dma_strided_plan_falls_back_on_uneven_regions(emu, seed):
+    pool, spans, chunks = cases.make_case(np.random.default_rng(29_500 + seed), tok_multiple=16,
+                                          max_bytes=8 << 20, head_major=False)
+    copies, _ = _dma_case(emu, pool, spans, chunks, seed, True, even_regions=False)
+    tiles = sum((chunks["layer_end"] - chunks["layer_begin"]) * pool["num_kv"] * cases.cdiv(t1 - t0, pool["block_size"])
+                for _, t0, t1, _ in spans)
+    assert copies == tiles
