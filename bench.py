@@ -541,7 +541,9 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
         return t, 4 * win_layers * payload_layer / (ms * 1e-3) / 1e9
 
     reps = {"gemm_8192": 100, "gemm_prefill": 150, "elementwise": 60}
-    whole_c, whole_t = torch.cuda.Stream(), torch.cuda.Stream()
+    # whole-chip streams with a hardware queue each (pool streams may share a queue)
+    h_wc, whole_c = masked(dev, range(n_cu))
+    h_wt, whole_t = masked(dev, range(n_cu))
     io_cus = list(range(8))
     h_io, io = masked(dev, io_cus)
     h_cmp, cmp = masked(dev, [i for i in range(n_cu) if i not in io_cus])
@@ -566,8 +568,8 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
         assert K.kv_pool_get_error(P.h, whole_t) == 0
     finally:
         torch.cuda.synchronize()
-        destroy_stream(h_io)
-        destroy_stream(h_cmp)
+        for h in (h_io, h_cmp, h_wc, h_wt):
+            destroy_stream(h)
     log("interference: " + json.dumps(out))
     del ops, x
     return out
@@ -604,8 +606,13 @@ def pipeline_leg(args, dev):
     w_down = torch.randn(ffn, hidden, dtype=torch.bfloat16, device=dev)
     h_up = torch.empty(new_tok, 2 * ffn, dtype=torch.bfloat16, device=dev)
     y = torch.empty(new_tok, hidden, dtype=torch.bfloat16, device=dev)
-    shared_streams = (torch.cuda.Stream(), torch.cuda.Stream())
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    # Both streams of the shared case get the whole chip but a hardware queue each
+    # (streams from torch's pool can share one of the few hardware queues, which
+    # serialises their work).
+    h_cs, cs = cu_masked_stream(dev, range(n_cu))
+    h_ts, ts = cu_masked_stream(dev, range(n_cu))
+    shared_streams = (cs, ts)
     h_io, io = cu_masked_stream(dev, range(8))
     h_cmp, cmp = cu_masked_stream(dev, range(8, n_cu))
     compute, transfer = shared_streams
@@ -687,8 +694,8 @@ def pipeline_leg(args, dev):
         return res
     finally:
         torch.cuda.synchronize()
-        destroy_stream(h_io)
-        destroy_stream(h_cmp)
+        for h in (h_io, h_cmp, h_cs, h_ts):
+            destroy_stream(h)
         K.kv_ring_destroy(ring)
         P.close()
         del P

@@ -280,11 +280,8 @@ struct kv_pool {
     // the oldest call in flight is always the next one in the way.
     uint8_t *d_arena = nullptr;
     uint8_t *h_arena = nullptr;
-    hipEvent_t fl_ev[kInflight] = {};
-    int64_t fl_off[kInflight] = {};
-    int64_t fl_bytes[kInflight] = {};
-    int fl_first = 0, fl_count = 0;
-    int64_t arena_head = 0;
+    kvx::ArenaRing<kInflight> arena;
+    hipEvent_t fl_ev[kInflight] = {};  // one per arena slot
     // staging-memory kind of the last staging base seen
     const void *last_base = nullptr;
     bool last_base_host = false;
@@ -316,44 +313,30 @@ void free_device_state(kv_pool *p)
         if (p->fl_ev[i]) (void)hipEventDestroy(p->fl_ev[i]), p->fl_ev[i] = nullptr;
     if (p->h_arena) (void)hipHostFree(p->h_arena), p->h_arena = nullptr;
     if (p->d_arena) (void)hipFree(p->d_arena), p->d_arena = nullptr;
-    p->fl_first = p->fl_count = 0;
-    p->arena_head = 0;
+    p->arena.reset();
     if (p->d_err) (void)hipFree(p->d_err), p->d_err = nullptr;
     if (p->d_regions) (void)hipFree(p->d_regions), p->d_regions = nullptr;
     p->device = -1;
 }
 
-// Reserve `bytes` of the span-record arena for one call.  The host waits only for
-// calls still using that stretch, or for the oldest call when kInflight are queued.
+// Reserve `bytes` of the span-record arena for one call, waiting for the calls
+// that still use them (or for the oldest call when kInflight are queued).
 int arena_take(kv_pool *p, int64_t bytes, int64_t *off)
 {
-    int64_t start = p->arena_head;
-    if (start + bytes > kArenaBytes) start = 0;
-    while (p->fl_count > 0) {
-        const int i = p->fl_first;
-        const bool overlap = p->fl_off[i] < start + bytes && start < p->fl_off[i] + p->fl_bytes[i];
-        if (!overlap && p->fl_count < kInflight) break;
-        if (!HIP_OK(hipEventSynchronize(p->fl_ev[i]))) return KV_ERR_HIP;
-        p->fl_first = (i + 1) % kInflight;
-        --p->fl_count;
-    }
-    *off = start;
-    return KV_OK;
+    return p->arena.take(bytes, off, [p](int i) {
+        return HIP_OK(hipEventSynchronize(p->fl_ev[i])) ? 0 : KV_ERR_HIP;
+    });
 }
 
 // Mark the stretch as used by the work just queued on `stream`.
 int arena_commit(kv_pool *p, int64_t off, int64_t bytes, hipStream_t stream)
 {
-    const int i = (p->fl_first + p->fl_count) % kInflight;
-    if (!HIP_OK(hipEventRecord(p->fl_ev[i], stream))) {
+    if (!HIP_OK(hipEventRecord(p->fl_ev[p->arena.next_slot()], stream))) {
         // cannot fence the stretch: wait for the work instead so it is free again
         (void)hipStreamSynchronize(stream);
         return KV_ERR_HIP;
     }
-    p->fl_off[i] = off;
-    p->fl_bytes[i] = bytes;
-    ++p->fl_count;
-    p->arena_head = off + bytes;
+    p->arena.commit(off, bytes);
     return KV_OK;
 }
 
@@ -371,6 +354,8 @@ int device_setup(kv_pool *p)
     if (!HIP_OK(hipMemset(p->d_err, 0, sizeof(int32_t)))) goto fail;
     if (!HIP_OK(hipMalloc(&p->d_arena, kArenaBytes))) goto fail;
     if (!HIP_OK(hipHostMalloc((void **)&p->h_arena, kArenaBytes, hipHostMallocDefault))) goto fail;
+    p->arena.reset();
+    p->arena.size = kArenaBytes;
     for (int i = 0; i < kInflight; ++i)
         if (!HIP_OK(hipEventCreateWithFlags(&p->fl_ev[i], hipEventDisableTiming))) goto fail;
     p->device = dev;

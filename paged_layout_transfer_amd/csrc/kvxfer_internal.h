@@ -272,6 +272,54 @@ int prepare_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
                  const kv_chunk_spec *spec, SpanDev *records, uint32_t *n_records, Launch *launch,
                  kv_transfer_info *info);
 
+// ---- span-record arena (host bookkeeping) -----------------------------------
+
+// Byte ranges of a circular buffer of `size` bytes reserved by up to N calls in
+// flight, oldest first.  Reservations are sequential: a call takes the bytes after
+// the previous one, or wraps to offset 0 when they do not fit before the end (the
+// skipped tail then counts as taken too).  take() retires, oldest first, every call
+// whose bytes the new reservation needs -- and the oldest call whenever N are in
+// flight -- by calling wait(slot), which returns nonzero to abort.
+template <int N>
+struct ArenaRing {
+    int64_t size = 0;
+    int64_t off[N] = {}, bytes[N] = {};
+    int first = 0, count = 0;
+    int64_t head = 0;
+
+    void reset() { first = count = 0, head = 0; }
+
+    template <class Wait>
+    int take(int64_t b, int64_t *out, Wait wait)
+    {
+        int64_t start = head;
+        bool wrapped = false;
+        if (start + b > size) start = 0, wrapped = true;
+        while (count > 0) {
+            const int i = first;
+            // calls at or after the old head precede the wrap: they are the oldest
+            const bool in_tail = wrapped && off[i] >= head;
+            const bool overlap = off[i] < start + b && start < off[i] + bytes[i];
+            if (!in_tail && !overlap && count < N) break;
+            if (int rc = wait(i)) return rc;
+            first = (i + 1) % N;
+            --count;
+        }
+        *out = start;
+        return 0;
+    }
+    // Slot of the next commit (for the caller's per-call event).
+    int next_slot() const { return (first + count) % N; }
+    void commit(int64_t o, int64_t b)
+    {
+        const int i = next_slot();
+        off[i] = o;
+        bytes[i] = b;
+        ++count;
+        head = o + b;
+    }
+};
+
 // ---- the copy-engine path (host) ------------------------------------------
 
 // One copy issued by the host: `rows` rows of `width` bytes; row i lies at

@@ -149,3 +149,39 @@ extern "C" int emu_dma(int direction, const kv_pool_desc *d, const kv_span *span
                              return 0;
                          });
 }
+
+// The span-record arena's bookkeeping (kvx::ArenaRing) driven by a sequence of call
+// sizes, with calls finishing only when the arena waits for them (the slowest
+// device) or, with `lag` > 0, also on their own once `lag` newer calls exist.  Every
+// reservation must stay inside the arena and must not overlap the bytes of any call
+// still in flight; returns the number of violations.
+extern "C" int64_t emu_arena(int64_t size, const int64_t *sizes, int64_t n_calls, int32_t lag)
+{
+    constexpr int N = 256;
+    static kvx::ArenaRing<N> ring;
+    ring.reset();
+    ring.size = size;
+    struct Live { int64_t off, bytes, call; };
+    std::vector<Live> live;       // calls not yet finished, in call order
+    std::vector<int64_t> slot_call(N, -1);
+    int64_t violations = 0;
+    for (int64_t c = 0; c < n_calls; ++c) {
+        if (lag > 0)
+            while (!live.empty() && live.front().call + lag <= c) live.erase(live.begin());
+        int64_t off = -1;
+        ring.take(sizes[c], &off, [&](int slot) {
+            // waiting for the call in this slot finishes it (and every older call)
+            const int64_t call = slot_call[slot];
+            while (!live.empty() && live.front().call <= call) live.erase(live.begin());
+            return 0;
+        });
+        if (off < 0 || off + sizes[c] > size) ++violations;
+        for (const Live &l : live)
+            if (l.off < off + sizes[c] && off < l.off + l.bytes) ++violations;
+        slot_call[ring.next_slot()] = c;
+        ring.commit(off, sizes[c]);
+        live.push_back({off, sizes[c], c});
+        if ((int64_t)live.size() > N) ++violations;  // more than N calls in flight
+    }
+    return violations;
+}

@@ -37,6 +37,8 @@ def _build_emu(tmp_path_factory, defines=()):
                                  ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.c_void_p,
                                  ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.emu_arena.restype = ctypes.c_int64
+    lib.emu_arena.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
     lib.emu_dma.restype = ctypes.c_int
     lib.emu_dma.argtypes = [ctypes.c_int, ctypes.POINTER(K.kv_pool_desc), ctypes.POINTER(K.kv_span),
                             ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.c_void_p, ctypes.c_int64,
@@ -242,3 +244,20 @@ def test_dma_strided_plan_falls_back_on_uneven_regions(emu, seed):
     tiles = sum((chunks["layer_end"] - chunks["layer_begin"]) * pool["num_kv"] * cases.cdiv(t1 - t0, pool["block_size"])
                 for _, t0, t1, _ in spans)
     assert copies == tiles
+
+
+@pytest.mark.parametrize("lag", [0, 3, 40, 200])
+@pytest.mark.parametrize("pattern", ["queue_test", "random", "large_only"])
+def test_span_record_arena_never_overwrites_calls_in_flight(emu, pattern, lag):
+    """The arena bookkeeping the transfer calls use (kvx::ArenaRing, 4 MiB, 256 calls in
+    flight): no reservation may overlap a call that has not finished.  Record sizes are
+    64 bytes per span rounded up to 256, as the library reserves them."""
+    rng = np.random.default_rng(31_000 + lag)
+    if pattern == "queue_test":        # every eighth call carries 4096 spans
+        spans = [4096 if i % 8 == 0 else 1 for i in range(5000)]
+    elif pattern == "large_only":
+        spans = [int(x) for x in rng.integers(3000, 4097, size=3000)]
+    else:
+        spans = [int(x) for x in rng.choice([1, 2, 17, 300, 1000, 4096], size=5000)]
+    sizes = np.array([(64 * n + 255) // 256 * 256 for n in spans], dtype=np.int64)
+    assert emu.emu_arena(4 << 20, sizes.ctypes.data, sizes.size, lag) == 0
