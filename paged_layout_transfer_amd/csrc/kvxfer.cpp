@@ -18,6 +18,7 @@
 #include <new>
 #include <vector>
 
+#include "kvxfer_host.h"
 #include "kvxfer_internal.h"
 
 namespace {

@@ -10,6 +10,7 @@
 #include <cstring>
 #include <vector>
 
+#include "kvxfer_host.h"
 #include "kvxfer_internal.h"
 
 extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span *spans,
