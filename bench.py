@@ -495,8 +495,9 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
     "Non-Intrusive Resource Sizing"; the Tutti summary partitions SMs between
     compute and I/O).  A bf16 GEMM and a bandwidth-bound elementwise kernel are
     timed alone, then while scatter windows stream from the host ring on a second
-    stream: first with both streams on the whole chip at three transfer grid sizes,
-    then with CU-masked streams (the transfer on 8 CUs, compute on the other 248)."""
+    stream: first with both streams on the whole chip at three transfer grid sizes
+    (and at the default grid with plain cached instead of nontemporal accesses), then
+    with CU-masked streams (the transfer on 8 CUs, compute on the other 248)."""
     import torch
     from paged_layout_transfer_amd import kvxfer as K
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -527,11 +528,11 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
         e1.record(stream)
         return e0, e1
 
-    def measure(kind, n, compute, transfer=None, wg=0):
+    def measure(kind, n, compute, transfer=None, wg=0, flags=0):
         if transfer is not None:
             K.kv_pool_timing_start(P.h)
             for i in range(4):
-                K.kv_scatter_chunks(P.h, spans_d, spec_for((i * win_layers) % L, wg), transfer)
+                K.kv_scatter_chunks(P.h, spans_d, spec_for((i * win_layers) % L, wg, flags), transfer)
         e0, e1 = timed(kind, n, compute)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / n
@@ -559,6 +560,10 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
                 t, gbs = measure(kind, n, whole_c, whole_t, wg)
                 row["shared_grid_%s" % (wg if wg else "default16")] = {
                     "ms": round(t, 4), "slowdown": round(t / alone - 1, 4), "transfer_gbs": round(gbs, 2)}
+            # the same default-grid reload with plain cached stores instead of nontemporal ones
+            t, gbs = measure(kind, n, whole_c, whole_t, 0, K.KV_FLAG_CACHED)
+            row["shared_grid_default16_cached"] = {
+                "ms": round(t, 4), "slowdown": round(t / alone - 1, 4), "transfer_gbs": round(gbs, 2)}
             t_alone_masked, _ = measure(kind, n, cmp)
             t, gbs = measure(kind, n, cmp, io, 0)
             row["partitioned"] = {"compute_alone_ms": round(t_alone_masked, 4),

@@ -115,6 +115,11 @@ extern "C" {
 #define KV_FLAG_DMA_STRIDED 0x2 /* read by the _dma entry points only: where the regions are
                                    evenly spaced, one strided copy per (chunk, page) covers
                                    the page's chunk_layers*num_kv tiles */
+#define KV_FLAG_CACHED 0x4 /* kernel entry points: plain cached loads and stores instead of the
+                              default nontemporal ones (same bytes, same result).  The default
+                              keeps a transfer from evicting the working set of kernels that
+                              run beside it (Strata guide, "Non-Intrusive Resource Sizing");
+                              this flag is for callers that touch the moved bytes right after */
 
 /* device error bits reported through kv_pool_get_error */
 #define KV_DEVERR_BLOCK_RANGE 0x1 /* a block table held an id outside [0, num_blocks); that

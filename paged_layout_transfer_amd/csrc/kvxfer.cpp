@@ -106,7 +106,7 @@ int check_spec(const kv_pool_desc *d, const kv_chunk_spec *s)
     if (s->slot_bytes % 16 != 0) return KV_ERR_ALIGN;
     if (s->n_slots > INT64_MAX / s->slot_bytes) return KV_ERR_ARG;
     if (s->max_workgroups < 0) return KV_ERR_ARG;
-    if (s->flags & ~(KV_FLAG_VALIDATE | KV_FLAG_DMA_STRIDED)) return KV_ERR_ARG;
+    if (s->flags & ~(KV_FLAG_VALIDATE | KV_FLAG_DMA_STRIDED | KV_FLAG_CACHED)) return KV_ERR_ARG;
     return KV_OK;
 }
 
@@ -226,6 +226,7 @@ int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
     a->block_size = (uint32_t)d->block_size;
     a->layout = (uint32_t)spec->layout;
     a->page_layout = (uint32_t)d->page_layout;
+    a->cached = (spec->flags & KV_FLAG_CACHED) ? 1u : 0u;
     if (d->page_layout == KV_PAGE_HEAD_MAJOR) {
         const uint32_t r16 = (uint32_t)((int64_t)d->head_dim * d->elem_bytes / 16);
         const uint32_t H = (uint32_t)d->num_heads;

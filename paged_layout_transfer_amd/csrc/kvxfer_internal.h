@@ -75,12 +75,6 @@ namespace kvx {
 #ifndef KVX_TAIL_GROUP
 #define KVX_TAIL_GROUP 4       // vectors per lane per group after the full groups
 #endif
-#ifndef KVX_NT_LOAD
-#define KVX_NT_LOAD 1          // nontemporal loads
-#endif
-#ifndef KVX_NT_STORE
-#define KVX_NT_STORE 1         // nontemporal stores
-#endif
 // Cache-policy bits of a gfx950 buffer load/store (the builtin's last argument).
 #define KVX_POL_SC0 1
 #define KVX_POL_NT 2
@@ -140,7 +134,7 @@ struct Launch {
     uint32_t hm_r16;
     uint32_t hm_bs_r16;
     uint32_t hm_dq, hm_dh, hm_dj;
-    uint32_t pad_;
+    uint32_t cached;       // 1: plain cached loads and stores (KV_FLAG_CACHED), else nontemporal
 };
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,

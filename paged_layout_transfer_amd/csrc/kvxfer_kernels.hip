@@ -64,22 +64,19 @@ __device__ __forceinline__ SpanDev load_span(const KVX_CONST SpanDev *p)
     return r;
 }
 
+// NT: nontemporal (the default policy) or plain cached accesses (KV_FLAG_CACHED).
+template <bool NT>
 __device__ __forceinline__ u32x4 ld(const gvec *p)
 {
-#if KVX_NT_LOAD
-    return __builtin_nontemporal_load(p);
-#else
+    if (NT) return __builtin_nontemporal_load(p);
     return *p;
-#endif
 }
 
+template <bool NT>
 __device__ __forceinline__ void st(gvec *p, u32x4 v)
 {
-#if KVX_NT_STORE
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
 }
 
 // One side of a tile copy, addressed in 16-byte vectors from the start of its range.
@@ -87,11 +84,16 @@ __device__ __forceinline__ void st(gvec *p, u32x4 v)
 // range, which lets the instruction carry an explicit cache policy (the gfx950 buffer
 // instructions' sc0 / nt / sc1 bits, KVX_POL_*) and makes the hardware drop any
 // access past the range's end.
+template <bool NT>
 struct PtrSide {
     gvec *p;
-    __device__ __forceinline__ u32x4 load(uint32_t v) const { return ld(p + v); }
-    __device__ __forceinline__ void store(uint32_t v, u32x4 x) const { st(p + v, x); }
+    __device__ __forceinline__ u32x4 load(uint32_t v) const { return ld<NT>(p + v); }
+    __device__ __forceinline__ void store(uint32_t v, u32x4 x) const { st<NT>(p + v, x); }
 };
+
+// Buffer-instruction policies of gather's two sides, nontemporal or cached.
+template <bool NT> constexpr int kGatherPoolPol = NT ? KVX_GATHER_POOL_POL : 0;
+template <bool NT> constexpr int kGatherChunkPol = NT ? KVX_GATHER_CHUNK_POL : 0;
 
 template <int POL>
 struct BufSide {
@@ -188,11 +190,12 @@ __device__ __forceinline__ void copy_loop(const S &src, const D &dst, uint32_t n
 // stores carry nt + sc1: measured on MI355X, sequential stores with that policy
 // raise gather by 2-4 % over plain nontemporal stores (the scattered stores of
 // scatter show no such gain, so scatter keeps plain nontemporal accesses).
+template <bool NT>
 __device__ __forceinline__ void gather_tile(const uint8_t *pool, uint8_t *chunk, uint32_t nvec,
                                             uint32_t lane)
 {
-    copy_loop<KVX_GATHER_UNROLL>(BufSide<KVX_GATHER_POOL_POL>(pool, nvec * 16u),
-                                 BufSide<KVX_GATHER_CHUNK_POL>(chunk, nvec * 16u), nvec, lane,
+    copy_loop<KVX_GATHER_UNROLL>(BufSide<kGatherPoolPol<NT>>(pool, nvec * 16u),
+                                 BufSide<kGatherChunkPol<NT>>(chunk, nvec * 16u), nvec, lane,
                                  KVX_GATHER_PIPELINE);
 }
 
@@ -200,45 +203,40 @@ __device__ __forceinline__ void gather_tile(const uint8_t *pool, uint8_t *chunk,
 // restrict-qualified pointers let the compiler interleave a group's stores with the
 // next loads (62 VGPRs, eight waves per SIMD), which measured faster than issuing
 // all sixteen loads first.
+template <bool NT>
 __device__ __forceinline__ void scatter_tile(const gvec *__restrict__ chunk, gvec *__restrict__ pool,
                                              uint32_t nvec, uint32_t lane)
 {
-    copy_loop<KVX_SCATTER_UNROLL>(PtrSide{(gvec *)chunk}, PtrSide{pool}, nvec, lane,
+    copy_loop<KVX_SCATTER_UNROLL>(PtrSide<NT>{(gvec *)chunk}, PtrSide<NT>{pool}, nvec, lane,
                                   KVX_SCATTER_PIPELINE);
 }
 
 // The permuted (pool) side of a head-major tile touches each cache line of the block
 // from several wave instructions (one per token whose head row shares the line), so
 // whether those accesses bypass the caches is a separate choice.
+template <bool NT>
 __device__ __forceinline__ u32x4 ld_hm_pool(const gvec *p)
 {
-#if KVX_HM_POOL_NT
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
+    return ld<NT && KVX_HM_POOL_NT>(p);
 }
 
+template <bool NT>
 __device__ __forceinline__ void st_hm_pool(gvec *p, u32x4 v)
 {
-#if KVX_HM_POOL_NT
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+    st<NT && KVX_HM_POOL_NT>(p, v);
 }
 
 // Head-major pool block against a token-major chunk tile: vectors [first, end) of
 // the tile in token-major order.  The chunk side is contiguous; on the pool side each
 // lane follows a cursor to its vector's place in the block's [H][bs][r16] order, so a
 // wave's 1 KiB touches whole D*E-byte head rows.
-template <int DIR, int U>
+template <int DIR, int U, bool NT>
 __device__ __forceinline__ void copy_head_major(gvec *__restrict__ block, uint8_t *chunk_tile,
                                                 uint32_t first, uint32_t end, uint32_t lane,
                                                 const Launch &a)
 {
-    const BufSide<KVX_GATHER_CHUNK_POL> out(chunk_tile, end * 16u);
-    const PtrSide in{as_global(chunk_tile)};
+    const BufSide<kGatherChunkPol<NT>> out(chunk_tile, end * 16u);
+    const PtrSide<NT> in{as_global(chunk_tile)};
     HmCursor c;
     c.init(first + lane, a);
     for (uint32_t v = first + lane; v < end; v += 64u * U) {
@@ -252,17 +250,17 @@ __device__ __forceinline__ void copy_head_major(gvec *__restrict__ block, uint8_
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (v + 64u * u < end)
-                r[u] = DIR == KV_GATHER ? ld_hm_pool(block + pv[u]) : in.load(v + 64u * u);
+                r[u] = DIR == KV_GATHER ? ld_hm_pool<NT>(block + pv[u]) : in.load(v + 64u * u);
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (v + 64u * u < end) {
                 if (DIR == KV_GATHER) out.store(v + 64u * u, r[u]);
-                else st_hm_pool(block + pv[u], r[u]);
+                else st_hm_pool<NT>(block + pv[u], r[u]);
             }
     }
 }
 
-template <int DIR, int LAYOUT, int PAGE>
+template <int DIR, int LAYOUT, int PAGE, bool NT>
 __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -292,23 +290,29 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
         uint8_t *chunk_tile = a.chunk_base + t.chunk_off;
         if (PAGE == KV_PAGE_HEAD_MAJOR) {
-            copy_head_major<DIR, KVX_HM_UNROLL>(as_global(block), chunk_tile, first, first + count,
-                                                lane, a);
+            copy_head_major<DIR, KVX_HM_UNROLL, NT>(as_global(block), chunk_tile, first, first + count,
+                                                    lane, a);
         } else {
             uint8_t *pool = block + first * 16ll;
             uint8_t *chunk = chunk_tile + first * 16ll;
-            if (DIR == KV_GATHER) gather_tile(pool, chunk, count, lane);
-            else scatter_tile(as_global(chunk), as_global(pool), count, lane);
+            if (DIR == KV_GATHER) gather_tile<NT>(pool, chunk, count, lane);
+            else scatter_tile<NT>(as_global(chunk), as_global(pool), count, lane);
         }
     }
+}
+
+template <int DIR, int LAYOUT, int PAGE>
+static const void *pick_policy(const Launch &a)
+{
+    return a.cached ? (const void *)&tile_copy<DIR, LAYOUT, PAGE, false>
+                    : (const void *)&tile_copy<DIR, LAYOUT, PAGE, true>;
 }
 
 template <int DIR, int LAYOUT>
 static const void *pick_page(const Launch &a)
 {
-    return a.page_layout == KV_PAGE_HEAD_MAJOR
-               ? (const void *)&tile_copy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>
-               : (const void *)&tile_copy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>;
+    return a.page_layout == KV_PAGE_HEAD_MAJOR ? pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a)
+                                               : pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
 }
 
 int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t stream)

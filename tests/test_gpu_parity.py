@@ -255,6 +255,18 @@ def test_strided_dma_matches_oracle(seed):
                  ring=bool(seed % 2), flags=K.KV_FLAG_DMA_STRIDED)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_cached_policy_matches_oracle(seed):
+    """KV_FLAG_CACHED (plain cached loads and stores) moves the same bytes: both page
+    layouts, HBM and pinned-host staging."""
+    pool, spans, chunks = cases.make_case(np.random.default_rng(74_000 + seed), tok_multiple=16,
+                                          medium=bool(seed % 2), max_bytes=24 << 20, head_major=None)
+    regions, staging = _random(pool, chunks, seed)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "cached-%d" % seed, ring=seed % 4 == 3,
+                 flags=K.KV_FLAG_CACHED)
+
+
 def test_per_tile_dma_rejects_bad_ids_before_copying():
     pool = dict(num_layers=1, num_kv=1, num_heads=1, head_dim=64, elem_bytes=2, block_size=16,
                 num_blocks=8, block_stride=2048)
