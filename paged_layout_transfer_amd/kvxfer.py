@@ -263,13 +263,15 @@ def kv_scatter_chunks(pool: int, spans, spec: kv_chunk_spec, stream=None) -> Non
 
 
 def kv_gather_chunks_dma(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
-    """Per-tile hipMemcpyAsync gather; the spans' block tables are host arrays."""
+    """Copy-engine gather (one hipMemcpyAsync per tile, or one strided copy per chunk page
+    with KV_FLAG_DMA_STRIDED); the spans' block tables are host arrays."""
     _check(_lib.kv_gather_chunks_dma(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
            "kv_gather_chunks_dma")
 
 
 def kv_scatter_chunks_dma(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
-    """Per-tile hipMemcpyAsync scatter; the spans' block tables are host arrays."""
+    """Copy-engine scatter (one hipMemcpyAsync per tile, or one strided copy per chunk page
+    with KV_FLAG_DMA_STRIDED); the spans' block tables are host arrays."""
     _check(_lib.kv_scatter_chunks_dma(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
            "kv_scatter_chunks_dma")
 
