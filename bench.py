@@ -192,9 +192,12 @@ def hbm_leg(args, dev):
     for name, which in (("gather", ("g",)), ("scatter", ("s",))):
         K.kv_pool_timing_start(P.h)
         step(max(3, args.steps // 2), which)
-        ms, n = K.kv_pool_timing_read(P.h)
+        each = K.kv_pool_timing_read_each(P.h)
+        ms, n = float(each.sum()), each.size
         per_dir[name] = dict(kernel_ms=ms / n, gbs=payload / (ms / n * 1e-3) / 1e9,
-                             hbm_frac=2 * payload / (ms / n * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                             hbm_frac=2 * payload / (ms / n * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             kernel_ms_median=float(np.median(each)), kernel_ms_min=float(each.min()),
+                             kernel_ms_max=float(each.max()), launches=n)
 
     # the conventional engine on the same call: one hipMemcpyAsync per tile
     dma = {}

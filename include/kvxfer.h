@@ -267,9 +267,13 @@ KV_API int kv_pool_get_error(kv_pool *pool, hipStream_t stream, int32_t *out_bit
 /* Kernel timing.  After kv_pool_timing_start, every transfer records a HIP
  * event pair around its kernel launch on its stream (up to 4096 launches).
  * kv_pool_timing_read synchronizes those events, writes the summed kernel time
- * in milliseconds and the number of launches timed, and stops timing. */
+ * in milliseconds and the number of launches timed, and stops timing.
+ * kv_pool_timing_read_each does the same but writes each launch's time, in launch
+ * order, to ms_each[0 .. min(cap, *launches)) (caller-owned; may be null when cap
+ * is 0). */
 KV_API int kv_pool_timing_start(kv_pool *pool);
 KV_API int kv_pool_timing_read(kv_pool *pool, double *total_ms, int64_t *launches);
+KV_API int kv_pool_timing_read_each(kv_pool *pool, double *ms_each, int64_t cap, int64_t *launches);
 
 /* ---- pinned-host staging ring ------------------------------------------------ */
 

@@ -743,20 +743,35 @@ int kv_pool_timing_start(kv_pool *p)
     return KV_OK;
 }
 
-int kv_pool_timing_read(kv_pool *p, double *total_ms, int64_t *launches)
+int kv_pool_timing_read_each(kv_pool *p, double *ms_each, int64_t cap, int64_t *launches)
 {
-    if (!p || !total_ms || !launches) return KV_ERR_ARG;
-    double sum = 0.0;
+    if (!p || !launches || cap < 0 || (cap > 0 && !ms_each)) return KV_ERR_ARG;
     for (int i = 0; i < p->n_timed; ++i) {
         if (!HIP_OK(hipEventSynchronize(p->t_ev[2 * i + 1]))) return KV_ERR_HIP;
         float ms = 0.f;
         if (!HIP_OK(hipEventElapsedTime(&ms, p->t_ev[2 * i], p->t_ev[2 * i + 1]))) return KV_ERR_HIP;
-        sum += ms;
+        if (i < cap) ms_each[i] = ms;
     }
-    *total_ms = sum;
     *launches = p->n_timed;
     p->timing = false;
     p->n_timed = 0;
+    return KV_OK;
+}
+
+int kv_pool_timing_read(kv_pool *p, double *total_ms, int64_t *launches)
+{
+    if (!p || !total_ms || !launches) return KV_ERR_ARG;
+    std::vector<double> each;
+    try {
+        each.resize(std::max(1, p->n_timed));
+    } catch (...) {
+        return KV_ERR_OOM;
+    }
+    const int rc = kv_pool_timing_read_each(p, each.data(), (int64_t)each.size(), launches);
+    if (rc) return rc;
+    double sum = 0.0;
+    for (int64_t i = 0; i < *launches; ++i) sum += each[i];
+    *total_ms = sum;
     return KV_OK;
 }
 

@@ -115,6 +115,7 @@ _sig("kv_scatter_chunks_dma", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, c
 _sig("kv_pool_get_error", ctypes.c_int, _P, _P, ctypes.POINTER(_I32))
 _sig("kv_pool_timing_start", ctypes.c_int, _P)
 _sig("kv_pool_timing_read", ctypes.c_int, _P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64))
+_sig("kv_pool_timing_read_each", ctypes.c_int, _P, _P, _I64, ctypes.POINTER(_I64))
 _sig("kv_ring_create", ctypes.c_int, _I64, _I64, _I32, ctypes.POINTER(_P))
 _sig("kv_ring_slot", ctypes.c_int, _P, _I64, ctypes.POINTER(_P), ctypes.POINTER(_P))
 _sig("kv_ring_destroy", ctypes.c_int, _P)
@@ -130,7 +131,7 @@ EXPORTED = ("kv_pool_create", "kv_pool_destroy", "kv_pool_alloc_blocks", "kv_poo
             "kv_pool_free_count", "kv_check_transfer", "kv_chunk_bytes", "kv_validate_targets",
             "kv_gather_chunks", "kv_scatter_chunks", "kv_gather_chunks_dma", "kv_scatter_chunks_dma",
             "kv_pool_get_error", "kv_pool_timing_start",
-            "kv_pool_timing_read", "kv_ring_create", "kv_ring_slot", "kv_ring_destroy",
+            "kv_pool_timing_read", "kv_pool_timing_read_each", "kv_ring_create", "kv_ring_slot", "kv_ring_destroy",
             "kv_ring_record", "kv_ring_wait", "kv_ring_stream_wait",
             "kv_strerror", "kv_version", "kv_last_hip_error")
 
@@ -294,6 +295,15 @@ def kv_pool_timing_read(pool: int) -> tuple[float, int]:
     n = ctypes.c_int64()
     _check(_lib.kv_pool_timing_read(pool, ctypes.byref(ms), ctypes.byref(n)), "kv_pool_timing_read")
     return ms.value, n.value
+
+
+def kv_pool_timing_read_each(pool: int, cap: int = 4096) -> np.ndarray:
+    """Each timed launch's kernel time in milliseconds, in launch order; stops timing."""
+    out = np.empty(max(1, cap), dtype=np.float64)
+    n = ctypes.c_int64()
+    _check(_lib.kv_pool_timing_read_each(pool, out.ctypes.data, cap, ctypes.byref(n)),
+           "kv_pool_timing_read_each")
+    return out[:min(n.value, cap)].copy()
 
 
 def kv_ring_create(slot_bytes: int, n_slots: int, flags: int = KV_RING_COHERENT) -> int:

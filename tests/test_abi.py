@@ -3,6 +3,7 @@ allocator, ring-slot ownership, table checks.  Every check here runs before the
 library makes any HIP call, so it works in a CPU-only container."""
 from __future__ import annotations
 
+import ctypes
 import json
 import os
 import re
@@ -212,6 +213,21 @@ def test_spans_limit():
     with pytest.raises(K.KvError) as e:
         K.kv_check_transfer(d, too_many, _spec())
     assert e.value.code == K.KV_ERR_ARG
+
+
+def test_timing_read_each_rejects_bad_arguments():
+    """Argument errors are caught before any HIP call (so this runs without a GPU)."""
+    pool = K.kv_pool_create(_desc(N=10))
+    try:
+        n = ctypes.c_int64()
+        assert K._lib.kv_pool_timing_read_each(pool, None, -1, ctypes.byref(n)) == K.KV_ERR_ARG
+        assert K._lib.kv_pool_timing_read_each(pool, None, 4, ctypes.byref(n)) == K.KV_ERR_ARG
+        assert K._lib.kv_pool_timing_read_each(pool, None, 0, None) == K.KV_ERR_ARG
+        assert K._lib.kv_pool_timing_read_each(None, None, 0, ctypes.byref(n)) == K.KV_ERR_ARG
+        # nothing timed yet: no launches, no HIP call
+        assert K._lib.kv_pool_timing_read_each(pool, None, 0, ctypes.byref(n)) == K.KV_OK and n.value == 0
+    finally:
+        K.kv_pool_destroy(pool)
 
 
 # ---- allocator --------------------------------------------------------------------------

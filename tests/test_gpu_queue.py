@@ -71,3 +71,33 @@ def test_deep_queue_of_small_calls():
     exp_pool = np.full_like(regions, W.SENTINEL)
     oracle.scatter(pool, exp_pool, spans, chunks, exp_stg)
     assert np.array_equal(got_pool, exp_pool)
+
+
+def test_timing_reports_each_launch():
+    dev = torch.device("cuda", 0)
+    L, KV, H, D, E, bs, N = 2, 2, 2, 64, 2, 16, 64
+    tok = H * D * E
+    pool_d = torch.zeros((L * KV, N * bs * tok), dtype=torch.uint8, device=dev)
+    stg = torch.zeros(L * KV * 256 * tok, dtype=torch.uint8, device=dev)
+    tab = torch.arange(16, dtype=torch.int32, device=dev)
+    h = K.kv_pool_create(K.make_pool_desc(L, KV, H, D, E, bs, N, bs * tok,
+                                          [pool_d.data_ptr() + i * pool_d.stride(0) for i in range(L * KV)]))
+    spans = K.make_spans([(tab, 16, 0, 256, 0)])
+    spec = K.make_chunk_spec(K.KV_LAYER_FIRST, L, 256, 0, L, stg, stg.numel(), 1)
+    stream = torch.cuda.current_stream()
+    try:
+        print("[timing] 3 gathers, per-launch read; 2 scatters, summed read", flush=True)
+        K.kv_pool_timing_start(h)
+        for _ in range(3):
+            K.kv_gather_chunks(h, spans, spec, stream)
+        each = K.kv_pool_timing_read_each(h)
+        assert each.size == 3 and np.all(each > 0)
+        K.kv_pool_timing_start(h)
+        for _ in range(2):
+            K.kv_scatter_chunks(h, spans, spec, stream)
+        total, n = K.kv_pool_timing_read(h)
+        assert n == 2 and total > 0
+        assert K.kv_pool_get_error(h, stream) == 0
+    finally:
+        torch.cuda.synchronize()
+        K.kv_pool_destroy(h)
