@@ -310,7 +310,9 @@ KV_API int kv_ring_stream_wait(kv_ring *ring, int64_t first, int64_t count, hipS
 /* Static description of a KV_* return code. */
 KV_API const char *kv_strerror(int code);
 
-/* Library version: major*10000 + minor*100 + patch. */
+/* Library version: major*10000 + minor*100 + patch (KV_VERSION of the header the
+ * library was built with). */
+#define KV_VERSION 200
 KV_API int kv_version(void);
 
 /* The hipError_t of the last HIP runtime call that failed inside the library on

@@ -32,6 +32,7 @@ KV_DEVERR_BLOCK_RANGE = 0x1
 KV_RING_COHERENT = 0x0
 KV_RING_NONCOHERENT = 0x1
 KV_MAX_SPANS = 4096
+KV_VERSION = 200
 
 
 class kv_pool_desc(ctypes.Structure):

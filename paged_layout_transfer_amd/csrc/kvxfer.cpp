@@ -880,7 +880,7 @@ const char *kv_strerror(int code)
     }
 }
 
-int kv_version(void) { return 100; }
+int kv_version(void) { return KV_VERSION; }
 
 int kv_last_hip_error(const char **where)
 {
