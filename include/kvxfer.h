@@ -170,7 +170,9 @@ typedef struct {
     int32_t max_workgroups;/* 0 = library default grid: the whole chip when base is device
                               memory, 16 workgroups of 256 threads when it is host memory
                               (a host-link-bound copy needs few: Strata guide,
-                              "Non-Intrusive Resource Sizing"); > 0 caps the grid */
+                              "Non-Intrusive Resource Sizing"); the kind of memory is
+                              looked up with hipPointerGetAttributes and remembered for
+                              the last base the pool saw.  > 0 caps the grid */
     int32_t flags;         /* KV_FLAG_* */
 } kv_chunk_spec;
 
@@ -191,8 +193,9 @@ typedef struct {
  * (a base or block_stride not 16-byte aligned), KV_ERR_OOM. */
 KV_API int kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 
-/* Frees the handle and its device state (after synchronizing the device work it
- * issued).  The caller's regions are untouched.  NULL is accepted. */
+/* Frees the handle and its device state, after waiting for the transfers it
+ * queued that are still in flight (their fence events; other device work is not
+ * waited for).  The caller's regions are untouched.  NULL is accepted. */
 KV_API int kv_pool_destroy(kv_pool *pool);
 
 /* Block allocator (host free list, preallocated at create time, no allocation on

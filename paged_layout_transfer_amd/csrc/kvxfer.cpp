@@ -369,7 +369,12 @@ fail:
 
 void device_teardown(kv_pool *p)
 {
-    if (p->device >= 0) (void)hipDeviceSynchronize();
+    // Every launch that reads the pool's device state (region table, error word,
+    // span records) is fenced by its arena event, so waiting for the calls still in
+    // flight is enough; other work on the device is left alone.
+    if (p->device >= 0)
+        for (int k = 0; k < p->arena.count; ++k)
+            (void)hipEventSynchronize(p->fl_ev[(p->arena.first + k) % kInflight]);
     free_device_state(p);
     for (hipEvent_t &e : p->t_ev)
         if (e) (void)hipEventDestroy(e), e = nullptr;
