@@ -58,6 +58,21 @@ def test_small_random_cases(seed):
         _compare(d, pool, spans, chunks, regions, staging, "small-%d" % seed)
 
 
+def test_many_random_cases_with_random_options():
+    """200 more small random cases in one test, each with a random choice of page layout,
+    staging (HBM or pinned ring), cache policy and grid cap."""
+    for seed in range(200):
+        rng = np.random.default_rng(60_000 + seed)
+        pool, spans, chunks = cases.make_case(rng, tok_multiple=16, head_major=None)
+        regions, staging = _random(pool, chunks, seed)
+        flags = K.KV_FLAG_CACHED if rng.random() < 0.3 else 0
+        ring = bool(rng.random() < 0.25)
+        wg = int(rng.choice([0, 0, 1, 3, 7]))
+        for d in DIRS:
+            _compare(d, pool, spans, chunks, regions, staging, "many-%d" % seed, ring=ring, flags=flags,
+                     max_workgroups=wg)
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_medium_random_cases(seed):
     pool, spans, chunks = cases.make_case(np.random.default_rng(20_000 + seed), tok_multiple=16,
