@@ -787,8 +787,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": describe(args.workload, w),
-            "global_batch": len(w["requests"]), "seq_len": max(t1 - t0 for t0, t1 in w["requests"]),
-            "parallelism": "none",
+            "requests": len(w["requests"]), "max_request_tokens": max(t1 - t0 for t0, t1 in w["requests"]),
+            "gpus": 1,
             "payload_bytes_each_way": res["payload"], "tiles_per_launch": res["tiles"],
             "chunks": res["chunks"],
         },
