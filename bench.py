@@ -590,7 +590,9 @@ def pipeline_leg(args, dev):
     128 bf16, 16-token pages) cached in pinned host memory is reloaded one layer per
     call on a transfer stream; the compute stream waits for layer l's event and runs
     that layer's prefill MLP GEMMs for a chunk of new tokens.  Compared with reload
-    then compute on one stream."""
+    then compute on one stream.  The offload direction is measured the same way
+    (the Tutti summary's layer-granular store; the lifecycle figure's step 6): layer
+    l is gathered into the host ring as soon as layer l's compute has finished."""
     import numpy as np
     import torch
     from paged_layout_transfer_amd import kvxfer as K
@@ -665,7 +667,7 @@ def pipeline_leg(args, dev):
                     for _ in range(L):
                         layer_compute()
                 e1.record(compute)
-            else:  # pipelined: layer l's compute waits for layer l's reload
+            elif mode == "pipelined":  # layer l's compute waits for layer l's reload
                 e0.record(transfer)
                 compute.wait_event(e0)
                 for l in range(L):
@@ -676,10 +678,34 @@ def pipeline_leg(args, dev):
                         compute.wait_event(ev)
                         layer_compute()
                 e1.record(compute)
+            elif mode == "offload":
+                e0.record(transfer)
+                for l in range(L):
+                    K.kv_gather_chunks(P.h, spans, spec_layer(l), transfer)
+                e1.record(transfer)
+            elif mode == "offload_serial":
+                e0.record(compute)
+                with torch.cuda.stream(compute):
+                    for _ in range(L):
+                        layer_compute()
+                for l in range(L):
+                    K.kv_gather_chunks(P.h, spans, spec_layer(l), compute)
+                e1.record(compute)
+            else:  # offload_pipelined: layer l is offloaded as soon as its compute is done
+                e0.record(compute)
+                transfer.wait_event(e0)
+                for l in range(L):
+                    with torch.cuda.stream(compute):
+                        layer_compute()
+                    ev = torch.cuda.Event()
+                    ev.record(compute)
+                    transfer.wait_event(ev)
+                    K.kv_gather_chunks(P.h, spans, spec_layer(l), transfer)
+                e1.record(transfer)
             torch.cuda.synchronize()
             return e0.elapsed_time(e1)
 
-        modes = ("transfer", "compute", "serial", "pipelined")
+        modes = ("transfer", "compute", "serial", "pipelined", "offload", "offload_serial", "offload_pipelined")
         res = {}
         for tag, (c_s, t_s) in (("shared", shared_streams), ("partitioned", (cmp, io))):
             compute, transfer = c_s, t_s
@@ -689,6 +715,8 @@ def pipeline_leg(args, dev):
             r = res[tag]
             r["overlap_of_shorter"] = round((r["transfer"] + r["compute"] - r["pipelined"]) /
                                             min(r["transfer"], r["compute"]), 3)
+            r["offload_overlap_of_shorter"] = round((r["offload"] + r["compute"] - r["offload_pipelined"]) /
+                                                    min(r["offload"], r["compute"]), 3)
         assert K.kv_pool_get_error(P.h, transfer) == 0
         res["speedup_vs_serial_on_whole_chip"] = round(res["shared"]["serial"] / min(
             res["shared"]["pipelined"], res["partitioned"]["pipelined"]), 3)
