@@ -722,7 +722,8 @@ def pipeline_leg(args, dev):
             res["shared"]["pipelined"], res["partitioned"]["pipelined"]), 3)
         res.update(
             workload="70B-shaped context of %d cached tokens (%.2f GB) reloaded layer by layer from pinned "
-                     "host memory; per layer, %d new tokens through a %dx%d up/gate and %dx%d down GEMM" % (
+                     "host memory (and offloaded layer by layer to it); per layer, %d new tokens through a "
+                     "%dx%d up/gate and %dx%d down GEMM" % (
                          T, L * slot / 1e9, new_tok, hidden, 2 * ffn, ffn, hidden),
             reload_gbs=round(L * slot / (res["shared"]["transfer"] * 1e-3) / 1e9, 2),
             partition="transfer stream on CUs 0-7, compute stream on the other %d" % (n_cu - 8))
