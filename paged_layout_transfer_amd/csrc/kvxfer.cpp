@@ -462,7 +462,8 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     a.err = p->d_err;
 
     a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
-    uint32_t grid = kvx::default_grid(info.tiles << a.split_shift);
+    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
+    uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
     else if (staging_in_host_memory(p, spec->base)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
 

@@ -260,7 +260,7 @@ __device__ __forceinline__ void copy_head_major(gvec *__restrict__ block, uint8_
     }
 }
 
-template <int DIR, int LAYOUT, int PAGE, bool NT>
+template <int DIR, int LAYOUT, int PAGE, bool NT, bool SEG>
 __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -268,6 +268,35 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
     const KVX_CONST SpanDev *spans = as_const(a.spans);
     uint32_t s = 0;
+
+    if (SEG) {  // only instantiated for gather of token-major pages
+        // Work item = one segment of the tiles laid end to end: the pieces of the (at
+        // most a few) tiles it overlaps, copied in order.
+        const int64_t T = a.tile_bytes;
+        const int64_t total = a.total_tiles * T;
+        const int64_t n_seg = work_items(a);
+        for (int64_t seg = (int64_t)blockIdx.x * kWavesPerBlock + wave; seg < n_seg; seg += step) {
+            const int64_t x0 = seg * a.seg_bytes;
+            const int64_t x1 = x0 + a.seg_bytes < total ? x0 + a.seg_bytes : total;
+            for (int64_t tile = x0 / T; tile * T < x1; ++tile) {
+                s = find_span(spans, s, a.n_spans, tile);
+                const SpanDev sp = load_span(spans + s);
+                const TileRef t = resolve_tile<LAYOUT>(a, sp, tile);
+                int64_t lo, hi;
+                segment_piece(tile, T, t.nbytes, x0, x1, &lo, &hi);
+                if (hi <= lo) continue;
+                const int32_t blk = as_const(sp.table)[t.page];
+                if ((uint32_t)blk >= a.num_blocks) {
+                    if (lane == 0) atomicOr(a.err, KV_DEVERR_BLOCK_RANGE);
+                    continue;
+                }
+                const uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
+                gather_tile<NT>(block + lo, a.chunk_base + t.chunk_off + lo, (uint32_t)((hi - lo) >> 4),
+                                lane);
+            }
+        }
+        return;
+    }
 
     // Work item = one of a tile's 2^split_shift parts; the waves of a workgroup take
     // consecutive items, so a split tile is copied by neighbouring waves.
@@ -301,11 +330,20 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     }
 }
 
+// Segment walks are a separate instantiation so that the tile walk keeps its own
+// register allocation.
+template <int DIR, int LAYOUT, int PAGE, bool NT>
+static const void *pick_walk(const Launch &a)
+{
+    if (DIR == KV_GATHER && PAGE == KV_PAGE_TOKEN_MAJOR && a.seg_bytes)
+        return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, DIR == KV_GATHER && PAGE == KV_PAGE_TOKEN_MAJOR>;
+    return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, false>;
+}
+
 template <int DIR, int LAYOUT, int PAGE>
 static const void *pick_policy(const Launch &a)
 {
-    return a.cached ? (const void *)&tile_copy<DIR, LAYOUT, PAGE, false>
-                    : (const void *)&tile_copy<DIR, LAYOUT, PAGE, true>;
+    return a.cached ? pick_walk<DIR, LAYOUT, PAGE, false>(a) : pick_walk<DIR, LAYOUT, PAGE, true>(a);
 }
 
 template <int DIR, int LAYOUT>

@@ -7,6 +7,7 @@
 // checked against the buffers it must stay in before anything is copied, and
 // every tile must be visited exactly once.  With copy != 0 the tile bytes are
 // moved with memcpy so the result can be compared with the oracle.
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -36,10 +37,76 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
         if (spans[i].t_end > spans[i].t_begin) tlen.push_back(spans[i].table_len);
 
     a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
-    uint32_t grid = kvx::default_grid(info.tiles << a.split_shift);
+    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
+    uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
         grid = (uint32_t)spec->max_workgroups;
     *grid_out = grid;
+    const int64_t nreg_s = (int64_t)d->num_layers * d->num_kv;
+    if (direction == KV_GATHER && a.page_layout == KV_PAGE_TOKEN_MAJOR && a.seg_bytes) {
+        // the kernel's segment walk: the pieces of every tile must cover it exactly once
+        const int64_t T = a.tile_bytes, total = info.tiles * T, n_seg = kvx::work_items(a);
+        struct Piece { int64_t tile, lo, hi; };
+        std::vector<Piece> pieces;
+        std::vector<uint8_t> seg_seen((size_t)n_seg, 0);
+        const int64_t step_s = (int64_t)grid * kvx::kWavesPerBlock;
+        for (uint32_t b = 0; b < grid; ++b)
+            for (int w = 0; w < kvx::kWavesPerBlock; ++w) {
+                uint32_t s = 0;
+                for (int64_t seg = (int64_t)b * kvx::kWavesPerBlock + w; seg < n_seg; seg += step_s) {
+                    if (seg_seen[seg]++) ++*violations;
+                    const int64_t x0 = seg * a.seg_bytes;
+                    const int64_t x1 = x0 + a.seg_bytes < total ? x0 + a.seg_bytes : total;
+                    for (int64_t tile = x0 / T; tile * T < x1; ++tile) {
+                        if (tile >= info.tiles) { ++*violations; break; }
+                        s = kvx::find_span(records, s, n_rec, tile);
+                        const kvx::SpanDev &sp = records[s];
+                        const kvx::TileRef t = a.layout == KV_LAYER_FIRST
+                                                   ? kvx::resolve_tile<KV_LAYER_FIRST>(a, sp, tile)
+                                                   : kvx::resolve_tile<KV_PAGE_FIRST>(a, sp, tile);
+                        int64_t lo, hi;
+                        kvx::segment_piece(tile, T, t.nbytes, x0, x1, &lo, &hi);
+                        if (hi <= lo) continue;
+                        if (lo < 0 || lo % 16 || hi % 16 || hi > (int64_t)t.nbytes) { ++*violations; continue; }
+                        pieces.push_back({tile, lo, hi});
+                        if ((int64_t)t.page >= tlen[s] || (int64_t)t.region >= nreg_s || t.chunk_off < 0 ||
+                            t.chunk_off + hi > staging_bytes) {
+                            ++*violations;
+                            continue;
+                        }
+                        const int32_t blk = sp.table[t.page];
+                        if (blk < 0 || (uint32_t)blk >= a.num_blocks) continue;  // skipped, as the kernel does
+                        const int64_t poff = (int64_t)blk * a.block_stride;
+                        if (poff + hi > region_bytes[t.region]) { ++*violations; continue; }
+                        if (!copy) continue;
+                        uint8_t *pool = static_cast<uint8_t *>(d->bases[t.region]) + poff + lo;
+                        std::memcpy(a.chunk_base + t.chunk_off + lo, pool, (size_t)(hi - lo));
+                    }
+                }
+            }
+        for (int64_t i = 0; i < n_seg; ++i)
+            if (seg_seen[i] != 1) ++*violations;
+        // a tile whose block id the kernel skips is still walked, so coverage is complete:
+        // sorted by (tile, lo), each tile's pieces must run back to back from 0 to nbytes
+        std::sort(pieces.begin(), pieces.end(), [](const Piece &x, const Piece &y) {
+            return x.tile != y.tile ? x.tile < y.tile : x.lo < y.lo;
+        });
+        size_t k = 0;
+        for (int64_t i = 0; i < info.tiles; ++i) {
+            uint32_t s = kvx::find_span(records, 0, n_rec, i);
+            const kvx::TileRef t = a.layout == KV_LAYER_FIRST
+                                       ? kvx::resolve_tile<KV_LAYER_FIRST>(a, records[s], i)
+                                       : kvx::resolve_tile<KV_PAGE_FIRST>(a, records[s], i);
+            int64_t at = 0;
+            for (; k < pieces.size() && pieces[k].tile == i; ++k) {
+                if (pieces[k].lo != at) ++*violations;
+                at = pieces[k].hi;
+            }
+            if (at != (int64_t)t.nbytes) ++*violations;
+        }
+        if (k != pieces.size()) ++*violations;
+        return KV_OK;
+    }
     const uint32_t split = 1u << a.split_shift;
     const int64_t items = info.tiles * split;
     std::vector<uint8_t> seen((size_t)items, 0);
