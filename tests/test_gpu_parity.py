@@ -193,10 +193,12 @@ def test_interleaved_kv_pool():
             _compare(d, pool, spans, chunks, flat, staging, "interleaved-%d" % layout, views=views)
 
 
-def test_bad_block_id_is_skipped_and_reported():
+@pytest.mark.parametrize("H,D,bs", [(1, 64, 16), (2, 288, 16)])
+def test_bad_block_id_is_skipped_and_reported(H, D, bs):
     """A table entry past the pool: that page's tiles are skipped, the sticky error bit is
-    set, and every other tile still moves (page-first, one chunk per page)."""
-    L, KV, H, D, E, bs, N = 2, 2, 1, 64, 2, 16, 32
+    set, and every other tile still moves (page-first, one chunk per page).  The second
+    shape has 18 KiB tiles, so the gather takes the segment walk."""
+    L, KV, E, N = 2, 2, 2, 32
     tok = H * D * E
     pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
                 num_blocks=N, block_stride=bs * tok)
