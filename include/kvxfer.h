@@ -187,10 +187,11 @@ typedef struct {
 /* ---- pool ------------------------------------------------------------------ */
 
 /* Validates desc and creates a pool handle with a host free list of all
- * num_blocks ids.  Device-side state (a descriptor buffer, an error word) is
- * created on the first transfer, on the device current then; later transfers
- * must run with the same device current.  Errors: KV_ERR_ARG, KV_ERR_ALIGN
- * (a base or block_stride not 16-byte aligned), KV_ERR_OOM. */
+ * num_blocks ids (5 bytes of host memory per block).  Device-side state (a region
+ * table, an error word, a 4 MiB span-record arena with its pinned mirror and 256
+ * events) is created on the first transfer, on the device current then; later
+ * transfers must run with the same device current.  Errors: KV_ERR_ARG,
+ * KV_ERR_ALIGN (a base or block_stride not 16-byte aligned), KV_ERR_OOM. */
 KV_API int kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 
 /* Frees the handle and its device state, after waiting for the transfers it
