@@ -186,8 +186,8 @@ typedef struct {
 
 /* ---- pool ------------------------------------------------------------------ */
 
-/* Validates desc and creates a pool handle with a host free list of all
- * num_blocks ids (5 bytes of host memory per block).  Device-side state (a region
+/* Validates desc and creates a pool handle with a host bitmap of free blocks (one
+ * bit per block, all free).  Device-side state (a region
  * table, an error word, a 4 MiB span-record arena with its pinned mirror and 256
  * events) is created on the first transfer, on the device current then; later
  * transfers must run with the same device current.  Errors: KV_ERR_ARG,
@@ -199,11 +199,13 @@ KV_API int kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
  * waited for).  The caller's regions are untouched.  NULL is accepted. */
 KV_API int kv_pool_destroy(kv_pool *pool);
 
-/* Block allocator (host free list, preallocated at create time, no allocation on
- * the call path: Tutti summary, "Key implementation details", item 1).
- * alloc: writes n distinct free ids to out_ids, or fails with KV_ERR_OOM and
- * allocates nothing.  free: ids must be currently allocated and distinct, else
- * KV_ERR_RANGE and nothing is freed. */
+/* Block allocator (a host bitmap of free blocks, preallocated at create time, no
+ * allocation on the call path: Tutti summary, "Key implementation details", item 1).
+ * alloc: writes the n lowest free ids to out_ids in ascending order (so a request's
+ * pages lie as close together as the pool's fragmentation allows, which makes
+ * reloading them faster), or fails with KV_ERR_OOM and allocates nothing.
+ * free: ids must be currently allocated and distinct, else KV_ERR_RANGE and
+ * nothing is freed. */
 KV_API int kv_pool_alloc_blocks(kv_pool *pool, int32_t n, int32_t *out_ids);
 KV_API int kv_pool_free_blocks(kv_pool *pool, int32_t n, const int32_t *ids);
 KV_API int kv_pool_free_count(const kv_pool *pool, int64_t *out);

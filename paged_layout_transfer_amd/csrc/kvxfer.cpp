@@ -266,9 +266,8 @@ int prepare_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
 struct kv_pool {
     kv_pool_desc desc;
     std::vector<void *> bases;
-    // allocator: LIFO stack of free ids plus an allocated bitmap
-    std::vector<int32_t> free_ids;
-    std::vector<uint8_t> allocated;
+    // allocator: free-block bitmap, lowest ids first
+    kvx::BlockBitmap blocks;
     // validation scratch (no allocation on the call path)
     std::vector<SpanPlan> plans;
     std::vector<SlotRange> ranges;
@@ -575,11 +574,7 @@ int kv_pool_create(const kv_pool_desc *desc, kv_pool **out)
         p->desc = *desc;
         p->bases.assign(desc->bases, desc->bases + n);
         p->desc.bases = p->bases.data();
-        p->free_ids.resize(desc->num_blocks);
-        // LIFO: ids come out in increasing order from a fresh pool
-        for (int64_t i = 0; i < desc->num_blocks; ++i)
-            p->free_ids[i] = (int32_t)(desc->num_blocks - 1 - i);
-        p->allocated.assign(desc->num_blocks, 0);
+        p->blocks.init(desc->num_blocks);
         p->plans.resize(KV_MAX_SPANS);
         p->ranges.resize(KV_MAX_SPANS);
     } catch (...) {
@@ -601,35 +596,19 @@ int kv_pool_destroy(kv_pool *pool)
 int kv_pool_alloc_blocks(kv_pool *p, int32_t n, int32_t *out_ids)
 {
     if (!p || n < 0 || (n > 0 && !out_ids)) return KV_ERR_ARG;
-    if ((size_t)n > p->free_ids.size()) return KV_ERR_OOM;
-    for (int32_t i = 0; i < n; ++i) {
-        const int32_t id = p->free_ids.back();
-        p->free_ids.pop_back();
-        p->allocated[id] = 1;
-        out_ids[i] = id;
-    }
-    return KV_OK;
+    return p->blocks.alloc(n, out_ids);
 }
 
 int kv_pool_free_blocks(kv_pool *p, int32_t n, const int32_t *ids)
 {
     if (!p || n < 0 || (n > 0 && !ids)) return KV_ERR_ARG;
-    // check everything first so a bad call frees nothing
-    for (int32_t i = 0; i < n; ++i) {
-        if (ids[i] < 0 || ids[i] >= p->desc.num_blocks || !p->allocated[ids[i]]) {
-            for (int32_t j = 0; j < i; ++j) p->allocated[ids[j]] = 1;
-            return KV_ERR_RANGE;
-        }
-        p->allocated[ids[i]] = 0;  // provisional mark, catches duplicates within the call
-    }
-    for (int32_t i = 0; i < n; ++i) p->free_ids.push_back(ids[i]);
-    return KV_OK;
+    return p->blocks.release(n, ids);
 }
 
 int kv_pool_free_count(const kv_pool *p, int64_t *out)
 {
     if (!p || !out) return KV_ERR_ARG;
-    *out = (int64_t)p->free_ids.size();
+    *out = p->blocks.n_free;
     return KV_OK;
 }
 

@@ -5,9 +5,71 @@
 #pragma once
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "kvxfer_internal.h"
 
 namespace kvx {
+
+// ---- block allocator (host) --------------------------------------------------
+
+// The free blocks of a pool as a bitmap (bit b of word w: block 64w+b is free).
+// Allocation hands out the lowest free ids first, in ascending order, so a request's
+// pages sit as close together in each region as the pool's fragmentation allows:
+// reloading into nearby pages writes faster than into scattered ones.  Freeing
+// checks every id (in range, allocated, not repeated) before freeing any.
+struct BlockBitmap {
+    std::vector<uint64_t> free_bits;
+    int64_t n_blocks = 0, n_free = 0;
+    int64_t low_word = 0;  // no free block in the words below this one
+
+    void init(int64_t n)
+    {
+        n_blocks = n;
+        n_free = n;
+        low_word = 0;
+        free_bits.assign((size_t)((n + 63) / 64), ~0ull);
+        if (n % 64) free_bits.back() = (1ull << (n % 64)) - 1;
+    }
+    bool is_free(int64_t id) const { return (free_bits[(size_t)(id >> 6)] >> (id & 63)) & 1u; }
+
+    int alloc(int32_t n, int32_t *out)
+    {
+        if (n > n_free) return KV_ERR_OOM;
+        int32_t got = 0;
+        int64_t w = low_word;
+        while (got < n) {
+            uint64_t bits = free_bits[(size_t)w];
+            while (bits && got < n) {
+                const int b = __builtin_ctzll(bits);
+                bits &= bits - 1;
+                out[got++] = (int32_t)(w * 64 + b);
+            }
+            free_bits[(size_t)w] = bits;
+            if (bits) break;
+            ++w;
+        }
+        low_word = w;
+        n_free -= n;
+        return KV_OK;
+    }
+
+    int release(int32_t n, const int32_t *ids)
+    {
+        for (int32_t i = 0; i < n; ++i) {
+            const int64_t id = ids[i];
+            if (id < 0 || id >= n_blocks || is_free(id)) {  // out of range, free, or repeated
+                for (int32_t j = 0; j < i; ++j) free_bits[(size_t)(ids[j] >> 6)] &= ~(1ull << (ids[j] & 63));
+                return KV_ERR_RANGE;
+            }
+            free_bits[(size_t)(id >> 6)] |= 1ull << (id & 63);
+        }
+        for (int32_t i = 0; i < n; ++i) low_word = std::min<int64_t>(low_word, ids[i] >> 6);
+        n_free += n;
+        return KV_OK;
+    }
+};
 
 // ---- span-record arena (host bookkeeping) -----------------------------------
 

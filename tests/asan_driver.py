@@ -5,8 +5,9 @@ the sanitizer runtime; argv[1] is a build of the library's sources plus
 tests/kernel_emu.cpp with host-side instrumentation.  It drives, on small random
 cases, the host preparation and the kernel's tile walk (emu_transfer, copying the
 bytes), the copy-engine plan (emu_dma, per tile and strided), the span-record arena
-bookkeeping (emu_arena) and the host validation's error paths (kv_check_transfer),
-and compares every copied result with the oracle.  Prints "ok" at the end; any
+bookkeeping (emu_arena), the block allocator against a set model, and the host
+validation's error paths (kv_check_transfer), and compares every copied result with
+the oracle.  Prints "ok" at the end; any
 sanitizer report aborts the process.
 """
 from __future__ import annotations
@@ -103,6 +104,39 @@ def error_paths() -> None:
     check(A.KV_ERR_ARG, stride=1024)               # blocks overlap
 
 
+def allocator() -> None:
+    lib.kv_pool_create.argtypes = [ctypes.POINTER(A.kv_pool_desc), ctypes.POINTER(ctypes.c_void_p)]
+    lib.kv_pool_alloc_blocks.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.kv_pool_free_blocks.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.kv_pool_destroy.argtypes = [ctypes.c_void_p]
+    region = np.zeros(16, dtype=np.uint8)
+    for n_blocks in (1, 63, 64, 65, 1000):
+        desc = A.make_pool_desc(1, 1, 1, 8, 2, 1, n_blocks, 16, [region.ctypes.data])
+        h = ctypes.c_void_p()
+        assert lib.kv_pool_create(ctypes.byref(desc), ctypes.byref(h)) == 0
+        rng = np.random.default_rng(43_000 + n_blocks)
+        held = set()
+        for _ in range(300):
+            if held and rng.random() < 0.5:
+                ids = rng.permutation(sorted(held))[:int(rng.integers(1, len(held) + 1))].astype(np.int32)
+                assert lib.kv_pool_free_blocks(h, ids.size, ids.ctypes.data) == 0
+                held -= set(ids.tolist())
+            else:
+                free = sorted(set(range(n_blocks)) - held)
+                k = int(rng.integers(0, len(free) + 2))
+                out = np.full(max(1, k), -1, dtype=np.int32)
+                rc = lib.kv_pool_alloc_blocks(h, k, out.ctypes.data)
+                if k > len(free):
+                    assert rc == A.KV_ERR_OOM
+                else:
+                    assert rc == 0 and out[:k].tolist() == free[:k]
+                    held |= set(out[:k].tolist())
+            # out of range, or one id twice (free or held): rejected, nothing freed
+            bad = np.array([n_blocks, -1] if rng.random() < 0.5 else [0, 0], dtype=np.int32)
+            assert lib.kv_pool_free_blocks(h, 2, bad.ctypes.data) == A.KV_ERR_RANGE
+        assert lib.kv_pool_destroy(h) == 0
+
+
 def arena() -> None:
     rng = np.random.default_rng(42_000)
     for lag in (0, 5, 300):
@@ -115,5 +149,6 @@ if __name__ == "__main__":
     for seed in range(int(os.environ.get("ASAN_CASES", "24"))):
         run_case(seed)
     error_paths()
+    allocator()
     arena()
     print("ok", flush=True)

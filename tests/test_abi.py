@@ -232,6 +232,32 @@ def test_timing_read_each_rejects_bad_arguments():
 
 # ---- allocator --------------------------------------------------------------------------
 
+def test_allocator_hands_out_lowest_free_ids_in_order():
+    """Lowest free ids first, ascending, whatever order they were freed in; across
+    64-bit bitmap words; against a plain set model over a random alloc/free history."""
+    N = 300
+    pool = K.kv_pool_create(_desc(N=N))
+    try:
+        assert K.kv_pool_alloc_blocks(pool, 5).tolist() == [0, 1, 2, 3, 4]
+        rng = np.random.default_rng(5)
+        held = set(range(5))
+        for _ in range(400):
+            if held and rng.random() < 0.5:
+                k = int(rng.integers(1, len(held) + 1))
+                ids = rng.permutation(sorted(held))[:k]
+                K.kv_pool_free_blocks(pool, ids)
+                held -= set(ids.tolist())
+            else:
+                free = sorted(set(range(N)) - held)
+                k = int(rng.integers(0, min(len(free), 70) + 1))
+                got = K.kv_pool_alloc_blocks(pool, k).tolist()
+                assert got == free[:k]
+                held |= set(got)
+            assert K.kv_pool_free_count(pool) == N - len(held)
+    finally:
+        K.kv_pool_destroy(pool)
+
+
 def test_allocator():
     pool = K.kv_pool_create(_desc(N=10))
     try:
