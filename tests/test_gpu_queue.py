@@ -101,3 +101,60 @@ def test_timing_reports_each_launch():
     finally:
         torch.cuda.synchronize()
         K.kv_pool_destroy(h)
+
+
+def test_one_pool_on_two_streams():
+    """One pool handle used from two streams at once: gathers of two halves of a request
+    on stream A and stream B, 60 calls each without synchronisation (they share the
+    pool's span-record arena and error word), then scatters of both halves into a
+    second pool, again split over the two streams.  Every result equals the oracle."""
+    dev = torch.device("cuda", 0)
+    L, KV, H, D, E, bs, N = 2, 2, 2, 64, 2, 16, 256
+    tok = H * D * E
+    pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
+                num_blocks=N, block_stride=bs * tok)
+    rng = np.random.default_rng(91_000)
+    table = rng.permutation(N)[:64].astype(np.int32)           # a 1024-token request
+    regions = rng.integers(0, 256, size=(L * KV, N * bs * tok), dtype=np.uint8)
+    src_d = torch.from_numpy(regions).to(dev)
+    dst_d = torch.full_like(src_d, W.SENTINEL)
+    tab_d = torch.from_numpy(table).to(dev)
+    CT = 256
+    slot = L * KV * CT * tok
+    halves = [(0, 512), (512, 1024)]
+    stg = [torch.full((2 * slot,), W.SENTINEL, dtype=torch.uint8, device=dev) for _ in halves]
+
+    def make(t):
+        return K.kv_pool_create(K.make_pool_desc(L, KV, H, D, E, bs, N, bs * tok,
+                                                 [t.data_ptr() + i * t.stride(0) for i in range(L * KV)]))
+
+    src, dst = make(src_d), make(dst_d)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    spans = [K.make_spans([(tab_d, 64, t0, t1, 0)]) for t0, t1 in halves]
+    specs = [K.make_chunk_spec(K.KV_LAYER_FIRST, L, CT, 0, L, s, slot, 2) for s in stg]
+    try:
+        print("[streams] 2 x 60 gathers on two streams, then scatters on both", flush=True)
+        torch.cuda.synchronize()
+        for _ in range(60):
+            for h in range(2):
+                K.kv_gather_chunks(src, spans[h], specs[h], streams[h])
+        for h in range(2):
+            K.kv_scatter_chunks(dst, spans[h], specs[h], streams[h])
+        torch.cuda.synchronize()
+        assert K.kv_pool_get_error(src, streams[0]) == 0 and K.kv_pool_get_error(dst, streams[1]) == 0
+        got_stg = [s.cpu().numpy() for s in stg]
+        got_pool = dst_d.cpu().numpy()
+    finally:
+        torch.cuda.synchronize()
+        K.kv_pool_destroy(src)
+        K.kv_pool_destroy(dst)
+
+    chunks = dict(layout=0, chunk_layers=L, chunk_tokens=CT, layer_begin=0, layer_end=L, slot_bytes=slot,
+                  n_slots=2)
+    exp_pool = np.full_like(regions, W.SENTINEL)
+    for h, (t0, t1) in enumerate(halves):
+        exp = np.full(2 * slot, W.SENTINEL, dtype=np.uint8)
+        oracle.gather(pool, regions, [(table, t0, t1, 0)], chunks, exp)
+        assert np.array_equal(got_stg[h], exp), "gather half %d" % h
+        oracle.scatter(pool, exp_pool, [(table, t0, t1, 0)], chunks, exp)
+    assert np.array_equal(got_pool, exp_pool)
