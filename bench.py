@@ -21,6 +21,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,9 +40,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 of the kernel sources with comments and blank space removed, so that the
+    recorded counters stay attached to the code they were taken on and not to its
+    comments."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        text = open(os.path.join(ROOT, p), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -1,7 +1,9 @@
 // kvxfer_kernels.hip -- the gather/scatter tile-copy kernel for gfx950.
 //
-// One 64-lane wavefront copies one (layer, kv, page) tile per iteration of a
-// grid-stride loop.  Per tile it
+// One 64-lane wavefront copies one (layer, kv, page) tile -- or one part of a large
+// tile, or, for a gather over tiles whose size is not a power of two, one 32 KiB
+// segment of the tiles laid end to end -- per iteration of a grid-stride loop.  Per
+// tile it
 //   1. finds the span (binary search over the per-span tile prefix, wave-uniform,
 //      so it runs on the scalar unit with scalar loads),
 //   2. splits the local tile index into (layer chunk, token chunk, layer, kv, page)
@@ -10,7 +12,8 @@
 //      (Strata guide, "Two-Dimensional Memory Layout Decoupling"), and
 //   4. copies the tile's n_tok*tok contiguous bytes with 16-byte vector loads and
 //      stores, 64 lanes x 16 B = 1 KiB per wave instruction, 8-16 vectors in flight
-//      per lane, nontemporal on both sides (the Strata guide's reload kernel uses
+//      per lane, nontemporal on both sides unless the call asks for cached accesses
+//      (KV_FLAG_CACHED) (the Strata guide's reload kernel uses
 //      cache-streaming stores so a transfer does not evict the working set of
 //      concurrent compute kernels: "Non-Intrusive Resource Sizing").  Gather goes
 //      through buffer instructions so that its sequential chunk stores can also
