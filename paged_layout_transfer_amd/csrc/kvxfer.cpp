@@ -236,6 +236,7 @@ int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
         a->hm_dq = 64u % r16;
         a->hm_dh = (64u / r16) % H;
         a->hm_dj = (64u / r16) / H;
+        a->hm_t4 = kvx::hm_t4_ok(a->page_layout, r16, H, (uint32_t)d->block_size) ? 1u : 0u;
     }
     if (info) *info = inf;
     return KV_OK;

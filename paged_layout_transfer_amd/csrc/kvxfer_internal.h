@@ -83,6 +83,9 @@ namespace kvx {
 #ifndef KVX_HM_POOL_NT
 #define KVX_HM_POOL_NT 1       // nontemporal accesses on the pool side of head-major tiles
 #endif
+#ifndef KVX_HM_T4_UNITS
+#define KVX_HM_T4_UNITS 8      // 4x4 blocks (4 KiB each) in flight per wave, head-major pages
+#endif
 #ifndef KVX_TAIL_GROUP
 #define KVX_TAIL_GROUP 4       // vectors per lane per group after the full groups
 #endif
@@ -147,7 +150,7 @@ struct Launch {
     uint32_t hm_dq, hm_dh, hm_dj;
     uint32_t cached;       // 1: plain cached loads and stores (KV_FLAG_CACHED), else nontemporal
     uint32_t seg_bytes;    // > 0: gather in segments of this many bytes (gather_seg_bytes)
-    uint32_t pad2_;
+    uint32_t hm_t4;        // 1: head-major pages moved in 4-token x 4-head blocks (hm_t4_ok)
 };
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
@@ -260,6 +263,22 @@ __host__ __device__ constexpr uint32_t split_shift_for(int dir, int64_t tile_byt
     if (part > 0 && tile_bytes >= min_tile)
         while (sh < KVX_MAX_SPLIT_SHIFT && tile_bytes >= (part << (sh + 1))) ++sh;
     return sh;
+}
+
+// Head-major pages whose head rows are 256 bytes (16 vectors, one 16-lane row of a
+// wave) with heads and page tokens in multiples of 4 are moved in blocks of 4 tokens x
+// 4 heads: four 1 KiB accesses on each side, transposed in registers in between.
+__host__ __device__ constexpr bool hm_t4_ok(uint32_t page_layout, uint32_t r16, uint32_t heads,
+                                            uint32_t block_size)
+{
+    return page_layout == KV_PAGE_HEAD_MAJOR && r16 == 16 && heads % 4 == 0 && block_size % 4 == 0;
+}
+
+// Blocks of a head-major tile of n_tok tokens: (token group, head group) pairs,
+// token-group major.
+__host__ __device__ inline uint32_t hm_t4_units(uint32_t n_tok, uint32_t heads)
+{
+    return ((n_tok + 3) / 4) * (heads / 4);
 }
 
 // Segment size for a gather over tiles of tile_bytes (0: one tile per wave item).

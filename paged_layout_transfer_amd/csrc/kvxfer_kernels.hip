@@ -263,6 +263,73 @@ __device__ __forceinline__ void copy_head_major(gvec *__restrict__ block, uint8_
     }
 }
 
+// 4x4 transpose of 16-lane rows across four registers: on return, row r of register
+// t holds what row t of register r held.  gfx950's permlane32 swap exchanges the upper
+// half of one register with the lower half of another, the permlane16 swap the odd
+// 16-lane rows of one with the even rows of the other; two of each per dword.
+__device__ __forceinline__ void transpose_rows4(u32x4 &A, u32x4 &B, u32x4 &C, u32x4 &D)
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const auto ac = __builtin_amdgcn_permlane32_swap(A[c], C[c], false, false);
+        const auto bd = __builtin_amdgcn_permlane32_swap(B[c], D[c], false, false);
+        const auto ab = __builtin_amdgcn_permlane16_swap(ac[0], bd[0], false, false);
+        const auto cd = __builtin_amdgcn_permlane16_swap(ac[1], bd[1], false, false);
+        A[c] = ab[0];
+        B[c] = ab[1];
+        C[c] = cd[0];
+        D[c] = cd[1];
+    }
+}
+
+// Head-major pages with 256-byte head rows (see hm_t4_ok), blocks [u0, u1) of a tile
+// of n_tok tokens; block u = (tokens j0..j0+3, heads hb..hb+3).  On the pool side the
+// 4 tokens of one head are 1 KiB contiguous, lane = token*16 + vector; on the chunk
+// side the 4 heads of one token are, lane = head*16 + vector; so four loads, one
+// register transpose and four stores move a block with every access a whole 1 KiB.
+// Chunk accesses past the tile's n_tok tokens are dropped by the buffer range (gather)
+// or skipped (scatter), and so are pool writes of those tokens.
+template <int DIR, bool NT>
+__device__ __forceinline__ void copy_head_major_t4(const uint8_t *block, uint8_t *chunk_tile, uint32_t u0,
+                                                   uint32_t u1, uint32_t n_tok, uint32_t lane,
+                                                   const Launch &a)
+{
+    constexpr int U = KVX_HM_T4_UNITS;
+    const uint32_t H = a.hm_heads, bs = a.block_size, hgroups = H / 4;
+    const BufSide<kGatherPoolPol<NT>> pool_in(block, H * bs * 256u);
+    const BufSide<kGatherChunkPol<NT>> chunk_out(chunk_tile, n_tok * H * 256u);
+    const PtrSide<NT> chunk_in{(gvec *)chunk_tile};
+    gvec *const pool_out = (gvec *)block;
+    const uint32_t my_tok = lane >> 4;  // this lane's token within a block, pool side
+    for (uint32_t u = u0; u < u1; u += U) {
+        u32x4 x[U][4];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t uu = u + k, j0 = (uu / hgroups) * 4, hb = (uu % hgroups) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (uu >= u1) continue;
+                if (DIR == KV_GATHER) x[k][r] = pool_in.load(((hb + r) * bs + j0) * 16u + lane);
+                else if (j0 + r < n_tok) x[k][r] = chunk_in.load(((j0 + r) * H + hb) * 16u + lane);
+                else x[k][r] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (u + k < u1) transpose_rows4(x[k][0], x[k][1], x[k][2], x[k][3]);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t uu = u + k, j0 = (uu / hgroups) * 4, hb = (uu % hgroups) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (uu >= u1) continue;
+                if (DIR == KV_GATHER) chunk_out.store(((j0 + r) * H + hb) * 16u + lane, x[k][r]);
+                else if (j0 + my_tok < n_tok) st_hm_pool<NT>(pool_out + ((hb + r) * bs + j0) * 16u + lane, x[k][r]);
+            }
+        }
+    }
+}
+
 template <int DIR, int LAYOUT, int PAGE, bool NT, bool SEG>
 __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 {
@@ -318,9 +385,17 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
             continue;
         }
         uint32_t first, count;
-        part_range(t.nbytes >> 4, (uint32_t)(item & ((1 << shift) - 1)), 1u << shift, &first, &count);
         uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
         uint8_t *chunk_tile = a.chunk_base + t.chunk_off;
+        if (PAGE == KV_PAGE_HEAD_MAJOR && a.hm_t4) {
+            // parts of a split tile are ranges of 4x4 blocks
+            const uint32_t n_tok = t.nbytes / a.tok;
+            part_range(hm_t4_units(n_tok, a.hm_heads), (uint32_t)(item & ((1 << shift) - 1)), 1u << shift,
+                       &first, &count);
+            copy_head_major_t4<DIR, NT>(block, chunk_tile, first, first + count, n_tok, lane, a);
+            continue;
+        }
+        part_range(t.nbytes >> 4, (uint32_t)(item & ((1 << shift) - 1)), 1u << shift, &first, &count);
         if (PAGE == KV_PAGE_HEAD_MAJOR) {
             copy_head_major<DIR, KVX_HM_UNROLL, NT>(as_global(block), chunk_tile, first, first + count,
                                                     lane, a);

@@ -14,6 +14,40 @@
 #include "kvxfer_host.h"
 #include "kvxfer_internal.h"
 
+// One wave register of 16-byte values, emulated: each lane holds the index of the
+// vector it was loaded from (-1: zero).  The two gfx950 lane swaps the kernel's
+// 4x4 transpose uses, with the lane layout measured on the device:
+// permlane32_swap(a, b) -> (a lanes 0-31 | b lanes 0-31, a lanes 32-63 | b lanes 32-63);
+// permlane16_swap(a, b) -> (a row0, b row0, a row2, b row2 | a row1, b row1, a row3, b row3).
+struct EmuReg {
+    int64_t v[64];
+};
+static void emu_p32(EmuReg &a, EmuReg &b)
+{
+    EmuReg na, nb;
+    for (int l = 0; l < 32; ++l) {
+        na.v[l] = a.v[l], na.v[32 + l] = b.v[l];
+        nb.v[l] = a.v[32 + l], nb.v[32 + l] = b.v[32 + l];
+    }
+    a = na, b = nb;
+}
+static void emu_p16(EmuReg &a, EmuReg &b)
+{
+    EmuReg na, nb;
+    for (int l = 0; l < 16; ++l) {
+        na.v[l] = a.v[l], na.v[16 + l] = b.v[l], na.v[32 + l] = a.v[32 + l], na.v[48 + l] = b.v[32 + l];
+        nb.v[l] = a.v[16 + l], nb.v[16 + l] = b.v[16 + l], nb.v[32 + l] = a.v[48 + l], nb.v[48 + l] = b.v[48 + l];
+    }
+    a = na, b = nb;
+}
+static void emu_transpose4(EmuReg *x)
+{
+    emu_p32(x[0], x[2]);
+    emu_p32(x[1], x[3]);
+    emu_p16(x[0], x[1]);
+    emu_p16(x[2], x[3]);
+}
+
 extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span *spans,
                             int32_t n_spans, const kv_chunk_spec *spec, const int64_t *region_bytes,
                             int64_t staging_bytes, int32_t copy, int64_t *violations,
@@ -110,6 +144,9 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     const uint32_t split = 1u << a.split_shift;
     const int64_t items = info.tiles * split;
     std::vector<uint8_t> seen((size_t)items, 0);
+    // head-major 4x4-block walk: every vector of every tile written once
+    const int64_t tvec = a.tile_bytes / 16;
+    std::vector<uint64_t> written(a.hm_t4 ? (size_t)((info.tiles * tvec + 63) / 64) : 0, 0);
     const int64_t step = (int64_t)grid * kvx::kWavesPerBlock;
     const int64_t nreg = (int64_t)d->num_layers * d->num_kv;
 
@@ -139,6 +176,59 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
                     continue;
                 }
                 uint32_t first, count;
+                if (a.page_layout == KV_PAGE_HEAD_MAJOR && a.hm_t4) {
+                    // the kernel's block walk: loads, the register transpose, stores
+                    const uint32_t n_tok = t.nbytes / a.tok, H = a.hm_heads, bs = a.block_size;
+                    const int64_t page_vec = (int64_t)H * bs * 16, tile_vec = (int64_t)n_tok * H * 16;
+                    if (poff + page_vec * 16 > region_bytes[t.region]) { ++*violations; continue; }
+                    kvx::part_range(kvx::hm_t4_units(n_tok, H), (uint32_t)(item % split), split, &first, &count);
+                    uint8_t *block = static_cast<uint8_t *>(d->bases[t.region]) + poff;
+                    uint8_t *tile_p = a.chunk_base + t.chunk_off;
+                    for (uint32_t u = first; u < first + count; ++u) {
+                        const uint32_t j0 = (u / (H / 4)) * 4, hb = (u % (H / 4)) * 4;
+                        EmuReg x[4];
+                        for (int r = 0; r < 4; ++r)
+                            for (int l = 0; l < 64; ++l) {
+                                if (direction == KV_GATHER) {
+                                    const int64_t pv = ((int64_t)(hb + r) * bs + j0) * 16 + l;
+                                    if (pv >= page_vec) ++*violations;
+                                    x[r].v[l] = pv;
+                                } else {
+                                    x[r].v[l] = j0 + r < n_tok ? ((int64_t)(j0 + r) * H + hb) * 16 + l : -1;
+                                }
+                            }
+                        emu_transpose4(x);
+                        for (int r = 0; r < 4; ++r)
+                            for (int l = 0; l < 64; ++l) {
+                                int64_t dst, mark;
+                                if (direction == KV_GATHER) {
+                                    dst = ((int64_t)(j0 + r) * H + hb) * 16 + l;  // chunk vector
+                                    if (dst >= tile_vec) continue;                // past the tile: dropped
+                                    mark = dst;
+                                } else {
+                                    if (j0 + (l >> 4) >= n_tok) continue;         // token past the tile
+                                    dst = ((int64_t)(hb + r) * bs + j0) * 16 + l;   // pool vector
+                                    if (dst >= page_vec) { ++*violations; continue; }
+                                    // the pool vector of (head, token, q) is the tile's
+                                    // chunk-order vector (token, head, q)
+                                    const int64_t hh = dst / (bs * 16), jj = dst / 16 % bs, q = dst % 16;
+                                    mark = (jj * H + hh) * 16 + q;
+                                }
+                                const int64_t src = x[r].v[l];
+                                if (src < 0) { ++*violations; continue; }      // would store a zero
+                                const uint64_t bit = (uint64_t)(tile * tvec + mark);
+                                if (written[bit / 64] >> (bit % 64) & 1u) ++*violations;
+                                written[bit / 64] |= 1ull << (bit % 64);
+                                if (direction == KV_GATHER) {
+                                    if (t.chunk_off + dst * 16 + 16 > staging_bytes) { ++*violations; continue; }
+                                    if (copy) std::memcpy(tile_p + dst * 16, block + src * 16, 16);
+                                } else {
+                                    if (copy) std::memcpy(block + dst * 16, tile_p + src * 16, 16);
+                                }
+                            }
+                    }
+                    continue;
+                }
                 kvx::part_range(t.nbytes >> 4, (uint32_t)(item % split), split, &first, &count);
                 if (a.page_layout == KV_PAGE_HEAD_MAJOR) {
                     // each lane's cursor, as the kernel advances it, 64 vectors at a time
@@ -170,6 +260,21 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     }
     for (int64_t i = 0; i < items; ++i)
         if (seen[i] != 1) ++*violations;
+    if (a.hm_t4) {  // every vector of every tile with a valid block id written exactly once
+        uint32_t s = 0;
+        for (int64_t i = 0; i < info.tiles; ++i) {
+            s = kvx::find_span(records, s, n_rec, i);
+            const kvx::TileRef t = a.layout == KV_LAYER_FIRST ? kvx::resolve_tile<KV_LAYER_FIRST>(a, records[s], i)
+                                                              : kvx::resolve_tile<KV_PAGE_FIRST>(a, records[s], i);
+            const int32_t blk = records[s].table[t.page];
+            if (blk < 0 || (uint32_t)blk >= a.num_blocks) continue;
+            for (int64_t v = 0; v < tvec; ++v) {
+                const uint64_t bit = (uint64_t)(i * tvec + v);
+                const bool w = written[bit / 64] >> (bit % 64) & 1u;
+                if (w != (v < (int64_t)(t.nbytes / 16))) ++*violations;
+            }
+        }
+    }
     return KV_OK;
 }
 
