@@ -801,7 +801,8 @@ def main():
     cpu = cpu_baseline(res, args.cpu_budget) if args.cpu_baseline else None
     res.pop("host_sample", None)
     host = host_leg(args, dev) if args.host_path else None
-    others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8"], 5) \
+    others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
+                                  "hnd_rows24"], 5) \
         if args.others else None
     pipeline = pipeline_leg(args, dev) if args.pipeline else None
 

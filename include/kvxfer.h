@@ -142,8 +142,11 @@ typedef struct {
     int32_t head_dim;     /* D >= 1 */
     int32_t elem_bytes;   /* 1, 2, 4 or 8 (the payload is moved as opaque bytes) */
     int32_t block_size;   /* tokens per page, >= 1 */
-    int32_t page_layout;  /* KV_PAGE_TOKEN_MAJOR or KV_PAGE_HEAD_MAJOR; head-major needs
-                             head_dim*elem_bytes to be a multiple of 16 */
+    int32_t page_layout;  /* KV_PAGE_TOKEN_MAJOR or KV_PAGE_HEAD_MAJOR; a head-major row,
+                             head_dim*elem_bytes bytes, must be a multiple of 16 bytes, or a
+                             multiple of 4 with tok <= 8192 (such rows are transposed
+                             through LDS); other rows: KV_ERR_ALIGN, too large a token for
+                             4-byte rows: KV_ERR_ARG */
     int64_t num_blocks;   /* blocks per (layer, kv) region, 1 .. 2^31-1 */
     int64_t block_stride; /* bytes between consecutive blocks of one region */
     void *const *bases;   /* host array of num_layers*num_kv device pointers; the
@@ -191,7 +194,8 @@ typedef struct {
  * table, an error word, a 4 MiB span-record arena with its pinned mirror and 256
  * events) is created on the first transfer, on the device current then; later
  * transfers must run with the same device current.  Errors: KV_ERR_ARG,
- * KV_ERR_ALIGN (a base or block_stride not 16-byte aligned), KV_ERR_OOM. */
+ * KV_ERR_ALIGN (a base, block_stride or tok not 16-byte aligned, or a head-major
+ * row neither 16- nor 4-byte aligned), KV_ERR_OOM. */
 KV_API int kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 
 /* Frees the handle and its device state, after waiting for the transfers it

@@ -68,11 +68,16 @@ int check_desc(const kv_pool_desc *d)
     if (d->num_blocks < 1 || d->num_blocks > kMaxU31) return KV_ERR_ARG;
     if (d->page_layout != KV_PAGE_TOKEN_MAJOR && d->page_layout != KV_PAGE_HEAD_MAJOR)
         return KV_ERR_ARG;
-    if (d->page_layout == KV_PAGE_HEAD_MAJOR && ((int64_t)d->head_dim * d->elem_bytes) % 16 != 0)
-        return KV_ERR_ALIGN;
-    const int64_t tok = (int64_t)d->num_heads * d->head_dim * d->elem_bytes;
+    const int64_t row = (int64_t)d->head_dim * d->elem_bytes;
+    const int64_t tok = (int64_t)d->num_heads * row;
     if (tok > kMaxU31 || tok * d->block_size > kMaxU31) return KV_ERR_ARG;
     if (tok % 16 != 0) return KV_ERR_ALIGN;
+    // head-major rows: whole 16-byte vectors, or whole 4-byte words with a token
+    // (all heads) that fits one wave's LDS slice
+    if (d->page_layout == KV_PAGE_HEAD_MAJOR && row % 16 != 0) {
+        if (row % 4 != 0) return KV_ERR_ALIGN;
+        if (!kvx::hm_lds_ok(KV_PAGE_HEAD_MAJOR, row, tok)) return KV_ERR_ARG;
+    }
     const int64_t tile = tok * d->block_size;
     if (d->block_stride < tile) return KV_ERR_ARG;
     if (d->block_stride % 16 != 0) return KV_ERR_ALIGN;
@@ -228,15 +233,25 @@ int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
     a->page_layout = (uint32_t)d->page_layout;
     a->cached = (spec->flags & KV_FLAG_CACHED) ? 1u : 0u;
     if (d->page_layout == KV_PAGE_HEAD_MAJOR) {
-        const uint32_t r16 = (uint32_t)((int64_t)d->head_dim * d->elem_bytes / 16);
+        const int64_t row = (int64_t)d->head_dim * d->elem_bytes;
         const uint32_t H = (uint32_t)d->num_heads;
         a->hm_heads = H;
-        a->hm_r16 = r16;
-        a->hm_bs_r16 = (uint32_t)d->block_size * r16;
-        a->hm_dq = 64u % r16;
-        a->hm_dh = (64u / r16) % H;
-        a->hm_dj = (64u / r16) / H;
-        a->hm_t4 = kvx::hm_t4_ok(a->page_layout, r16, H, (uint32_t)d->block_size) ? 1u : 0u;
+        a->hm_row = (uint32_t)row;
+        if (kvx::hm_lds_ok(a->page_layout, row, tok_bytes(d))) {
+            a->hm_lds = 1;
+            a->hm_rd = (uint32_t)(row / 4);
+            a->hm_tj = kvx::hm_lds_tokens(row, tok_bytes(d), (uint32_t)d->block_size);
+            a->hm_m_rd = kvx::magic_u16(a->hm_rd);
+            a->hm_m_run = kvx::magic_u16(a->hm_tj * a->hm_rd);
+        } else {
+            const uint32_t r16 = (uint32_t)(row / 16);
+            a->hm_r16 = r16;
+            a->hm_bs_r16 = (uint32_t)d->block_size * r16;
+            a->hm_dq = 64u % r16;
+            a->hm_dh = (64u / r16) % H;
+            a->hm_dj = (64u / r16) / H;
+            a->hm_t4 = kvx::hm_t4_ok(a->page_layout, r16, H, (uint32_t)d->block_size) ? 1u : 0u;
+        }
     }
     if (info) *info = inf;
     return KV_OK;

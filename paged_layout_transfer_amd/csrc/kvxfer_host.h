@@ -211,14 +211,14 @@ int dma_walk(const Launch &a, const SpanDev *rec, uint32_t n_rec, const int32_t 
             if (int rc = emit(c)) return rc;
             continue;
         }
-        const int64_t row = (int64_t)a.hm_r16 * 16;
+        const int64_t row = a.hm_row;
         c.width = row;
         c.rows = t.nbytes / a.tok;
         c.pool_pitch = row;
         c.chunk_pitch = (int64_t)a.hm_heads * row;
         uint8_t *pool0 = c.pool, *chunk0 = c.chunk;
         for (uint32_t h = 0; h < a.hm_heads; ++h) {
-            c.pool = pool0 + (int64_t)h * a.hm_bs_r16 * 16;
+            c.pool = pool0 + (int64_t)h * a.block_size * row;
             c.chunk = chunk0 + h * row;
             if (int rc = emit(c)) return rc;
         }

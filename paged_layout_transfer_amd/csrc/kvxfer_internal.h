@@ -86,6 +86,12 @@ namespace kvx {
 #ifndef KVX_HM_T4_UNITS
 #define KVX_HM_T4_UNITS 8      // 4x4 blocks (4 KiB each) in flight per wave, head-major pages
 #endif
+#ifndef KVX_HM_LDS_SLICE
+#define KVX_HM_LDS_SLICE 8192  // LDS bytes per wave, head-major rows not of whole 16-byte vectors
+#endif
+#ifndef KVX_HM_LDS_UNROLL
+#define KVX_HM_LDS_UNROLL 8    // 4-byte words per lane in flight, same pages
+#endif
 #ifndef KVX_TAIL_GROUP
 #define KVX_TAIL_GROUP 4       // vectors per lane per group after the full groups
 #endif
@@ -151,7 +157,19 @@ struct Launch {
     uint32_t cached;       // 1: plain cached loads and stores (KV_FLAG_CACHED), else nontemporal
     uint32_t seg_bytes;    // > 0: gather in segments of this many bytes (gather_seg_bytes)
     uint32_t hm_t4;        // 1: head-major pages moved in 4-token x 4-head blocks (hm_t4_ok)
+    // head-major pages whose head rows are not whole 16-byte vectors (hm_lds_ok): row
+    // bytes, 4-byte words per row, tokens per LDS slab (hm_lds_tokens), and the
+    // multipliers (magic_u16) that divide by hm_rd and by hm_tj * hm_rd
+    uint32_t hm_lds;
+    uint32_t hm_row;
+    uint32_t hm_rd;
+    uint32_t hm_tj;
+    uint64_t hm_m_rd;
+    uint64_t hm_m_run;
 };
+
+// Kernel-internal page layout value: head-major pages staged through LDS.
+#define KVX_PAGE_HM_LDS 2
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
 // vector q of that head's row -- and its offset (in vectors) inside a head-major
@@ -279,6 +297,46 @@ __host__ __device__ constexpr bool hm_t4_ok(uint32_t page_layout, uint32_t r16, 
 __host__ __device__ inline uint32_t hm_t4_units(uint32_t n_tok, uint32_t heads)
 {
     return ((n_tok + 3) / 4) * (heads / 4);
+}
+
+// Head-major pages whose head rows (row = D*E bytes) are not whole 16-byte vectors go
+// through a per-wave LDS slice in slabs of whole tokens: rows must be whole 4-byte
+// words and one token (all heads) must fit the slice.
+__host__ __device__ constexpr bool hm_lds_ok(uint32_t page_layout, int64_t row, int64_t tok)
+{
+    return page_layout == KV_PAGE_HEAD_MAJOR && row % 16 != 0 && row % 4 == 0 && tok <= KVX_HM_LDS_SLICE;
+}
+
+// Tokens per LDS slab (a slab is all heads of whole tokens: one contiguous run of the
+// chunk, and one run of tj rows per head in the pool block).  As many as the slice
+// holds, at most a page; when a slab is less than a page, a multiple of the tokens that
+// make a head's run whole 128-byte lines (128 / gcd(row, 128)) if one fits, so no slab
+// boundary splits a pool line between two slabs.
+__host__ __device__ inline uint32_t hm_lds_tokens(int64_t row, int64_t tok, uint32_t block_size)
+{
+    const int64_t fit = KVX_HM_LDS_SLICE / tok;
+    if (fit >= block_size) return block_size;
+    int64_t g = 128, r = row;
+    while (r) {
+        const int64_t t = g % r;
+        g = r;
+        r = t;
+    }
+    const int64_t q = 128 / g;
+    return (uint32_t)(fit >= q ? fit - fit % q : fit);
+}
+
+// Division by a constant d in [1, 2^16] as a multiply: with m = ceil(2^32 / d),
+// (n * m) >> 32 == n / d for every n < 2^16 (m*d - 2^32 < d, so the error term
+// n*(m*d - 2^32) / (d*2^32) stays below 1/d, less than the gap from n/d's fraction
+// to the next integer).
+__host__ __device__ constexpr uint64_t magic_u16(uint32_t d)
+{
+    return ((1ull << 32) + d - 1) / d;
+}
+__host__ __device__ inline uint32_t mdiv(uint32_t n, uint64_t m)
+{
+    return (uint32_t)(((uint64_t)n * m) >> 32);
 }
 
 // Segment size for a gather over tiles of tile_bytes (0: one tile per wave item).

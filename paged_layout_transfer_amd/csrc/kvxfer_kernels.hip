@@ -330,6 +330,99 @@ __device__ __forceinline__ void copy_head_major_t4(const uint8_t *block, uint8_t
     }
 }
 
+// 4-byte pool-side words of the LDS-staged head-major path.
+typedef KVX_GLOBAL uint32_t gword;
+template <bool NT>
+__device__ __forceinline__ uint32_t ld_word(const gword *p)
+{
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st_word(gword *p, uint32_t v)
+{
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// Head-major pages whose head rows are not whole 16-byte vectors (rows of rd 4-byte
+// words): slabs [s0, s1) of all heads x tj tokens (hm_lds_tokens) pass through this
+// wave's LDS slice, which holds a slab in chunk (token-major) order, so the chunk side
+// moves whole 16-byte vectors of the slab's contiguous run.  The pool side is the
+// slab's run of tj rows in each head, moved as 4-byte words with consecutive lanes on
+// consecutive words (pool order): pool word w of a slab is head h = w / (tj*rd), row
+// jj and word q of i = w - h*tj*rd (jj = i / rd), at pool word (h*bs + j0)*rd + i and
+// slice word (jj*H + h)*rd + q, the two divisions done as multiplies (magic_u16).
+// Gather fills the slice word by word from the pool and empties it in vectors into
+// the chunk; scatter the reverse.  Only this wave uses its slice and a wave's LDS
+// accesses complete in order, so the phases need no barrier; wave_barrier only keeps
+// the compiler from moving accesses across a phase boundary.
+template <int DIR, bool NT>
+__device__ __forceinline__ void copy_head_major_lds(uint32_t *lds, uint8_t *block, uint8_t *chunk_tile,
+                                                    uint32_t s0, uint32_t s1, uint32_t n_tok, uint32_t lane,
+                                                    const Launch &a)
+{
+    constexpr int U = KVX_HM_LDS_UNROLL;
+    constexpr int UV = KVX_HM_LDS_SLICE / 1024;  // chunk vectors per lane in a full slab
+    const uint32_t H = a.hm_heads, rd = a.hm_rd, tj = a.hm_tj, bs = a.block_size;
+    const uint32_t run = tj * rd, words = H * run;
+    gword *const pool = (gword *)block;
+    for (uint32_t sl = s0; sl < s1; ++sl) {
+        const uint32_t j0 = sl * tj;
+        const uint32_t t = min32(tj, n_tok - j0);
+        const uint32_t nvec = t * a.tok / 16u;
+        uint8_t *const cs = chunk_tile + (uint64_t)j0 * a.tok;
+        if (DIR == KV_SCATTER) {  // chunk run -> slice
+            const PtrSide<NT> in{as_global(cs)};
+            u32x4 x[UV];
+#pragma unroll
+            for (int k = 0; k < UV; ++k)
+                if (lane + 64u * k < nvec) x[k] = in.load(lane + 64u * k);
+#pragma unroll
+            for (int k = 0; k < UV; ++k)
+                if (lane + 64u * k < nvec) *(u32x4 *)(lds + 4u * (lane + 64u * k)) = x[k];
+            __builtin_amdgcn_wave_barrier();
+        }
+        for (uint32_t w = lane; w < words; w += 64u * U) {
+            uint32_t pw[U], lw[U], x[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t ww = w + 64u * u;
+                const uint32_t h = mdiv(ww, a.hm_m_run);
+                const uint32_t i = ww - h * run;
+                const uint32_t jj = mdiv(i, a.hm_m_rd);
+                ok[u] = ww < words && jj < t;
+                pw[u] = (h * bs + j0) * rd + i;
+                lw[u] = (jj * H + h) * rd + (i - jj * rd);
+            }
+            if (DIR == KV_GATHER) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (ok[u]) x[u] = ld_word<NT>(pool + pw[u]);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (ok[u]) lds[lw[u]] = x[u];
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (ok[u]) x[u] = lds[lw[u]];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (ok[u]) st_word<NT>(pool + pw[u], x[u]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (DIR == KV_GATHER) {  // slice -> chunk run
+            const BufSide<kGatherChunkPol<NT>> out(cs, nvec * 16u);
+#pragma unroll
+            for (int k = 0; k < UV; ++k)
+                if (lane + 64u * k < nvec) out.store(lane + 64u * k, *(const u32x4 *)(lds + 4u * (lane + 64u * k)));
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 template <int DIR, int LAYOUT, int PAGE, bool NT, bool SEG>
 __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 {
@@ -387,6 +480,15 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         uint32_t first, count;
         uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
         uint8_t *chunk_tile = a.chunk_base + t.chunk_off;
+        if constexpr (PAGE == KVX_PAGE_HM_LDS) {
+            // parts of a split tile are ranges of slabs
+            __shared__ __attribute__((aligned(16))) uint32_t slices[kWavesPerBlock][KVX_HM_LDS_SLICE / 4];
+            const uint32_t n_tok = t.nbytes / a.tok;
+            part_range((n_tok + a.hm_tj - 1) / a.hm_tj, (uint32_t)(item & ((1 << shift) - 1)), 1u << shift,
+                       &first, &count);
+            copy_head_major_lds<DIR, NT>(slices[wave], block, chunk_tile, first, first + count, n_tok, lane, a);
+            continue;
+        }
         if (PAGE == KV_PAGE_HEAD_MAJOR && a.hm_t4) {
             // parts of a split tile are ranges of 4x4 blocks
             const uint32_t n_tok = t.nbytes / a.tok;
@@ -427,8 +529,10 @@ static const void *pick_policy(const Launch &a)
 template <int DIR, int LAYOUT>
 static const void *pick_page(const Launch &a)
 {
-    return a.page_layout == KV_PAGE_HEAD_MAJOR ? pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a)
-                                               : pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
+    if (a.page_layout == KV_PAGE_HEAD_MAJOR)
+        return a.hm_lds ? pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS>(a)
+                        : pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a);
+    return pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
 }
 
 int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t stream)

@@ -13,7 +13,7 @@ values, so random bytes of the stated element width are used.
 
 Seeds: table/length seed 1000 + k and data seed k for workload k
 (tiny 1, llama8b 2, llama70b 3, mixed 4, mla_fp8 5, int8_kv 6, llama8b_hnd 7,
-fp8_hnd_d64 8, llama8b_tp8 9).  page_layout (default 0) is the pool's in-page order: 0 token-major
+fp8_hnd_d64 8, llama8b_tp8 9, hnd_rows24 10).  page_layout (default 0) is the pool's in-page order: 0 token-major
 [block_size][H][D], 1 head-major [H][block_size][D].
 """
 from __future__ import annotations
@@ -70,6 +70,12 @@ WORKLOADS: dict[str, dict] = {
                         block_size=16, num_blocks=16384, tokens=32768, fill="bytes",
                         layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm",
                         page_layout=1),
+    # Head-major pages whose head rows are not whole 16-byte vectors: 16 heads x 12 bf16
+    # dims = 24-byte rows, 64-token pages (24 KiB per layer-page).
+    "hnd_rows24": dict(k=10, num_layers=32, num_kv=2, num_heads=16, head_dim=12, elem_bytes=2,
+                       block_size=64, num_blocks=4096, tokens=32768, fill="bf16_uniform",
+                       layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm",
+                       page_layout=1),
 }
 
 

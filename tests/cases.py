@@ -25,6 +25,12 @@ def slot_capacity(pool: dict, chunks: dict) -> int:
     return chunks["chunk_layers"] * pool["num_kv"] * chunks["chunk_tokens"] * tok
 
 
+def head_rows_ok(row: int, tok: int) -> bool:
+    """Head-major pages the library takes: head rows of whole 16-byte vectors, or of
+    whole 4-byte words when a token (all heads) is at most 8 KiB."""
+    return row % 16 == 0 or (row % 4 == 0 and tok <= 8192)
+
+
 def make_case(rng: np.random.Generator, *, tok_multiple: int = 1, max_bytes: int = 1 << 20,
               layout: int | None = None, n_spans: int | None = None, medium: bool = False,
               head_major: bool | None = False):
@@ -75,9 +81,9 @@ def make_case(rng: np.random.Generator, *, tok_multiple: int = 1, max_bytes: int
         CT = bs * int(rng.integers(1, 4))
         lay = int(rng.integers(0, 2)) if layout is None else layout
         page_layout = int(rng.integers(0, 2)) if head_major is None else int(head_major)
-        if page_layout == 1 and (D * E) % tok_multiple:
+        if page_layout == 1 and not head_rows_ok(D * E, tok):
             if head_major:
-                continue            # head rows must be whole 16-byte vectors: draw again
+                continue            # a head-major shape the library refuses: draw again
             page_layout = 0
         pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E,
                     block_size=bs, num_blocks=N, block_stride=block_stride, page_layout=page_layout)
@@ -110,3 +116,43 @@ def staging_for(chunks: dict, fill: int | None = None, rng: np.random.Generator 
     if rng is not None:
         return rng.integers(0, 256, size=n, dtype=np.uint8)
     return np.full(n, 0xA5 if fill is None else fill, dtype=np.uint8)
+
+
+# H, D, E, bs: head rows not of whole 16-byte vectors (4-byte words), staged through LDS
+# in 8 KiB slabs of all heads x tokens: a whole page; tokens cut to whole pool lines
+# (20 x 12-byte rows: 34 fit, 32 taken, pages of 64; 16 x 24-byte rows: 21 fit, 16
+# taken); too few for a whole line (4 x 100-byte rows: 20 fit, 32 would be needed);
+# one token (64 x 100-byte rows).
+HM_LDS_SHAPES = [(4, 2, 2, 16), (2, 4, 2, 16), (4, 6, 2, 8), (8, 8, 1, 16), (4, 10, 2, 32), (2, 12, 2, 64),
+                 (16, 12, 2, 64), (20, 3, 4, 64), (64, 100, 1, 4), (2, 1, 8, 16), (128, 8, 1, 32),
+                 (4, 100, 1, 128)]
+
+
+def head_major_case(rng: np.random.Generator, H: int, D: int, E: int, bs: int):
+    """A head-major case of a given head shape: 1-3 layers, K/V or one, 1-2 spans that
+    start 0-2 pages in and end in a partial page, chunks of 1-3 pages, either chunk
+    layout, all layers per chunk or one."""
+    L, KV = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    tok = H * D * E
+    spans_tok = [(int(rng.integers(0, 3)) * bs, 0) for _ in range(int(rng.integers(1, 3)))]
+    spans_tok = [(t0, t0 + int(rng.integers(1, 6 * bs))) for t0, _ in spans_tok]   # partial last pages
+    n_pages = sum(-(-t1 // bs) for _, t1 in spans_tok)
+    N = n_pages + 5
+    perm = rng.permutation(N).astype(np.int32)
+    CT = bs * int(rng.integers(1, 4))
+    layout = int(rng.integers(0, 2))
+    CL = L if rng.random() < 0.5 else 1
+    spans, used, fc, slot = [], 0, 0, 0
+    for t0, t1 in spans_tok:
+        n = -(-t1 // bs)
+        tbl = perm[used:used + n]
+        used += n
+        n_tc = -(-(t1 - t0) // CT)
+        spans.append((tbl, t0, t1, fc))
+        fc += (L // CL) * n_tc
+    slot = CL * KV * CT * tok
+    pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs, num_blocks=N,
+                block_stride=bs * tok, page_layout=1)
+    chunks = dict(layout=layout, chunk_layers=CL, chunk_tokens=CT, layer_begin=0, layer_end=L, slot_bytes=slot,
+                  n_slots=fc)
+    return pool, spans, chunks

@@ -147,6 +147,13 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     // head-major 4x4-block walk: every vector of every tile written once
     const int64_t tvec = a.tile_bytes / 16;
     std::vector<uint64_t> written(a.hm_t4 ? (size_t)((info.tiles * tvec + 63) / 64) : 0, 0);
+    // LDS-staged head-major walk: every 4-byte word of every tile written once (words
+    // numbered in chunk order), and every slice word read was written in the same slab
+    const int64_t twords = a.tile_bytes / 4;
+    std::vector<uint64_t> wwritten(a.hm_lds ? (size_t)((info.tiles * twords + 63) / 64) : 0, 0);
+    std::vector<uint32_t> slice(KVX_HM_LDS_SLICE / 4);
+    std::vector<int64_t> tag(KVX_HM_LDS_SLICE / 4, -1);
+    int64_t gen = 0;
     const int64_t step = (int64_t)grid * kvx::kWavesPerBlock;
     const int64_t nreg = (int64_t)d->num_layers * d->num_kv;
 
@@ -176,6 +183,81 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
                     continue;
                 }
                 uint32_t first, count;
+                if (a.page_layout == KV_PAGE_HEAD_MAJOR && a.hm_lds) {
+                    // the kernel's LDS slab walk, lane by lane and phase by phase (lanes
+                    // of one phase touch distinct slice words, so their order is free)
+                    const uint32_t n_tok = t.nbytes / a.tok, H = a.hm_heads, rd = a.hm_rd, tj = a.hm_tj,
+                                   bs = a.block_size;
+                    const uint32_t run = tj * rd, words = H * run;
+                    const int64_t page_words = (int64_t)H * bs * rd;
+                    if (tj == 0 || (int64_t)words * 4 > KVX_HM_LDS_SLICE ||
+                        poff + page_words * 4 > region_bytes[t.region]) {
+                        ++*violations;
+                        continue;
+                    }
+                    kvx::part_range((n_tok + tj - 1) / tj, (uint32_t)(item % split), split, &first, &count);
+                    uint8_t *block = static_cast<uint8_t *>(d->bases[t.region]) + poff;
+                    uint8_t *tile_p = a.chunk_base + t.chunk_off;
+                    auto mark = [&](int64_t word) {  // chunk-order word of this tile
+                        const uint64_t bit = (uint64_t)(tile * twords + word);
+                        if (wwritten[bit / 64] >> (bit % 64) & 1u) ++*violations;
+                        wwritten[bit / 64] |= 1ull << (bit % 64);
+                    };
+                    for (uint32_t sl = first; sl < first + count; ++sl) {
+                        const uint32_t j0 = sl * tj, tt = std::min(tj, n_tok - j0), nvec = tt * a.tok / 16;
+                        const int64_t cs = (int64_t)j0 * a.tok;
+                        ++gen;
+                        if (direction == KV_SCATTER)
+                            for (uint32_t lane = 0; lane < 64; ++lane)
+                                for (uint32_t v = lane; v < nvec; v += 64) {
+                                    if (v >= 64u * (KVX_HM_LDS_SLICE / 1024) ||
+                                        t.chunk_off + cs + (v + 1) * 16ll > staging_bytes) {
+                                        ++*violations;
+                                        continue;
+                                    }
+                                    if (copy) std::memcpy(&slice[4 * v], tile_p + cs + v * 16ll, 16);
+                                    for (int k = 0; k < 4; ++k) tag[4 * v + k] = gen;
+                                }
+                        for (uint32_t lane = 0; lane < 64; ++lane)
+                            for (uint32_t w = lane; w < words; w += 64u * KVX_HM_LDS_UNROLL)
+                                for (uint32_t u = 0; u < KVX_HM_LDS_UNROLL; ++u) {
+                                    const uint32_t ww = w + 64u * u;
+                                    const uint32_t h = kvx::mdiv(ww, a.hm_m_run);
+                                    const uint32_t i = ww - h * run;
+                                    const uint32_t jj = kvx::mdiv(i, a.hm_m_rd);
+                                    if (!(ww < words && jj < tt)) continue;
+                                    if (h != ww / run || jj != i / rd) { ++*violations; continue; }
+                                    const uint32_t q = i - jj * rd;
+                                    const int64_t pw = ((int64_t)h * bs + j0) * rd + i;
+                                    const int64_t lw = ((int64_t)jj * H + h) * rd + q;
+                                    if (pw >= page_words || lw * 4 >= KVX_HM_LDS_SLICE) { ++*violations; continue; }
+                                    if (direction == KV_GATHER) {
+                                        if (tag[lw] == gen) ++*violations;  // two words into one place
+                                        if (copy) std::memcpy(&slice[lw], block + pw * 4, 4);
+                                        tag[lw] = gen;
+                                    } else {
+                                        if (tag[lw] != gen) { ++*violations; continue; }  // stale slice word
+                                        if (copy) std::memcpy(block + pw * 4, &slice[lw], 4);
+                                        mark(((int64_t)(j0 + jj) * H + h) * rd + q);
+                                    }
+                                }
+                        if (direction == KV_GATHER)
+                            for (uint32_t lane = 0; lane < 64; ++lane)
+                                for (uint32_t v = lane; v < nvec; v += 64) {
+                                    if (v >= 64u * (KVX_HM_LDS_SLICE / 1024) ||
+                                        t.chunk_off + cs + (v + 1) * 16ll > staging_bytes) {
+                                        ++*violations;
+                                        continue;
+                                    }
+                                    bool fresh = true;
+                                    for (int k = 0; k < 4; ++k) fresh = fresh && tag[4 * v + k] == gen;
+                                    if (!fresh) { ++*violations; continue; }
+                                    if (copy) std::memcpy(tile_p + cs + v * 16ll, &slice[4 * v], 16);
+                                    for (int k = 0; k < 4; ++k) mark(cs / 4 + 4ll * v + k);
+                                }
+                    }
+                    continue;
+                }
                 if (a.page_layout == KV_PAGE_HEAD_MAJOR && a.hm_t4) {
                     // the kernel's block walk: loads, the register transpose, stores
                     const uint32_t n_tok = t.nbytes / a.tok, H = a.hm_heads, bs = a.block_size;
@@ -260,6 +342,21 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     }
     for (int64_t i = 0; i < items; ++i)
         if (seen[i] != 1) ++*violations;
+    if (a.hm_lds) {  // every word of every tile with a valid block id written exactly once
+        uint32_t s = 0;
+        for (int64_t i = 0; i < info.tiles; ++i) {
+            s = kvx::find_span(records, s, n_rec, i);
+            const kvx::TileRef t = a.layout == KV_LAYER_FIRST ? kvx::resolve_tile<KV_LAYER_FIRST>(a, records[s], i)
+                                                              : kvx::resolve_tile<KV_PAGE_FIRST>(a, records[s], i);
+            const int32_t blk = records[s].table[t.page];
+            if (blk < 0 || (uint32_t)blk >= a.num_blocks) continue;
+            for (int64_t v = 0; v < twords; ++v) {
+                const uint64_t bit = (uint64_t)(i * twords + v);
+                const bool w = wwritten[bit / 64] >> (bit % 64) & 1u;
+                if (w != (v < (int64_t)(t.nbytes / 4))) ++*violations;
+            }
+        }
+    }
     if (a.hm_t4) {  // every vector of every tile with a valid block id written exactly once
         uint32_t s = 0;
         for (int64_t i = 0; i < info.tiles; ++i) {

@@ -116,7 +116,9 @@ POOL_CASES = [
     (dict(bases=[FAKE, FAKE + 8, FAKE, FAKE]), K.KV_ERR_ALIGN),
     (dict(bases=[FAKE, 0, FAKE, FAKE]), K.KV_ERR_ARG),
     (dict(page_layout=2), K.KV_ERR_ARG),
-    (dict(H=2, D=8, E=1, page_layout=1), K.KV_ERR_ALIGN),   # 8-byte head rows
+    (dict(H=8, D=1, E=2, page_layout=1), K.KV_ERR_ALIGN),   # 2-byte head rows
+    (dict(H=8, D=3, E=2, page_layout=1), K.KV_ERR_ALIGN),   # 6-byte head rows (tokens of 48 B)
+    (dict(H=1026, D=8, E=1, page_layout=1), K.KV_ERR_ARG),  # 8-byte rows, token over 8 KiB
 ]
 
 

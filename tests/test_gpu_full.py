@@ -139,6 +139,7 @@ HBM_CASES = {
     "llama8b_hnd": dict(layers=[0, 31], requests=[0]),
     "fp8_hnd_d64": dict(layers=[0, 31], requests=[0]),
     "llama8b_tp8": dict(layers=[0, 31], requests=[0]),
+    "hnd_rows24": dict(layers=[0, 31], requests=[0]),
 }
 
 

@@ -193,15 +193,16 @@ def test_interleaved_kv_pool():
             _compare(d, pool, spans, chunks, flat, staging, "interleaved-%d" % layout, views=views)
 
 
-@pytest.mark.parametrize("H,D,bs", [(1, 64, 16), (2, 288, 16)])
-def test_bad_block_id_is_skipped_and_reported(H, D, bs):
+@pytest.mark.parametrize("H,D,bs,page_layout", [(1, 64, 16, 0), (2, 288, 16, 0), (8, 4, 16, 1)])
+def test_bad_block_id_is_skipped_and_reported(H, D, bs, page_layout):
     """A table entry past the pool: that page's tiles are skipped, the sticky error bit is
     set, and every other tile still moves (page-first, one chunk per page).  The second
-    shape has 18 KiB tiles, so the gather takes the segment walk."""
+    shape has 18 KiB tiles, so the gather takes the segment walk; the third is head-major
+    with 8-byte rows (the LDS slab walk)."""
     L, KV, E, N = 2, 2, 2, 32
     tok = H * D * E
     pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
-                num_blocks=N, block_stride=bs * tok)
+                num_blocks=N, block_stride=bs * tok, page_layout=page_layout)
     rng = np.random.default_rng(60_000)
     good = rng.permutation(N)[:6].astype(np.int32)
     bad = good.copy()
@@ -310,11 +311,29 @@ def test_head_major_pool_cases(seed):
                  dma=seed % 4 == 0)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_head_major_lds_cases(seed):
+    """Head-major pages whose head rows are not whole 16-byte vectors (4 to 100 bytes),
+    moved through LDS slabs: every slab shape of the list twice, odd seeds staged in pinned
+    host memory, every third seed with cached accesses, every fourth through the per-tile
+    copy-engine path."""
+    rng = np.random.default_rng(86_000 + seed)
+    pool, spans, chunks = cases.head_major_case(rng, *cases.HM_LDS_SHAPES[seed % len(cases.HM_LDS_SHAPES)])
+    regions, staging = _random(pool, chunks, seed)
+    flags = K.KV_FLAG_CACHED if seed % 3 == 0 else 0
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "head-major-lds-%d" % seed, ring=bool(seed % 2),
+                 dma=seed % 4 == 0, flags=flags)
+
+
 EXTREMES = {
     # 1-token pages of 16-byte tokens: every tile is one vector
     "one_token_pages": dict(L=3, KV=2, H=1, D=16, E=1, bs=1, N=900, spans=[(0, 500), (0, 77)], CT=64, CL=3),
     # 512-token pages of 2 KiB tokens: 1 MiB tiles, split between waves in both directions
     "huge_pages": dict(L=2, KV=2, H=8, D=128, E=2, bs=512, N=8, spans=[(0, 1500), (512, 1100)], CT=1024, CL=1),
+    # 64 heads x 100-byte rows: 400 KiB tiles, one token per LDS slab when head-major, split
+    # between waves
+    "word_rows": dict(L=2, KV=2, H=64, D=100, E=1, bs=64, N=24, spans=[(0, 700), (64, 300)], CT=128, CL=1),
     # a span that starts 300 pages into its table
     "deep_start": dict(L=2, KV=1, H=2, D=64, E=2, bs=16, N=400, spans=[(300 * 16, 300 * 16 + 70)], CT=32, CL=2),
 }

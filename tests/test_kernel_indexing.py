@@ -122,7 +122,8 @@ def test_emulated_split_tiles_match_oracle(emu_split, seed):
     _copy_case(emu_split, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
 
 
-FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8"]
+FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
+        "hnd_rows24"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -173,7 +174,7 @@ def _extreme_case(name, layout, page_layout):
     return pool, spans, chunks
 
 
-@pytest.mark.parametrize("name", ["one_token_pages", "huge_pages", "deep_start"])
+@pytest.mark.parametrize("name", ["one_token_pages", "huge_pages", "deep_start", "word_rows"])
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("page_layout", [0, 1])
 def test_emulated_extreme_shapes(emu, name, layout, page_layout):
@@ -266,45 +267,50 @@ def test_span_record_arena_never_overwrites_calls_in_flight(emu, pattern, lag):
 T4_SHAPES = [(4, 128, 2, 4), (8, 256, 1, 16), (12, 128, 2, 8), (4, 128, 2, 32)]   # H, D, E, bs: 256-B head rows
 
 
-def _t4_case(rng, H, D, E, bs):
-    L, KV = int(rng.integers(1, 4)), int(rng.integers(1, 3))
-    tok = H * D * E
-    spans_tok = [(int(rng.integers(0, 3)) * bs, 0) for _ in range(int(rng.integers(1, 3)))]
-    spans_tok = [(t0, t0 + int(rng.integers(1, 6 * bs))) for t0, _ in spans_tok]   # partial last pages
-    n_pages = sum(-(-t1 // bs) for _, t1 in spans_tok)
-    N = n_pages + 5
-    perm = rng.permutation(N).astype(np.int32)
-    CT = bs * int(rng.integers(1, 4))
-    layout = int(rng.integers(0, 2))
-    CL = L if rng.random() < 0.5 else 1
-    spans, used, fc, slot = [], 0, 0, 0
-    for t0, t1 in spans_tok:
-        n = -(-t1 // bs)
-        tbl = perm[used:used + n]
-        used += n
-        n_tc = -(-(t1 - t0) // CT)
-        spans.append((tbl, t0, t1, fc))
-        fc += (L // CL) * n_tc
-    slot = CL * KV * CT * tok
-    pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs, num_blocks=N,
-                block_stride=bs * tok, page_layout=1)
-    chunks = dict(layout=layout, chunk_layers=CL, chunk_tokens=CT, layer_begin=0, layer_end=L, slot_bytes=slot,
-                  n_slots=fc)
-    return pool, spans, chunks
-
-
 @pytest.mark.parametrize("seed", range(16))
 def test_emulated_head_major_blocks_match_oracle(emu, seed):
     """Head-major pages with 256-byte head rows take the 4x4-block walk with the register
     transpose (emulated with the measured lane swaps): bytes equal the oracle's."""
     rng = np.random.default_rng(33_000 + seed)
-    pool, spans, chunks = _t4_case(rng, *T4_SHAPES[seed % len(T4_SHAPES)])
+    pool, spans, chunks = cases.head_major_case(rng, *T4_SHAPES[seed % len(T4_SHAPES)])
     _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
+
+
+LDS_SHAPES = cases.HM_LDS_SHAPES
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_emulated_head_major_lds_matches_oracle(emu, seed):
+    """Head-major pages whose rows are not whole 16-byte vectors take the LDS slab walk
+    (the kernel's lanes, magic-multiply divisions and slice indices replayed on the CPU):
+    every word lands once, no slice word is read stale, bytes equal the oracle's."""
+    rng = np.random.default_rng(35_000 + seed)
+    pool, spans, chunks = cases.head_major_case(rng, *LDS_SHAPES[seed % len(LDS_SHAPES)])
+    _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_emulated_head_major_lds_split_match_oracle(emu_split, seed):
+    """The same with tiles split between waves (parts are ranges of slabs)."""
+    rng = np.random.default_rng(36_000 + seed)
+    pool, spans, chunks = cases.head_major_case(rng, *LDS_SHAPES[seed % len(LDS_SHAPES)])
+    _copy_case(emu_split, pool, spans, chunks, seed)
+
+
+def test_magic_division_is_exact():
+    """The multiply that replaces division by d in the LDS walk (ceil(2^32/d), high
+    word of the product) equals floor division for every numerator below 2^16, checked
+    for every divisor the walk can use (row words and slab words up to 2048) against
+    numpy's integer division."""
+    n = np.arange(1 << 16, dtype=np.uint64)
+    for d in range(1, 2049):
+        m = np.uint64(((1 << 32) + d - 1) // d)
+        assert np.array_equal((n * m) >> np.uint64(32), n // np.uint64(d)), d
 
 
 @pytest.mark.parametrize("seed", range(8))
 def test_emulated_head_major_blocks_split_match_oracle(emu_split, seed):
     """The same with tiles split between waves (parts are ranges of 4x4 blocks)."""
     rng = np.random.default_rng(34_000 + seed)
-    pool, spans, chunks = _t4_case(rng, *T4_SHAPES[seed % len(T4_SHAPES)])
+    pool, spans, chunks = cases.head_major_case(rng, *T4_SHAPES[seed % len(T4_SHAPES)])
     _copy_case(emu_split, pool, spans, chunks, seed)
