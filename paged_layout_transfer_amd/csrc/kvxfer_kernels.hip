@@ -18,8 +18,9 @@
 //      concurrent compute kernels: "Non-Intrusive Resource Sizing").  Gather goes
 //      through buffer instructions so that its sequential chunk stores can also
 //      carry the sc1 bit; scatter through global instructions.
-// No LDS and no matrix instructions: it is a pure byte copy, bound by HBM (both
-// sides in HBM) or by the host link (chunks in pinned host memory).
+// No matrix instructions, and LDS only for head-major pages whose head rows are not
+// whole 16-byte vectors (copy_head_major_lds): it is a pure byte copy, bound by HBM
+// (both sides in HBM) or by the host link (chunks in pinned host memory).
 //
 // A block id outside [0, num_blocks) is not followed: lane 0 sets the sticky
 // error bit and the wave skips that tile.  All offsets are 64-bit (the printed
