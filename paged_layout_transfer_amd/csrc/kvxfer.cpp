@@ -243,6 +243,14 @@ int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
             a->hm_tj = kvx::hm_lds_tokens(row, tok_bytes(d), (uint32_t)d->block_size);
             a->hm_m_rd = kvx::magic_u16(a->hm_rd);
             a->hm_m_run = kvx::magic_u16(a->hm_tj * a->hm_rd);
+            for (int dir = 0; dir < 2; ++dir) {
+                kvx::hm_lds_head_slab(dir, H, row, tok_bytes(d), (uint32_t)d->block_size, &a->hm_hg[dir],
+                                      &a->hm_htj[dir]);
+                if (a->hm_hg[dir]) {
+                    a->hm_m_hrun[dir] = kvx::magic_u16(a->hm_htj[dir] * a->hm_rd);
+                    a->hm_m_hgrp[dir] = kvx::magic_u16(a->hm_hg[dir] * a->hm_rd);
+                }
+            }
         } else {
             const uint32_t r16 = (uint32_t)(row / 16);
             a->hm_r16 = r16;

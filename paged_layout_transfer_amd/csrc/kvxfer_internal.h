@@ -166,10 +166,20 @@ struct Launch {
     uint32_t hm_tj;
     uint64_t hm_m_rd;
     uint64_t hm_m_run;
+    // where a slab of all heads cannot keep a direction's writes whole lines
+    // (hm_lds_head_slab), that direction's slabs of hg heads x tj tokens (hg == 0: the
+    // token slabs above), with multipliers dividing by tj * hm_rd and by hg * hm_rd;
+    // index 0 gather, 1 scatter
+    uint32_t hm_hg[2];
+    uint32_t hm_htj[2];
+    uint64_t hm_m_hrun[2];
+    uint64_t hm_m_hgrp[2];
 };
 
-// Kernel-internal page layout value: head-major pages staged through LDS.
+// Kernel-internal page layout values: head-major pages staged through LDS in token
+// slabs, and in head-group slabs (hm_lds_head_slab).
 #define KVX_PAGE_HM_LDS 2
+#define KVX_PAGE_HM_LDS_HEADS 3
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
 // vector q of that head's row -- and its offset (in vectors) inside a head-major
@@ -324,6 +334,51 @@ __host__ __device__ inline uint32_t hm_lds_tokens(int64_t row, int64_t tok, uint
     }
     const int64_t q = 128 / g;
     return (uint32_t)(fit >= q ? fit - fit % q : fit);
+}
+
+// Each direction's slabs should write whole 128-byte lines.  A token slab
+// (hm_lds_tokens) writes the chunk in one contiguous run, so gather's writes are whole
+// lines, but it covers whole pool lines only when it is a page or its head runs are
+// whole lines; otherwise each pool line is split between slabs.  Scatter (which
+// writes the pool) then takes slabs of whole pages of a group of heads, one contiguous
+// run of the block: the largest divisor of H whose pages fit (all groups equal), or,
+// when one head's page does not fit, one head and as many tokens as fit, cut to whole
+// lines where possible.  Gather (which then reads split lines twice) takes head-group
+// slabs only where their chunk runs, hg*row bytes of each token, are whole lines.
+// *hg = 0: keep the token slabs.
+__host__ __device__ inline void hm_lds_head_slab(int dir, uint32_t heads, int64_t row, int64_t tok,
+                                                 uint32_t block_size, uint32_t *hg, uint32_t *tj)
+{
+    const uint32_t t0 = hm_lds_tokens(row, tok, block_size);
+    *hg = 0;
+    *tj = t0;
+    if (t0 == block_size || (t0 * row) % 128 == 0) return;
+    const int64_t cap = KVX_HM_LDS_SLICE, page_run = (int64_t)block_size * row;
+    if (dir == KV_GATHER) {
+        if (page_run > cap || tok % 128) return;
+        for (uint32_t g = (uint32_t)(cap / page_run < heads ? cap / page_run : heads); g >= 1; --g)
+            if (heads % g == 0 && (g * row) % 128 == 0) {
+                *hg = g;
+                *tj = block_size;
+                return;
+            }
+        return;
+    }
+    if (page_run <= cap) {
+        uint32_t g = (uint32_t)(cap / page_run < heads ? cap / page_run : heads);
+        while (heads % g) --g;
+        *hg = g;
+        *tj = block_size;
+    } else {
+        *hg = 1;
+        *tj = hm_lds_tokens(row, row, block_size);  // tokens of one head that fit
+    }
+}
+
+// Slabs of a tile of n_tok tokens in head-group slabs: groups x token ranges.
+__host__ __device__ inline uint32_t hm_lds_slabs(uint32_t n_tok, uint32_t heads, uint32_t hg, uint32_t tj)
+{
+    return (heads / hg) * ((n_tok + tj - 1) / tj);
 }
 
 // Division by a constant d in [1, 2^16] as a multiply: with m = ceil(2^32 / d),

@@ -424,6 +424,137 @@ __device__ __forceinline__ void copy_head_major_lds(uint32_t *lds, uint8_t *bloc
     }
 }
 
+// Scatter of head-major rows of 4-byte words in slabs of hg heads x tj tokens
+// (hm_lds_head_slab: whole pages of a head group, where a slab of all heads cannot be
+// whole pool lines).  Slab sl is head group g = sl / (token ranges), token range the
+// rest.  The chunk's words of the slab, hg*rd per token, are read in chunk order --
+// word w is row jj = w / (hg*rd), head hh and word q of the remainder -- into the
+// slice in pool order, slice word (hh*tj + jj)*rd + q; the slice is then written out
+// along the pool, slice word w to pool word ((h0 + hh)*bs + j0)*rd + i with
+// hh = w / (tj*rd), i = w - hh*tj*rd: one contiguous run of the block when tj = bs.
+template <bool NT>
+__device__ __forceinline__ void hm_lds_scatter_heads(uint32_t *lds, uint8_t *block, const uint8_t *chunk_tile,
+                                                     uint32_t s0, uint32_t s1, uint32_t n_tok, uint32_t lane,
+                                                     const Launch &a)
+{
+    constexpr int U = KVX_HM_LDS_UNROLL;
+    const uint32_t H = a.hm_heads, rd = a.hm_rd, hg = a.hm_hg[1], tj = a.hm_htj[1], bs = a.block_size;
+    const uint32_t run = tj * rd, grp = hg * rd, n_tr = (n_tok + tj - 1) / tj;
+    gword *const pool = (gword *)block;
+    const gword *const chunk = (const gword *)chunk_tile;
+    for (uint32_t sl = s0; sl < s1; ++sl) {
+        const uint32_t g = sl / n_tr, j0 = (sl - g * n_tr) * tj, h0 = g * hg;
+        const uint32_t t = min32(tj, n_tok - j0);
+        const uint32_t in_words = t * grp;
+        for (uint32_t w = lane; w < in_words; w += 64u * U) {
+            uint32_t cw[U], lw[U], x[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t ww = w + 64u * u;
+                const uint32_t jj = mdiv(ww, a.hm_m_hgrp[1]);
+                const uint32_t rem = ww - jj * grp;
+                const uint32_t hh = mdiv(rem, a.hm_m_rd);
+                ok[u] = ww < in_words;
+                cw[u] = ((j0 + jj) * H + h0) * rd + rem;
+                lw[u] = (hh * tj + jj) * rd + (rem - hh * rd);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) x[u] = ld_word<NT>(chunk + cw[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) lds[lw[u]] = x[u];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t words = hg * run;
+        for (uint32_t w = lane; w < words; w += 64u * U) {
+            uint32_t pw[U], x[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t ww = w + 64u * u;
+                const uint32_t hh = mdiv(ww, a.hm_m_hrun[1]);
+                const uint32_t i = ww - hh * run;
+                ok[u] = ww < words && mdiv(i, a.hm_m_rd) < t;
+                pw[u] = ((h0 + hh) * bs + j0) * rd + i;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) x[u] = lds[w + 64u * u];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) st_word<NT>(pool + pw[u], x[u]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Gather of head-major rows of 4-byte words in slabs of whole pages of hg heads
+// (hm_lds_head_slab: where token slabs would split pool lines and a head group's chunk
+// runs are whole lines): the group's pages, one contiguous run of the block, are read
+// in pool order into the slice (slice word w = pool word ((h0 + hh)*bs + j0)*rd + i,
+// hh = w / (tj*rd), i = w - hh*tj*rd); the slice is then written out along the chunk,
+// hg*rd words per token -- chunk word w of the slab is row jj = w / (hg*rd), head hh
+// and word q of the remainder, from slice word (hh*tj + jj)*rd + q.
+template <bool NT>
+__device__ __forceinline__ void hm_lds_gather_heads(uint32_t *lds, const uint8_t *block, uint8_t *chunk_tile,
+                                                    uint32_t s0, uint32_t s1, uint32_t n_tok, uint32_t lane,
+                                                    const Launch &a)
+{
+    constexpr int U = KVX_HM_LDS_UNROLL;
+    const uint32_t H = a.hm_heads, rd = a.hm_rd, hg = a.hm_hg[0], tj = a.hm_htj[0], bs = a.block_size;
+    const uint32_t run = tj * rd, grp = hg * rd, n_tr = (n_tok + tj - 1) / tj;
+    const gword *const pool = (const gword *)block;
+    gword *const chunk = (gword *)chunk_tile;
+    for (uint32_t sl = s0; sl < s1; ++sl) {
+        const uint32_t g = sl / n_tr, j0 = (sl - g * n_tr) * tj, h0 = g * hg;
+        const uint32_t t = min32(tj, n_tok - j0);
+        const uint32_t words = hg * run;
+        for (uint32_t w = lane; w < words; w += 64u * U) {
+            uint32_t pw[U], x[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t ww = w + 64u * u;
+                const uint32_t hh = mdiv(ww, a.hm_m_hrun[0]);
+                const uint32_t i = ww - hh * run;
+                ok[u] = ww < words && mdiv(i, a.hm_m_rd) < t;
+                pw[u] = ((h0 + hh) * bs + j0) * rd + i;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) x[u] = ld_word<NT>(pool + pw[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) lds[w + 64u * u] = x[u];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t out_words = t * grp;
+        for (uint32_t w = lane; w < out_words; w += 64u * U) {
+            uint32_t cw[U], lw[U], x[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t ww = w + 64u * u;
+                const uint32_t jj = mdiv(ww, a.hm_m_hgrp[0]);
+                const uint32_t rem = ww - jj * grp;
+                const uint32_t hh = mdiv(rem, a.hm_m_rd);
+                ok[u] = ww < out_words;
+                cw[u] = ((j0 + jj) * H + h0) * rd + rem;
+                lw[u] = (hh * tj + jj) * rd + (rem - hh * rd);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) x[u] = lds[lw[u]];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) st_word<NT>(chunk + cw[u], x[u]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <int DIR, int LAYOUT, int PAGE, bool NT, bool SEG>
 __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 {
@@ -481,12 +612,21 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         uint32_t first, count;
         uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
         uint8_t *chunk_tile = a.chunk_base + t.chunk_off;
-        if constexpr (PAGE == KVX_PAGE_HM_LDS) {
+        if constexpr (PAGE == KVX_PAGE_HM_LDS || PAGE == KVX_PAGE_HM_LDS_HEADS) {
             // parts of a split tile are ranges of slabs
             __shared__ __attribute__((aligned(16))) uint32_t slices[kWavesPerBlock][KVX_HM_LDS_SLICE / 4];
             const uint32_t n_tok = t.nbytes / a.tok;
-            part_range((n_tok + a.hm_tj - 1) / a.hm_tj, (uint32_t)(item & ((1 << shift) - 1)), 1u << shift,
-                       &first, &count);
+            const uint32_t part = (uint32_t)(item & ((1 << shift) - 1));
+            if (PAGE == KVX_PAGE_HM_LDS_HEADS) {  // head-group slabs
+                part_range(hm_lds_slabs(n_tok, a.hm_heads, a.hm_hg[DIR], a.hm_htj[DIR]), part, 1u << shift,
+                           &first, &count);
+                if (DIR == KV_GATHER)
+                    hm_lds_gather_heads<NT>(slices[wave], block, chunk_tile, first, first + count, n_tok, lane, a);
+                else
+                    hm_lds_scatter_heads<NT>(slices[wave], block, chunk_tile, first, first + count, n_tok, lane, a);
+                continue;
+            }
+            part_range((n_tok + a.hm_tj - 1) / a.hm_tj, part, 1u << shift, &first, &count);
             copy_head_major_lds<DIR, NT>(slices[wave], block, chunk_tile, first, first + count, n_tok, lane, a);
             continue;
         }
@@ -530,9 +670,11 @@ static const void *pick_policy(const Launch &a)
 template <int DIR, int LAYOUT>
 static const void *pick_page(const Launch &a)
 {
-    if (a.page_layout == KV_PAGE_HEAD_MAJOR)
+    if (a.page_layout == KV_PAGE_HEAD_MAJOR) {
+        if (a.hm_lds && a.hm_hg[DIR]) return pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS_HEADS>(a);
         return a.hm_lds ? pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS>(a)
                         : pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a);
+    }
     return pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
 }
 

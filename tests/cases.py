@@ -122,10 +122,13 @@ def staging_for(chunks: dict, fill: int | None = None, rng: np.random.Generator 
 # in 8 KiB slabs of all heads x tokens: a whole page; tokens cut to whole pool lines
 # (20 x 12-byte rows: 34 fit, 32 taken, pages of 64; 16 x 24-byte rows: 21 fit, 16
 # taken); too few for a whole line (4 x 100-byte rows: 20 fit, 32 would be needed);
-# one token (64 x 100-byte rows).
+# one token (64 x 100-byte rows).  Where a token slab would split pool lines (100 x
+# 12-byte rows: 6 tokens fit, 32 would be needed; 128 x 8-byte rows: 8 fit, 16
+# needed), scatter takes slabs of whole pages of a group of heads (25 of 100, 32 of
+# 128), and so does gather where the group's chunk runs are whole lines (32 x 8 bytes).
 HM_LDS_SHAPES = [(4, 2, 2, 16), (2, 4, 2, 16), (4, 6, 2, 8), (8, 8, 1, 16), (4, 10, 2, 32), (2, 12, 2, 64),
                  (16, 12, 2, 64), (20, 3, 4, 64), (64, 100, 1, 4), (2, 1, 8, 16), (128, 8, 1, 32),
-                 (4, 100, 1, 128)]
+                 (4, 100, 1, 128), (100, 6, 2, 16)]
 
 
 def head_major_case(rng: np.random.Generator, H: int, D: int, E: int, bs: int):

@@ -183,6 +183,90 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
                     continue;
                 }
                 uint32_t first, count;
+                if (a.page_layout == KV_PAGE_HEAD_MAJOR && a.hm_lds && a.hm_hg[direction]) {
+                    // the kernel's head-group slabs, lane by lane and phase by phase; the
+                    // slice holds a slab in pool order, the chunk side is walked in chunk order
+                    const uint32_t n_tok = t.nbytes / a.tok, H = a.hm_heads, rd = a.hm_rd, bs = a.block_size;
+                    const uint32_t hg = a.hm_hg[direction], tj = a.hm_htj[direction], run = tj * rd, grp = hg * rd;
+                    const int64_t page_words = (int64_t)H * bs * rd;
+                    if (tj == 0 || H % hg || (int64_t)hg * run * 4 > KVX_HM_LDS_SLICE ||
+                        poff + page_words * 4 > region_bytes[t.region]) {
+                        ++*violations;
+                        continue;
+                    }
+                    const uint32_t n_tr = (n_tok + tj - 1) / tj;
+                    kvx::part_range(kvx::hm_lds_slabs(n_tok, H, hg, tj), (uint32_t)(item % split), split, &first,
+                                    &count);
+                    uint8_t *block = static_cast<uint8_t *>(d->bases[t.region]) + poff;
+                    uint8_t *tile_p = a.chunk_base + t.chunk_off;
+                    const uint32_t U = KVX_HM_LDS_UNROLL;
+                    auto mark = [&](int64_t word) {  // chunk-order word of this tile
+                        const uint64_t bit = (uint64_t)(tile * twords + word);
+                        if (wwritten[bit / 64] >> (bit % 64) & 1u) ++*violations;
+                        wwritten[bit / 64] |= 1ull << (bit % 64);
+                    };
+                    for (uint32_t sl = first; sl < first + count; ++sl) {
+                        ++gen;
+                        const uint32_t gi = sl / n_tr, j0 = (sl - gi * n_tr) * tj, h0 = gi * hg;
+                        const uint32_t tt = std::min(tj, n_tok - j0), c_words = tt * grp, p_words = hg * run;
+                        // pool side: slice word w <-> pool word ((h0 + hh)*bs + j0)*rd + i
+                        auto pool_side = [&](bool load) {
+                            for (uint32_t lane = 0; lane < 64; ++lane)
+                                for (uint32_t w = lane; w < p_words; w += 64u * U)
+                                    for (uint32_t u = 0; u < U; ++u) {
+                                        const uint32_t ww = w + 64u * u;
+                                        const uint32_t hh = kvx::mdiv(ww, a.hm_m_hrun[direction]);
+                                        const uint32_t i = ww - hh * run;
+                                        const uint32_t jj = kvx::mdiv(i, a.hm_m_rd);
+                                        if (!(ww < p_words && jj < tt)) continue;
+                                        if (hh != ww / run || jj != i / rd) { ++*violations; continue; }
+                                        const int64_t pw = ((int64_t)(h0 + hh) * bs + j0) * rd + i;
+                                        if (pw >= page_words || ww * 4ll >= KVX_HM_LDS_SLICE) { ++*violations; continue; }
+                                        if (load) {
+                                            if (tag[ww] == gen) ++*violations;
+                                            if (copy) std::memcpy(&slice[ww], block + pw * 4, 4);
+                                            tag[ww] = gen;
+                                        } else {
+                                            if (tag[ww] != gen) { ++*violations; continue; }  // stale slice word
+                                            if (copy) std::memcpy(block + pw * 4, &slice[ww], 4);
+                                            mark(((int64_t)(j0 + jj) * H + h0 + hh) * rd + (i - jj * rd));
+                                        }
+                                    }
+                        };
+                        // chunk side: chunk word ((j0 + jj)*H + h0)*rd + rem <-> slice word (hh*tj + jj)*rd + q
+                        auto chunk_side = [&](bool load) {
+                            for (uint32_t lane = 0; lane < 64; ++lane)
+                                for (uint32_t w = lane; w < c_words; w += 64u * U)
+                                    for (uint32_t u = 0; u < U; ++u) {
+                                        const uint32_t ww = w + 64u * u;
+                                        if (ww >= c_words) continue;
+                                        const uint32_t jj = kvx::mdiv(ww, a.hm_m_hgrp[direction]);
+                                        const uint32_t rem = ww - jj * grp;
+                                        const uint32_t hh = kvx::mdiv(rem, a.hm_m_rd);
+                                        if (jj != ww / grp || hh != rem / rd) { ++*violations; continue; }
+                                        const int64_t cw = ((int64_t)(j0 + jj) * H + h0) * rd + rem;
+                                        const int64_t lw = ((int64_t)hh * tj + jj) * rd + (rem - hh * rd);
+                                        if (cw * 4 + 4 > (int64_t)t.nbytes || t.chunk_off + cw * 4 + 4 > staging_bytes ||
+                                            lw * 4 >= KVX_HM_LDS_SLICE) {
+                                            ++*violations;
+                                            continue;
+                                        }
+                                        if (load) {
+                                            if (tag[lw] == gen) ++*violations;
+                                            if (copy) std::memcpy(&slice[lw], tile_p + cw * 4, 4);
+                                            tag[lw] = gen;
+                                        } else {
+                                            if (tag[lw] != gen) { ++*violations; continue; }
+                                            if (copy) std::memcpy(tile_p + cw * 4, &slice[lw], 4);
+                                            mark(cw);
+                                        }
+                                    }
+                        };
+                        if (direction == KV_GATHER) pool_side(true), chunk_side(false);
+                        else chunk_side(true), pool_side(false);
+                    }
+                    continue;
+                }
                 if (a.page_layout == KV_PAGE_HEAD_MAJOR && a.hm_lds) {
                     // the kernel's LDS slab walk, lane by lane and phase by phase (lanes
                     // of one phase touch distinct slice words, so their order is free)

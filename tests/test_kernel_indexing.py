@@ -279,7 +279,7 @@ def test_emulated_head_major_blocks_match_oracle(emu, seed):
 LDS_SHAPES = cases.HM_LDS_SHAPES
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(26))
 def test_emulated_head_major_lds_matches_oracle(emu, seed):
     """Head-major pages whose rows are not whole 16-byte vectors take the LDS slab walk
     (the kernel's lanes, magic-multiply divisions and slice indices replayed on the CPU):
@@ -289,7 +289,7 @@ def test_emulated_head_major_lds_matches_oracle(emu, seed):
     _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(13))
 def test_emulated_head_major_lds_split_match_oracle(emu_split, seed):
     """The same with tiles split between waves (parts are ranges of slabs)."""
     rng = np.random.default_rng(36_000 + seed)
