@@ -403,6 +403,21 @@ __host__ __device__ constexpr uint32_t gather_seg_bytes(int dir, uint32_t page_l
                : 0u;
 }
 
+// Vectors per lane per group of the segment walk: the pieces a segment cuts from the
+// tiles are multiples of gcd(tile_bytes, seg_bytes), and groups that divide them keep
+// every piece in whole pipelined groups (a 4 KiB piece in 8 KiB groups is a tail copy
+// without overlap): 8 (8 KiB) when that gcd allows, else 4, else 2.
+__host__ __device__ inline int gather_seg_unroll(int64_t tile_bytes, int64_t seg_bytes)
+{
+    int64_t g = seg_bytes, r = tile_bytes;
+    while (r) {
+        const int64_t t = g % r;
+        g = r;
+        r = t;
+    }
+    return g % 8192 == 0 ? 8 : g % 4096 == 0 ? 4 : 2;
+}
+
 // Work items of a call: segments of the tiles laid end to end at a tile_bytes pitch,
 // or tiles times their parts.
 __host__ __device__ inline int64_t work_items(const Launch &a)

@@ -194,11 +194,11 @@ __device__ __forceinline__ void copy_loop(const S &src, const D &dst, uint32_t n
 // stores carry nt + sc1: measured on MI355X, sequential stores with that policy
 // raise gather by 2-4 % over plain nontemporal stores (the scattered stores of
 // scatter show no such gain, so scatter keeps plain nontemporal accesses).
-template <bool NT>
+template <bool NT, int U = KVX_GATHER_UNROLL>
 __device__ __forceinline__ void gather_tile(const uint8_t *pool, uint8_t *chunk, uint32_t nvec,
                                             uint32_t lane)
 {
-    copy_loop<KVX_GATHER_UNROLL>(BufSide<kGatherPoolPol<NT>>(pool, nvec * 16u),
+    copy_loop<U>(BufSide<kGatherPoolPol<NT>>(pool, nvec * 16u),
                                  BufSide<kGatherChunkPol<NT>>(chunk, nvec * 16u), nvec, lane,
                                  KVX_GATHER_PIPELINE);
 }
@@ -555,7 +555,9 @@ __device__ __forceinline__ void hm_lds_gather_heads(uint32_t *lds, const uint8_t
     }
 }
 
-template <int DIR, int LAYOUT, int PAGE, bool NT, bool SEG>
+// SEG = 0: the tile walk; SEG = 2, 4 or 8: the segment walk (gather of token-major
+// pages), in groups of SEG vectors per lane (gather_seg_unroll).
+template <int DIR, int LAYOUT, int PAGE, bool NT, int SEG>
 __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -586,8 +588,8 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
                     continue;
                 }
                 const uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
-                gather_tile<NT>(block + lo, a.chunk_base + t.chunk_off + lo, (uint32_t)((hi - lo) >> 4),
-                                lane);
+                gather_tile<NT, (SEG > 0 ? SEG : 1)>(block + lo, a.chunk_base + t.chunk_off + lo,
+                                                    (uint32_t)((hi - lo) >> 4), lane);
             }
         }
         return;
@@ -651,14 +653,21 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     }
 }
 
-// Segment walks are a separate instantiation so that the tile walk keeps its own
-// register allocation.
+// Segment walks are separate instantiations, one per group size, so that the tile
+// walk keeps its own register allocation.
 template <int DIR, int LAYOUT, int PAGE, bool NT>
 static const void *pick_walk(const Launch &a)
 {
-    if (DIR == KV_GATHER && PAGE == KV_PAGE_TOKEN_MAJOR && a.seg_bytes)
-        return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, DIR == KV_GATHER && PAGE == KV_PAGE_TOKEN_MAJOR>;
-    return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, false>;
+    if constexpr (DIR == KV_GATHER && PAGE == KV_PAGE_TOKEN_MAJOR) {
+        if (a.seg_bytes) {
+            switch (gather_seg_unroll(a.tile_bytes, a.seg_bytes)) {
+            case 2: return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, 2>;
+            case 4: return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, 4>;
+            default: return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, 8>;
+            }
+        }
+    }
+    return (const void *)&tile_copy<DIR, LAYOUT, PAGE, NT, 0>;
 }
 
 template <int DIR, int LAYOUT, int PAGE>
