@@ -539,3 +539,18 @@ extern "C" int64_t emu_arena(int64_t size, const int64_t *sizes, int64_t n_calls
     }
     return violations;
 }
+
+// The launch-shape rules of the library's host preparation, for direct checks.
+extern "C" int emu_gather_seg_unroll(int64_t tile_bytes, int64_t seg_bytes)
+{
+    return kvx::gather_seg_unroll(tile_bytes, seg_bytes);
+}
+extern "C" uint32_t emu_hm_lds_tokens(int64_t row, int64_t tok, uint32_t block_size)
+{
+    return kvx::hm_lds_tokens(row, tok, block_size);
+}
+extern "C" void emu_hm_lds_head_slab(int dir, uint32_t heads, int64_t row, int64_t tok, uint32_t block_size,
+                                     uint32_t *hg, uint32_t *tj)
+{
+    kvx::hm_lds_head_slab(dir, heads, row, tok, block_size, hg, tj);
+}

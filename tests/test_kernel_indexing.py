@@ -39,6 +39,13 @@ def _build_emu(tmp_path_factory, defines=()):
                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.emu_arena.restype = ctypes.c_int64
     lib.emu_arena.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
+    lib.emu_gather_seg_unroll.restype = ctypes.c_int
+    lib.emu_gather_seg_unroll.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    lib.emu_hm_lds_tokens.restype = ctypes.c_uint32
+    lib.emu_hm_lds_tokens.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32]
+    lib.emu_hm_lds_head_slab.restype = None
+    lib.emu_hm_lds_head_slab.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32,
+                                         ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
     lib.emu_dma.restype = ctypes.c_int
     lib.emu_dma.argtypes = [ctypes.c_int, ctypes.POINTER(K.kv_pool_desc), ctypes.POINTER(K.kv_span),
                             ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.c_void_p, ctypes.c_int64,
@@ -295,6 +302,45 @@ def test_emulated_head_major_lds_split_match_oracle(emu_split, seed):
     rng = np.random.default_rng(36_000 + seed)
     pool, spans, chunks = cases.head_major_case(rng, *LDS_SHAPES[seed % len(LDS_SHAPES)])
     _copy_case(emu_split, pool, spans, chunks, seed)
+
+
+@pytest.mark.parametrize("tile_kib,unroll", [(36, 4), (28, 4), (24, 8), (40, 8), (72, 8), (18, 2), (20, 4)])
+def test_segment_group_size(emu, tile_kib, unroll):
+    """The segment walk's group size is the largest of 8, 4, 2 KiB dividing the pieces a
+    32 KiB segment cuts from the tiles, i.e. gcd(tile, 32 KiB)."""
+    assert emu.emu_gather_seg_unroll(tile_kib * 1024, 32768) == unroll
+
+
+@pytest.mark.parametrize("row,heads,bs,tj", [
+    (24, 16, 64, 16),    # 21 tokens fit; 16 make 384-byte (whole-line) head runs
+    (12, 20, 64, 32),    # 34 fit; 32 make 384 bytes
+    (100, 4, 128, 20),   # 20 fit; whole lines need 32, so all 20
+    (8, 32, 16, 16),     # a whole page fits
+    (100, 64, 4, 1),     # one token
+])
+def test_lds_slab_tokens(emu, row, heads, bs, tj):
+    got = emu.emu_hm_lds_tokens(row, row * heads, bs)
+    assert got == tj
+    assert got * row * heads <= 8192 and 1 <= got <= bs
+
+
+@pytest.mark.parametrize("row,heads,bs,gather,scatter", [
+    (24, 16, 64, (0, 16), (0, 16)),      # token slabs of whole lines in both directions
+    (12, 100, 16, (0, 6), (25, 16)),     # scatter: 25 heads x whole pages; gather keeps tokens
+    (8, 128, 32, (32, 32), (32, 32)),    # both: 32 heads x 8 bytes = 256-byte chunk runs
+    (100, 4, 128, (0, 20), (1, 64)),     # scatter: one head, 64 of its 128 rows (50 lines)
+    (100, 64, 4, (0, 1), (16, 4)),       # scatter: 20 pages fit, 16 divides 64
+])
+def test_lds_head_group_slabs(emu, row, heads, bs, gather, scatter):
+    """Where token slabs would split pool lines, scatter takes whole pages of a head
+    group (the largest divisor of H that fits, or one head and part of its page) and
+    gather does so only when the group's chunk runs are whole 128-byte lines."""
+    hg, tj = ctypes.c_uint32(), ctypes.c_uint32()
+    for d, want in ((K.KV_GATHER, gather), (K.KV_SCATTER, scatter)):
+        emu.emu_hm_lds_head_slab(d, heads, row, row * heads, bs, ctypes.byref(hg), ctypes.byref(tj))
+        assert (hg.value, tj.value) == want, (d, hg.value, tj.value)
+        if hg.value:
+            assert heads % hg.value == 0 and hg.value * tj.value * row <= 8192
 
 
 def test_magic_division_is_exact():
