@@ -746,13 +746,15 @@ def pipeline_leg(args, dev):
         torch.cuda.empty_cache()
 
 
-def traffic_for(achieved_bytes_per_launch):
+def traffic_for(algorithmic_bytes_per_launch):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source."""
+    taken on the current kernel source and on launches of the same algorithmic size."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     t = json.load(open(TRAFFIC_FILE))
     if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if t.get("algorithmic_bytes_per_launch") != algorithmic_bytes_per_launch:
         return None
     return t.get("bytes_per_launch")
 
