@@ -252,9 +252,13 @@ __device__ __forceinline__ void copy_head_major(gvec *__restrict__ block, uint8_
         }
         u32x4 r[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (v + 64u * u < end)
-                r[u] = DIR == KV_GATHER ? ld_hm_pool<NT>(block + pv[u]) : in.load(v + 64u * u);
+        for (int u = 0; u < U; ++u) {
+            // lanes past the end load a valid vector that is not stored (no load behind a
+            // lane-dependent branch, which would wait for all earlier loads)
+            const bool in_range = v + 64u * u < end;
+            r[u] = DIR == KV_GATHER ? ld_hm_pool<NT>(block + (in_range ? pv[u] : 0u))
+                                    : in.load(in_range ? v + 64u * u : end - 1u);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (v + 64u * u < end) {
@@ -398,9 +402,10 @@ __device__ __forceinline__ void copy_head_major_lds(uint32_t *lds, uint8_t *bloc
                 lw[u] = (jj * H + h) * rd + (i - jj * rd);
             }
             if (DIR == KV_GATHER) {
+                // every lane loads (word 0 of the block where it has nothing to move): a
+                // load behind a lane-dependent branch would wait for all earlier ones
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (ok[u]) x[u] = ld_word<NT>(pool + pw[u]);
+                for (int u = 0; u < U; ++u) x[u] = ld_word<NT>(pool + (ok[u] ? pw[u] : 0u));
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     if (ok[u]) lds[lw[u]] = x[u];
