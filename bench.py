@@ -206,6 +206,33 @@ def hbm_leg(args, dev):
                              kernel_ms_median=float(np.median(each)), kernel_ms_min=float(each.min()),
                              kernel_ms_max=float(each.max()), launches=n)
 
+    # The same call with each request's pages in the blocks the library's allocator
+    # hands a fresh pool (lowest free ids first, so consecutive runs) instead of the
+    # workload's shuffled table: what a reload writes into an unfragmented pool.
+    alloc_order = {}
+    lens = [t.size for t in w["block_tables"]]
+    if args.others and sum(lens) <= pool["num_blocks"]:
+        ids = K.kv_pool_alloc_blocks(P.h, sum(lens))
+        offs = np.cumsum([0] + lens)
+        tabs_a = [torch.from_numpy(np.ascontiguousarray(ids[offs[i]:offs[i + 1]])).to(dev)
+                  for i in range(len(lens))]
+        spans_a = K.make_spans([(tb, tb.numel(), t0, t1, fc) for tb, (t0, t1), fc in
+                                zip(tabs_a, w["requests"], plan["first_chunk"])])
+        for name, fn in (("gather", K.kv_gather_chunks), ("scatter", K.kv_scatter_chunks)):
+            fn(P.h, spans_a, spec, stream)
+            K.kv_pool_timing_start(P.h)
+            for _ in range(max(3, args.steps // 2)):
+                fn(P.h, spans_a, spec, stream)
+            each = K.kv_pool_timing_read_each(P.h)
+            alloc_order[name] = dict(kernel_ms_median=round(float(np.median(each)), 4),
+                                     hbm_frac=round(2 * payload / (float(np.median(each)) * 1e-3) / 1e9
+                                                    / HBM_PEAK_GBS, 4))
+        assert K.kv_pool_get_error(P.h, stream) == 0
+        K.kv_pool_free_blocks(P.h, ids)
+        del tabs_a
+        log("allocator-ordered blocks: gather %.1f%%, scatter %.1f%% of HBM peak" % (
+            100 * alloc_order["gather"]["hbm_frac"], 100 * alloc_order["scatter"]["hbm_frac"]))
+
     # the conventional engine on the same call: one hipMemcpyAsync per tile
     dma = {}
     if args.dma_baseline:
@@ -252,7 +279,7 @@ def hbm_leg(args, dev):
         payload=payload, ms_per_step=ms_per_step, kernel_ms_avg=kern_ms / launches, launches=launches,
         value=2 * payload / (ms_per_step * 1e-3) / 1e9,
         achieved=2 * payload / avg_kernel_s / 1e9, per_dir=per_dir, parity=parity,
-        d2d_copy_gbs=d2d_gbs, dma=dma, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
+        d2d_copy_gbs=d2d_gbs, dma=dma, alloc_order=alloc_order, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
         name=args.workload)
     # keep host copies for the CPU baseline (first layers), then free the device
     res["host_sample"] = None
@@ -773,7 +800,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-layers", type=int, default=32)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--no-other-workloads", dest="others", action="store_false")
+    ap.add_argument("--no-other-workloads", dest="others", action="store_false",
+                    help="skip the other workloads and the allocator-ordered table")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--no-pipeline", dest="pipeline", action="store_false",
                     help="skip the layer-pipelined reload measurement")
@@ -844,6 +872,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res["per_dir"].items()},
         "d2d_memcpy_gbs": round(res["d2d_copy_gbs"], 1),
+        "allocator_ordered_blocks": res["alloc_order"],
         "per_tile_dma": res["dma"],
         "parity": res["parity"],
         "host_path": host,
