@@ -74,6 +74,16 @@
  * Transfers are asynchronous on the given stream (0 = the null stream): the
  * caller keeps every buffer alive and unmodified until the stream has passed
  * the call.  Handles are not thread-safe.
+ * The caller's buffers must hold what the call declares: each region
+ * (num_blocks - 1) * block_stride + block_size * tok bytes, the staging area
+ * n_slots * slot_bytes, each device block table table_len entries.  Where the
+ * HIP runtime knows the allocation holding such a pointer (hipMalloc'd device
+ * memory, hipHostMalloc'd or registered host memory), a
+ * transfer whose declared extent runs past the end of that allocation is
+ * refused with KV_ERR_RANGE before anything is enqueued (an access past an
+ * allocation would fault the GPU); memory the runtime does not know is taken
+ * on trust.  A sub-allocator's block (e.g. a torch tensor) is checked against
+ * the runtime allocation it lies in, not against its own size.
  */
 #ifndef KVXFER_H
 #define KVXFER_H
@@ -91,7 +101,7 @@ extern "C" {
 #define KV_OK 0
 #define KV_ERR_ARG (-1)    /* null pointer, bad shape, empty or inverted range */
 #define KV_ERR_ALIGN (-2)  /* pointer, stride, slot size or token size not a multiple of 16 */
-#define KV_ERR_RANGE (-3)  /* span past its block table, slot too small, block id out of range */
+#define KV_ERR_RANGE (-3)  /* span past its block table, slot too small, block id out of range, buffer past its allocation */
 #define KV_ERR_OOM (-4)    /* allocator exhausted, or a host/device allocation failed */
 #define KV_ERR_RING (-5)   /* two chunks of one call share a staging slot */
 #define KV_ERR_HIP (-6)    /* a HIP runtime call failed (no device, launch failure, ...) */
@@ -155,7 +165,7 @@ typedef struct {
 
 typedef struct {
     const int32_t *block_table; /* device array (host array for kv_validate_targets) */
-    int64_t table_len;          /* entries in block_table; >= ceil(t_end / block_size) */
+    int64_t table_len;          /* entries in block_table; >= ceil(t_end / block_size), < 2^31 */
     int64_t t_begin;            /* first token, a multiple of block_size, >= 0 */
     int64_t t_end;              /* one past the last token, >= t_begin (an empty span moves nothing) */
     int64_t first_chunk;        /* chunk index of the span's first chunk, >= 0 */
@@ -218,7 +228,8 @@ KV_API int kv_pool_free_count(const kv_pool *pool, int64_t *out);
 
 /* Host-only dry run: validates a prospective call exactly as kv_gather_chunks /
  * kv_scatter_chunks do (shapes, alignment, span ranges, slot sizes, one slot per
- * chunk) and reports its sizes.  Makes no HIP call; info may be NULL. */
+ * chunk) and reports its sizes.  Makes no HIP call, so the allocation-extent
+ * checks (Conventions above) are left to the transfer itself; info may be NULL. */
 KV_API int kv_check_transfer(const kv_pool_desc *desc, const kv_span *spans, int32_t n_spans,
                       const kv_chunk_spec *spec, kv_transfer_info *info);
 

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -152,7 +153,7 @@ int validate_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
         }
         if (!sp.block_table) return KV_ERR_ARG;
         if (sp.t_end / bs >= kMaxU31) return KV_ERR_RANGE;
-        if (sp.table_len < cdiv(sp.t_end, bs)) return KV_ERR_RANGE;
+        if (sp.table_len < cdiv(sp.t_end, bs) || sp.table_len > kMaxU31) return KV_ERR_RANGE;
         p.n_pages = cdiv(len, bs);
         p.ppc = std::min<int64_t>(s->chunk_tokens / bs, p.n_pages);
         p.n_tc = cdiv(p.n_pages, p.ppc);
@@ -287,6 +288,14 @@ int prepare_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
 
 }  // namespace kvx
 
+// End addresses of the allocations holding recently seen pointers, as the HIP
+// runtime reports them: a small direct-mapped table keyed by pointer.
+struct ExtentCache {
+    static constexpr int kEntries = 128;
+    const void *key[kEntries] = {};
+    uintptr_t end[kEntries] = {};
+};
+
 struct kv_pool {
     kv_pool_desc desc;
     std::vector<void *> bases;
@@ -310,6 +319,10 @@ struct kv_pool {
     // staging-memory kind of the last staging base seen
     const void *last_base = nullptr;
     bool last_base_host = false;
+    // allocation ends of the regions, staging bases and block tables seen (see
+    // check_buffers); the regions are checked until they have passed once
+    ExtentCache extents;
+    bool regions_ok = false;
     // timing
     bool timing = false;
     int n_timed = 0;
@@ -443,6 +456,64 @@ bool staging_in_host_memory(kv_pool *p, const void *base)
     return p->last_base_host;
 }
 
+// The kernels and copies trust the extents a call declares: num_blocks blocks per
+// region, n_slots * slot_bytes of staging, table_len entries per block table.  An
+// access past the end of an allocation faults the GPU, so where the HIP runtime
+// knows the allocation holding a pointer (device memory, hipHostMalloc'd
+// or registered host memory) a declared extent that runs past its end is refused
+// before anything is enqueued.  Memory the runtime does not know (pageable host
+// memory, other allocators) is taken on trust.
+
+// End of the allocation holding q, or 0 when the runtime does not know q.
+uintptr_t alloc_end(const void *q)
+{
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(q)) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return reinterpret_cast<uintptr_t>(base) + size;
+}
+
+// KV_OK when [q, q + bytes) lies inside the allocation holding q, or the runtime
+// does not know q; else KV_ERR_RANGE.  A cached end that covers the range is
+// trusted; anything else is looked up again first (an allocation freed and made
+// again at the same address may have grown).
+int check_extent(ExtentCache &c, const void *q, int64_t bytes)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(q);
+    const uintptr_t need = a + (uintptr_t)bytes;
+    const int i = (int)(((a >> 9) ^ (a >> 21)) % ExtentCache::kEntries);
+    if (c.key[i] == q && c.end[i] >= need) return KV_OK;
+    const uintptr_t end = alloc_end(q);
+    c.key[i] = q;
+    c.end[i] = end ? end : UINTPTR_MAX;
+    return end && end < need ? KV_ERR_RANGE : KV_OK;
+}
+
+// Extents of a validated call: every region (until they have passed once), the
+// staging area, and, when the tables are device memory, each span's block table.
+int check_buffers(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
+                  bool device_tables)
+{
+    const kv_pool_desc &d = p->desc;
+    if (!p->regions_ok) {
+        const int64_t extent = (int64_t)(d.num_blocks - 1) * d.block_stride + tok_bytes(&d) * d.block_size;
+        for (void *b : p->bases)
+            if (check_extent(p->extents, b, extent)) return KV_ERR_RANGE;
+        p->regions_ok = true;
+    }
+    if (check_extent(p->extents, spec->base, spec->n_slots * spec->slot_bytes)) return KV_ERR_RANGE;
+    if (device_tables)
+        for (int32_t i = 0; i < n_spans; ++i) {
+            if (spans[i].t_end == spans[i].t_begin) continue;
+            if (check_extent(p->extents, spans[i].block_table, spans[i].table_len * (int64_t)sizeof(int32_t)))
+                return KV_ERR_RANGE;
+        }
+    return KV_OK;
+}
+
 int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
              hipStream_t stream, int direction)
 {
@@ -452,6 +523,8 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
     if (rc) return rc;
     if (info.tiles == 0) return KV_OK;
+    rc = check_buffers(p, spans, n_spans, spec, true);
+    if (rc) return rc;
     rc = device_setup(p);
     if (rc) return rc;
     if (spec->flags & KV_FLAG_VALIDATE) {
@@ -511,6 +584,8 @@ int transfer_dma(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chu
     int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
     if (rc) return rc;
     if (info.tiles == 0) return KV_OK;
+    rc = check_buffers(p, spans, n_spans, spec, false);
+    if (rc) return rc;
     std::vector<const int32_t *> tables(n_spans);
     for (int32_t i = 0; i < n_spans; ++i) tables[i] = spans[i].block_table;
     rc = kv_validate_targets(&p->desc, spans, n_spans, tables.data(), direction);
@@ -879,7 +954,7 @@ const char *kv_strerror(int code)
     case KV_OK: return "ok";
     case KV_ERR_ARG: return "invalid argument";
     case KV_ERR_ALIGN: return "pointer, stride, slot size or token size not 16-byte aligned";
-    case KV_ERR_RANGE: return "out of range (table length, slot size or block id)";
+    case KV_ERR_RANGE: return "out of range (table length, slot size, block id, or a buffer past its allocation)";
     case KV_ERR_OOM: return "out of memory or blocks";
     case KV_ERR_RING: return "two chunks of one call share a staging slot";
     case KV_ERR_HIP: return "HIP runtime error";

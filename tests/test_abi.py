@@ -144,6 +144,7 @@ CALL_CASES = [
     (dict(base=0), [_span()], K.KV_ERR_ARG),
     (dict(base=FAKE + 4), [_span()], K.KV_ERR_ALIGN),
     (dict(slot_bytes=256 * 1024 - 16), [_span()], K.KV_ERR_RANGE),  # chunk does not fit
+    (dict(), [_span(n=1 << 31)], K.KV_ERR_RANGE),   # declared table length past the 31-bit limit
     (dict(slot_bytes=256 * 1024 + 8), [_span()], K.KV_ERR_ALIGN),
     (dict(n_slots=0), [_span()], K.KV_ERR_ARG),
     (dict(max_workgroups=-1), [_span()], K.KV_ERR_ARG),
