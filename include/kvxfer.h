@@ -78,12 +78,13 @@
  * (num_blocks - 1) * block_stride + block_size * tok bytes, the staging area
  * n_slots * slot_bytes, each device block table table_len entries.  Where the
  * HIP runtime knows the allocation holding such a pointer (hipMalloc'd device
- * memory, hipHostMalloc'd or registered host memory), a
- * transfer whose declared extent runs past the end of that allocation is
- * refused with KV_ERR_RANGE before anything is enqueued (an access past an
- * allocation would fault the GPU); memory the runtime does not know is taken
- * on trust.  A sub-allocator's block (e.g. a torch tensor) is checked against
- * the runtime allocation it lies in, not against its own size.
+ * memory, hipHostMalloc'd or registered host memory, virtual-memory mappings),
+ * a transfer whose declared extent runs past the end of that allocation and
+ * any allocations adjoining it without a gap is refused with KV_ERR_RANGE
+ * before anything is enqueued (an access past mapped memory would fault the
+ * GPU); memory the runtime does not know is taken on trust.  A sub-allocator's
+ * block (e.g. a torch tensor) is checked against the runtime allocation it lies
+ * in, not against its own size.
  */
 #ifndef KVXFER_H
 #define KVXFER_H

@@ -464,29 +464,47 @@ bool staging_in_host_memory(kv_pool *p, const void *base)
 // before anything is enqueued.  Memory the runtime does not know (pageable host
 // memory, other allocators) is taken on trust.
 
-// End of the allocation holding q, or 0 when the runtime does not know q.
-uintptr_t alloc_end(const void *q)
+// End of the allocation holding q, or 0 when the runtime does not know q.  Memory
+// mapped through the virtual-memory API (hipMemMap) reports each mapping as an
+// allocation of its own.
+uintptr_t alloc_end(uintptr_t q)
 {
     hipDeviceptr_t base = nullptr;
     size_t size = 0;
-    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(q)) != hipSuccess) {
+    if (hipMemGetAddressRange(&base, &size, reinterpret_cast<hipDeviceptr_t>(q)) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
     return reinterpret_cast<uintptr_t>(base) + size;
 }
 
-// KV_OK when [q, q + bytes) lies inside the allocation holding q, or the runtime
-// does not know q; else KV_ERR_RANGE.  A cached end that covers the range is
-// trusted; anything else is looked up again first (an allocation freed and made
-// again at the same address may have grown).
+// How far from q the runtime's allocations reach without a gap, walking from one
+// allocation (or mapping) to the next until `need` is covered: 0 when q itself is
+// unknown, UINTPTR_MAX when the walk is cut short (too many pieces to follow).
+uintptr_t covered_end(uintptr_t q, uintptr_t need)
+{
+    constexpr int kMaxPieces = 1 << 16;
+    uintptr_t cur = q;
+    for (int i = 0; i < kMaxPieces; ++i) {
+        const uintptr_t end = alloc_end(cur);
+        if (end <= cur) return i == 0 ? 0 : cur;   // unknown memory after known pieces
+        if (end >= need) return end;
+        cur = end;
+    }
+    return UINTPTR_MAX;
+}
+
+// KV_OK when [q, q + bytes) lies inside memory the runtime has allocated or mapped
+// without a gap, or the runtime does not know q; else KV_ERR_RANGE.  A cached end
+// that covers the range is trusted; anything else is looked up again first (an
+// allocation freed and made again at the same address may have grown).
 int check_extent(ExtentCache &c, const void *q, int64_t bytes)
 {
     const uintptr_t a = reinterpret_cast<uintptr_t>(q);
     const uintptr_t need = a + (uintptr_t)bytes;
     const int i = (int)(((a >> 9) ^ (a >> 21)) % ExtentCache::kEntries);
     if (c.key[i] == q && c.end[i] >= need) return KV_OK;
-    const uintptr_t end = alloc_end(q);
+    const uintptr_t end = covered_end(a, need);
     c.key[i] = q;
     c.end[i] = end ? end : UINTPTR_MAX;
     return end && end < need ? KV_ERR_RANGE : KV_OK;

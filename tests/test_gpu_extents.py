@@ -29,12 +29,20 @@ TILE = BS * TOK
 
 
 def _alloc_end(ptr: int) -> int:
-    """End address of the runtime allocation holding ptr (a torch block lies inside one)."""
+    """How far the runtime's allocations reach from ptr without a gap (a torch block
+    lies inside one allocation; virtual-memory mappings count one by one), as the
+    library itself walks them."""
     hip = ctypes.CDLL("libamdhip64.so")
-    base, size = ctypes.c_void_p(), ctypes.c_size_t()
-    rc = hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ctypes.c_void_p(ptr))
-    assert rc == 0, "hipMemGetAddressRange failed (%d)" % rc
-    return base.value + size.value
+    cur = ptr
+    for i in range(1 << 16):
+        base, size = ctypes.c_void_p(), ctypes.c_size_t()
+        rc = hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ctypes.c_void_p(cur))
+        if rc != 0:
+            hip.hipGetLastError()
+            assert i > 0, "hipMemGetAddressRange does not know the buffer (%d)" % rc
+            return cur
+        cur = base.value + size.value
+    raise AssertionError("allocations reach too far to follow")
 
 
 def _setup():
@@ -97,6 +105,8 @@ def test_regions_declared_past_their_allocation_are_refused():
     _, pool_t, stg, tab = _setup()
     last = pool_t.data_ptr() + (L * KV - 1) * pool_t.stride(0)
     fits = (_alloc_end(last) - last - TILE) // TILE + 1  # blocks the last region can hold
+    if fits + 1 > 2**31 - 1:
+        pytest.skip("the allocations after the pool reach past a 31-bit block count")
     stream = torch.cuda.current_stream()
     spans = K.make_spans([(tab, 4, 0, BS, 0)])          # block 0 only
     bad = _pool(pool_t, num_blocks=fits + 1)
@@ -120,6 +130,8 @@ def test_regions_declared_past_their_allocation_are_refused():
 def test_block_table_declared_past_its_allocation_is_refused():
     _, pool_t, stg, tab = _setup()
     entries = (_alloc_end(tab.data_ptr()) - tab.data_ptr()) // 4
+    if entries + 1 > 2**31 - 1:
+        pytest.skip("the allocations after the table reach past a 31-bit table length")
     p = _pool(pool_t)
     stream = torch.cuda.current_stream()
     try:
