@@ -288,14 +288,6 @@ int prepare_call(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
 
 }  // namespace kvx
 
-// End addresses of the allocations holding recently seen pointers, as the HIP
-// runtime reports them: a small direct-mapped table keyed by pointer.
-struct ExtentCache {
-    static constexpr int kEntries = 128;
-    const void *key[kEntries] = {};
-    uintptr_t end[kEntries] = {};
-};
-
 struct kv_pool {
     kv_pool_desc desc;
     std::vector<void *> bases;
@@ -321,7 +313,7 @@ struct kv_pool {
     bool last_base_host = false;
     // allocation ends of the regions, staging bases and block tables seen (see
     // check_buffers); the regions are checked until they have passed once
-    ExtentCache extents;
+    kvx::ExtentCache extents;
     bool regions_ok = false;
     // timing
     bool timing = false;
@@ -466,7 +458,7 @@ bool staging_in_host_memory(kv_pool *p, const void *base)
 
 // End of the allocation holding q, or 0 when the runtime does not know q.  Memory
 // mapped through the virtual-memory API (hipMemMap) reports each mapping as an
-// allocation of its own.
+// allocation of its own, which kvx::covered_end walks across.
 uintptr_t alloc_end(uintptr_t q)
 {
     hipDeviceptr_t base = nullptr;
@@ -478,36 +470,9 @@ uintptr_t alloc_end(uintptr_t q)
     return reinterpret_cast<uintptr_t>(base) + size;
 }
 
-// How far from q the runtime's allocations reach without a gap, walking from one
-// allocation (or mapping) to the next until `need` is covered: 0 when q itself is
-// unknown, UINTPTR_MAX when the walk is cut short (too many pieces to follow).
-uintptr_t covered_end(uintptr_t q, uintptr_t need)
+int check_extent(kvx::ExtentCache &c, const void *q, int64_t bytes)
 {
-    constexpr int kMaxPieces = 1 << 16;
-    uintptr_t cur = q;
-    for (int i = 0; i < kMaxPieces; ++i) {
-        const uintptr_t end = alloc_end(cur);
-        if (end <= cur) return i == 0 ? 0 : cur;   // unknown memory after known pieces
-        if (end >= need) return end;
-        cur = end;
-    }
-    return UINTPTR_MAX;
-}
-
-// KV_OK when [q, q + bytes) lies inside memory the runtime has allocated or mapped
-// without a gap, or the runtime does not know q; else KV_ERR_RANGE.  A cached end
-// that covers the range is trusted; anything else is looked up again first (an
-// allocation freed and made again at the same address may have grown).
-int check_extent(ExtentCache &c, const void *q, int64_t bytes)
-{
-    const uintptr_t a = reinterpret_cast<uintptr_t>(q);
-    const uintptr_t need = a + (uintptr_t)bytes;
-    const int i = (int)(((a >> 9) ^ (a >> 21)) % ExtentCache::kEntries);
-    if (c.key[i] == q && c.end[i] >= need) return KV_OK;
-    const uintptr_t end = covered_end(a, need);
-    c.key[i] = q;
-    c.end[i] = end ? end : UINTPTR_MAX;
-    return end && end < need ? KV_ERR_RANGE : KV_OK;
+    return c.covers(q, bytes, alloc_end) ? KV_OK : KV_ERR_RANGE;
 }
 
 // Extents of a validated call: every region (until they have passed once), the

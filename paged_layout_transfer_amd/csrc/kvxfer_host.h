@@ -12,6 +12,52 @@
 
 namespace kvx {
 
+// ---- declared extents against the runtime's allocations (host) ---------------
+
+// How far from address q the allocations the runtime knows reach without a gap,
+// walking from one allocation (or virtual-memory mapping) to the next until `need` is
+// covered.  lookup(a) returns the end of the allocation holding a, or 0 when the
+// runtime does not know a.  Returns 0 when q itself is unknown, the end of the last
+// adjoining allocation otherwise, and UINTPTR_MAX when more than max_pieces would
+// have to be followed (the range is then taken on trust).
+template <class Lookup>
+uintptr_t covered_end(uintptr_t q, uintptr_t need, Lookup lookup, int max_pieces = 1 << 16)
+{
+    uintptr_t cur = q;
+    for (int i = 0; i < max_pieces; ++i) {
+        const uintptr_t end = lookup(cur);
+        if (end <= cur) return i == 0 ? 0 : cur;   // unknown memory after known pieces
+        if (end >= need) return end;
+        cur = end;
+    }
+    return UINTPTR_MAX;
+}
+
+// Ends of the allocations holding recently seen pointers: a small direct-mapped table
+// keyed by pointer, so a call on the same buffers asks the runtime nothing.
+struct ExtentCache {
+    static constexpr int kEntries = 128;
+    const void *key[kEntries] = {};
+    uintptr_t end[kEntries] = {};
+
+    // true when [q, q + bytes) lies inside memory the runtime has allocated or mapped
+    // without a gap, or the runtime does not know q.  A cached end that covers the
+    // range is trusted; anything else is looked up again first (an allocation freed
+    // and made again at the same address may have grown).
+    template <class Lookup>
+    bool covers(const void *q, int64_t bytes, Lookup lookup)
+    {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(q);
+        const uintptr_t need = a + (uintptr_t)bytes;
+        const int i = (int)(((a >> 9) ^ (a >> 21)) % kEntries);
+        if (key[i] == q && end[i] >= need) return true;
+        const uintptr_t e = covered_end(a, need, lookup);
+        key[i] = q;
+        end[i] = e ? e : UINTPTR_MAX;
+        return !(e && e < need);
+    }
+};
+
 // ---- block allocator (host) --------------------------------------------------
 
 // The free blocks of a pool as a bitmap (bit b of word w: block 64w+b is free).

@@ -51,6 +51,13 @@ def _build_emu(tmp_path_factory, defines=()):
                             ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.c_void_p, ctypes.c_int64,
                             ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                             ctypes.POINTER(ctypes.c_int64)]
+    lib.emu_set_allocs.restype = None
+    lib.emu_set_allocs.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    lib.emu_covered_end.restype = ctypes.c_uint64
+    lib.emu_covered_end.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32]
+    lib.emu_cache_reset.restype = None
+    lib.emu_cache_covers.restype = ctypes.c_int32
+    lib.emu_cache_covers.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
     return lib
 
 
@@ -360,3 +367,50 @@ def test_emulated_head_major_blocks_split_match_oracle(emu_split, seed):
     rng = np.random.default_rng(34_000 + seed)
     pool, spans, chunks = cases.head_major_case(rng, *T4_SHAPES[seed % len(T4_SHAPES)])
     _copy_case(emu_split, pool, spans, chunks, seed)
+
+
+# ---- declared extents against a fake allocation table ------------------------------
+
+def _allocs(lib, pieces):
+    bases = np.array([b for b, _ in pieces], dtype=np.uint64)
+    sizes = np.array([n for _, n in pieces], dtype=np.uint64)
+    lib.emu_set_allocs(bases.ctypes.data, sizes.ctypes.data, len(pieces))
+    return bases, sizes   # keep alive
+
+
+def test_extent_walk_follows_adjoining_allocations_and_stops_at_gaps(emu):
+    MB = 1 << 20
+    A = 0x7F0000000000
+    # one 4 MiB allocation; three adjoining 2 MiB mappings; then a gap; then 1 MiB
+    keep = _allocs(emu, [(A, 4 * MB), (A + 16 * MB, 2 * MB), (A + 18 * MB, 2 * MB), (A + 20 * MB, 2 * MB),
+                         (A + 23 * MB, MB)])
+    UMAX = 2**64 - 1
+    assert emu.emu_covered_end(A, A + MB, 1 << 16) == A + 4 * MB                 # inside one allocation
+    assert emu.emu_covered_end(A + MB, A + 4 * MB, 1 << 16) == A + 4 * MB         # ends exactly at its end
+    assert emu.emu_covered_end(A, A + 4 * MB + 1, 1 << 16) == A + 4 * MB          # one byte past: short
+    assert emu.emu_covered_end(A + 17 * MB, A + 22 * MB, 1 << 16) == A + 22 * MB  # across three mappings
+    assert emu.emu_covered_end(A + 17 * MB, A + 23 * MB, 1 << 16) == A + 22 * MB  # the gap stops the walk
+    assert emu.emu_covered_end(A + 8 * MB, A + 9 * MB, 1 << 16) == 0              # unknown memory
+    assert emu.emu_covered_end(A + 16 * MB, A + 22 * MB, 2) == UMAX               # too many pieces: trusted
+    assert emu.emu_covered_end(A + 16 * MB, A + 22 * MB, 3) == A + 22 * MB
+    del keep
+
+
+def test_extent_cache_answers_repeat_calls_and_rechecks_refusals(emu):
+    MB = 1 << 20
+    A = 0x7F0000000000
+    n = ctypes.c_int64()
+    emu.emu_cache_reset()
+    keep = _allocs(emu, [(A, 4 * MB)])
+    assert emu.emu_cache_covers(A, 4 * MB, ctypes.byref(n)) == 1 and n.value == 1
+    assert emu.emu_cache_covers(A, 2 * MB, ctypes.byref(n)) == 1 and n.value == 0    # cached end covers it
+    assert emu.emu_cache_covers(A, 4 * MB + 16, ctypes.byref(n)) == 0 and n.value >= 1
+    # the allocation is made again larger at the same address: a refusal is looked up afresh
+    keep = _allocs(emu, [(A, 8 * MB)])
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1 and n.value >= 1
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1 and n.value == 0
+    # memory the runtime does not know is taken on trust, and remembered as such
+    B = A + 64 * MB
+    assert emu.emu_cache_covers(B, 1 << 40, ctypes.byref(n)) == 1 and n.value == 1
+    assert emu.emu_cache_covers(B, 1 << 40, ctypes.byref(n)) == 1 and n.value == 0
+    del keep
