@@ -516,7 +516,9 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     }
 
     // Span records go to a free stretch of the pinned arena, then one stream-ordered
-    // copy to the same stretch of the device arena.
+    // copy to the same stretch of the device arena; calls with at most
+    // KVX_INLINE_SPANS records pass them in the kernel arguments instead and skip the
+    // copy (their stretch still carries the call's fence event).
     const int64_t rec_bytes = ((int64_t)std::max(1, (int)n_spans) * (int64_t)sizeof(kvx::SpanDev) + 255) & ~255LL;
     int64_t off = 0;
     rc = arena_take(p, rec_bytes, &off);
@@ -528,7 +530,11 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     rc = prepare_with(&p->desc, spans, n_spans, spec, h, &n_rec, &a, &info, p->plans.data(),
                       p->ranges.data());
     if (rc) return rc;
-    if (!HIP_OK(hipMemcpyAsync(dd, h, n_rec * sizeof(kvx::SpanDev), hipMemcpyHostToDevice, stream)))
+    // a few records ride in the kernel arguments; more go to the device arena
+    const bool inline_records = n_rec <= KVX_INLINE_SPANS;
+    if (inline_records)
+        std::memcpy(a.inl, h, n_rec * sizeof(kvx::SpanDev));
+    else if (!HIP_OK(hipMemcpyAsync(dd, h, n_rec * sizeof(kvx::SpanDev), hipMemcpyHostToDevice, stream)))
         return KV_ERR_HIP;
     // From here the copy may be in flight: a failure waits for the stream before
     // returning, so the uncommitted arena stretch is free again.
@@ -537,7 +543,7 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
         return KV_ERR_HIP;
     };
     a.regions = p->d_regions;
-    a.spans = dd;
+    a.spans = inline_records ? nullptr : dd;
     a.err = p->d_err;
 
     a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);

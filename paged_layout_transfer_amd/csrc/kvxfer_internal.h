@@ -127,6 +127,12 @@ struct alignas(64) SpanDev {
 };
 static_assert(sizeof(SpanDev) == 64, "SpanDev must stay 64 bytes");
 
+// Calls with at most this many span records pass them in the kernel arguments
+// (Launch::inl) instead of uploading them to the device arena before the launch.
+#ifndef KVX_INLINE_SPANS
+#define KVX_INLINE_SPANS 4
+#endif
+
 struct Launch {
     uint8_t *const *regions;  // device array [num_layers * num_kv] of region bases
     const SpanDev *spans;     // device array [n_spans]
@@ -174,6 +180,9 @@ struct Launch {
     uint32_t hm_htj[2];
     uint64_t hm_m_hrun[2];
     uint64_t hm_m_hgrp[2];
+    // the span records themselves when n_spans <= KVX_INLINE_SPANS (spans is then
+    // unused): 64-byte SpanDev images, read by the kernel from its argument memory
+    uint64_t inl[KVX_INLINE_SPANS * sizeof(SpanDev) / sizeof(uint64_t)];
 };
 
 // Kernel-internal page layout values: head-major pages staged through LDS in token

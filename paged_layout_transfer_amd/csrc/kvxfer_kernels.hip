@@ -52,6 +52,17 @@ __device__ __forceinline__ const KVX_CONST T *as_const(const T *p)
 }
 __device__ __forceinline__ gvec *as_global(uint8_t *p) { return (gvec *)p; }
 
+// The call's span records: in the kernel's own argument memory for calls with at
+// most KVX_INLINE_SPANS of them (Launch::inl, at its offset in the one explicit
+// argument), else in the pool's device arena.  Either way read as constant memory.
+__device__ __forceinline__ const KVX_CONST SpanDev *span_records(const Launch &a)
+{
+    if (a.n_spans <= KVX_INLINE_SPANS)
+        return (const KVX_CONST SpanDev *)((const KVX_CONST uint8_t *)__builtin_amdgcn_kernarg_segment_ptr() +
+                                           offsetof(Launch, inl));
+    return as_const(a.spans);
+}
+
 __device__ __forceinline__ SpanDev load_span(const KVX_CONST SpanDev *p)
 {
     SpanDev r;
@@ -568,7 +579,7 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
-    const KVX_CONST SpanDev *spans = as_const(a.spans);
+    const KVX_CONST SpanDev *spans = span_records(a);
     uint32_t s = 0;
 
     if (SEG) {  // only instantiated for gather of token-major pages
