@@ -130,7 +130,7 @@ static_assert(sizeof(SpanDev) == 64, "SpanDev must stay 64 bytes");
 // Calls with at most this many span records pass them in the kernel arguments
 // (Launch::inl) instead of uploading them to the device arena before the launch.
 #ifndef KVX_INLINE_SPANS
-#define KVX_INLINE_SPANS 4
+#define KVX_INLINE_SPANS 16
 #endif
 
 struct Launch {
