@@ -11,6 +11,19 @@ import torch
 from paged_layout_transfer_amd import kvxfer as K
 
 
+def hip_runtime():
+    """The HIP runtime library this process already uses (the copy torch loaded, which
+    the transfer library shares), for direct runtime calls from tests."""
+    import ctypes
+    device()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64.so" in path:
+                return ctypes.CDLL(path)
+    return ctypes.CDLL("libamdhip64.so")
+
+
 def device():
     if not torch.cuda.is_available():
         raise RuntimeError("GPU tests need a ROCm device (torch.cuda.is_available() is False)")

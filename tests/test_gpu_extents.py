@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_harness as G
 from paged_layout_transfer_amd import kvxfer as K
 from paged_layout_transfer_amd import workloads as W
 
@@ -32,7 +33,7 @@ def _alloc_end(ptr: int) -> int:
     """How far the runtime's allocations reach from ptr without a gap (a torch block
     lies inside one allocation; virtual-memory mappings count one by one), as the
     library itself walks them."""
-    hip = ctypes.CDLL("libamdhip64.so")
+    hip = G.hip_runtime()
     cur = ptr
     for i in range(1 << 16):
         base, size = ctypes.c_void_p(), ctypes.c_size_t()

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_harness as G
 import oracle
 from paged_layout_transfer_amd import kvxfer as K
 
@@ -43,7 +44,7 @@ class MappedBuffer:
     """total bytes of device memory: CHUNK-sized physical allocations mapped in reverse order."""
 
     def __init__(self, total: int):
-        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip = G.hip_runtime()
         # the reservation runs two chunks past the mapped bytes, so the address after
         # the last mapping is never another allocation's
         self.total, self.reserved = total, total + 2 * CHUNK
