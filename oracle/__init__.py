@@ -26,11 +26,15 @@ LAYER_FIRST = 0
 PAGE_FIRST = 1
 
 
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp"]
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (plain -O2, single thread) into liboracle.so."""
+    """Compile oracle.c with gcc (plain -O2, OpenMP over the (span, layer) pairs)
+    into liboracle.so."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", _SRC, "-o", tmp])
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -66,6 +70,8 @@ def _load(path: str | None = None):
             ctypes.c_int, ctypes.POINTER(_Pool), ctypes.POINTER(ctypes.c_void_p),
             ctypes.POINTER(_Span), ctypes.c_int64, ctypes.POINTER(_Chunks), ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64]
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -75,7 +81,19 @@ def load_library(path: str):
     lib = ctypes.CDLL(path)
     lib.orc_transfer.restype = ctypes.c_int64
     lib.orc_transfer.argtypes = _load().orc_transfer.argtypes
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_max_threads.restype = ctypes.c_int
     return lib
+
+
+def set_threads(n: int, lib=None) -> None:
+    """Threads the following oracle calls share their (span, layer) pairs between."""
+    (lib or _load()).orc_set_threads(int(n))
+
+
+def max_threads(lib=None) -> int:
+    """Threads the oracle uses now (OpenMP's current maximum; 1 without OpenMP)."""
+    return int((lib or _load()).orc_max_threads())
 
 
 def transfer(direction: int, pool: dict, regions, spans, chunks: dict, chunk_buf: np.ndarray,

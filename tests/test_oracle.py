@@ -353,5 +353,5 @@ def test_planted_mistake_is_caught(name, old, new):
         c = os.path.join(d, "mut.c")
         so = os.path.join(d, "libmut.so")
         open(c, "w").write(src.replace(old, new))
-        subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", c, "-o", so])
+        subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-fopenmp", c, "-o", so])
         assert _battery_in_child(so) != 0, "planted mistake %r went unnoticed" % name
