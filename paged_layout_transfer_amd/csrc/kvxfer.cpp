@@ -309,10 +309,10 @@ struct kv_pool {
     kvx::ArenaRing<kInflight> arena;
     hipEvent_t fl_ev[kInflight] = {};  // one per arena slot
     // staging-memory kind of the last staging base seen
-    const void *last_base = nullptr;
-    bool last_base_host = false;
-    // allocation ends of the regions, staging bases and block tables seen (see
-    // check_buffers); the regions are checked until they have passed once
+    kvx::StagingKind staging_kind;
+    // the declared extents of the regions, staging bases and block tables against
+    // the allocations holding them (see check_buffers); the regions are checked until
+    // they have passed once
     kvx::ExtentCache extents;
     bool regions_ok = false;
     // timing
@@ -433,19 +433,16 @@ int validate_tables(kv_pool *p, const kv_span *spans, int32_t n_spans, int direc
 // Whether the staging memory is host memory (pinned, mapped): those transfers are
 // bound by the host link, which a few workgroups saturate, so by default they get a
 // small grid and leave the rest of the chip to compute (Strata guide,
-// "Non-Intrusive Resource Sizing").  The answer is cached per staging address.
-bool staging_in_host_memory(kv_pool *p, const void *base)
+// "Non-Intrusive Resource Sizing").  The answer is kept per staging address and the
+// allocation holding it (`alloc`, from the extent check).
+bool staging_in_host_memory(kv_pool *p, const void *base, const kvx::AllocRange &alloc)
 {
-    if (base != p->last_base) {
+    return p->staging_kind.is_host(base, alloc, [](const void *b) {
         hipPointerAttribute_t attr;
-        p->last_base_host = false;
-        if (hipPointerGetAttributes(&attr, base) == hipSuccess)
-            p->last_base_host = attr.type == hipMemoryTypeHost;
-        else
-            (void)hipGetLastError();  // unknown to the runtime: treat as device memory
-        p->last_base = base;
-    }
-    return p->last_base_host;
+        if (hipPointerGetAttributes(&attr, b) == hipSuccess) return attr.type == hipMemoryTypeHost;
+        (void)hipGetLastError();  // unknown to the runtime: treat as device memory
+        return false;
+    });
 }
 
 // The kernels and copies trust the extents a call declares: num_blocks blocks per
@@ -456,29 +453,31 @@ bool staging_in_host_memory(kv_pool *p, const void *base)
 // before anything is enqueued.  Memory the runtime does not know (pageable host
 // memory, other allocators) is taken on trust.
 
-// End of the allocation holding q, or 0 when the runtime does not know q.  Memory
-// mapped through the virtual-memory API (hipMemMap) reports each mapping as an
+// The allocation holding q, or an empty range when the runtime does not know q.
+// Memory mapped through the virtual-memory API (hipMemMap) reports each mapping as an
 // allocation of its own, which kvx::covered_end walks across.
-uintptr_t alloc_end(uintptr_t q)
+kvx::AllocRange alloc_range(uintptr_t q)
 {
     hipDeviceptr_t base = nullptr;
     size_t size = 0;
     if (hipMemGetAddressRange(&base, &size, reinterpret_cast<hipDeviceptr_t>(q)) != hipSuccess) {
         (void)hipGetLastError();
-        return 0;
+        return kvx::AllocRange{};
     }
-    return reinterpret_cast<uintptr_t>(base) + size;
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+    return kvx::AllocRange{b, b + size};
 }
 
-int check_extent(kvx::ExtentCache &c, const void *q, int64_t bytes)
+int check_extent(kvx::ExtentCache &c, const void *q, int64_t bytes, kvx::AllocRange *here = nullptr)
 {
-    return c.covers(q, bytes, alloc_end) ? KV_OK : KV_ERR_RANGE;
+    return c.covers(q, bytes, alloc_range, here) ? KV_OK : KV_ERR_RANGE;
 }
 
 // Extents of a validated call: every region (until they have passed once), the
 // staging area, and, when the tables are device memory, each span's block table.
+// *staging, if given, receives the allocation holding the staging base.
 int check_buffers(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
-                  bool device_tables)
+                  bool device_tables, kvx::AllocRange *staging = nullptr)
 {
     const kv_pool_desc &d = p->desc;
     if (!p->regions_ok) {
@@ -487,13 +486,21 @@ int check_buffers(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_ch
             if (check_extent(p->extents, b, extent)) return KV_ERR_RANGE;
         p->regions_ok = true;
     }
-    if (check_extent(p->extents, spec->base, spec->n_slots * spec->slot_bytes)) return KV_ERR_RANGE;
-    if (device_tables)
+    if (check_extent(p->extents, spec->base, spec->n_slots * spec->slot_bytes, staging)) return KV_ERR_RANGE;
+    if (device_tables) {
+        // spans often share one table: a table no longer than the last one checked at
+        // the same address needs no second lookup within the call
+        const int32_t *last = nullptr;
+        int64_t last_len = 0;
         for (int32_t i = 0; i < n_spans; ++i) {
             if (spans[i].t_end == spans[i].t_begin) continue;
+            if (spans[i].block_table == last && spans[i].table_len <= last_len) continue;
             if (check_extent(p->extents, spans[i].block_table, spans[i].table_len * (int64_t)sizeof(int32_t)))
                 return KV_ERR_RANGE;
+            last = spans[i].block_table;
+            last_len = spans[i].table_len;
         }
+    }
     return KV_OK;
 }
 
@@ -506,7 +513,8 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
     if (rc) return rc;
     if (info.tiles == 0) return KV_OK;
-    rc = check_buffers(p, spans, n_spans, spec, true);
+    kvx::AllocRange staging;
+    rc = check_buffers(p, spans, n_spans, spec, true, &staging);
     if (rc) return rc;
     rc = device_setup(p);
     if (rc) return rc;
@@ -550,7 +558,7 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
-    else if (staging_in_host_memory(p, spec->base)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
+    else if (staging_in_host_memory(p, spec->base, staging)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
 
     const bool timed = p->timing && p->n_timed < kMaxTimed;
     if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return fail();

@@ -14,47 +14,90 @@ namespace kvx {
 
 // ---- declared extents against the runtime's allocations (host) ---------------
 
+// One allocation (or virtual-memory mapping) as the runtime reports it: [base, end).
+// end == 0: the runtime does not know the address.
+struct AllocRange {
+    uintptr_t base = 0, end = 0;
+    bool operator==(const AllocRange &o) const { return base == o.base && end == o.end; }
+};
+
 // How far from address q the allocations the runtime knows reach without a gap,
 // walking from one allocation (or virtual-memory mapping) to the next until `need` is
-// covered.  lookup(a) returns the end of the allocation holding a, or 0 when the
-// runtime does not know a.  Returns 0 when q itself is unknown, the end of the last
-// adjoining allocation otherwise, and UINTPTR_MAX when more than max_pieces would
-// have to be followed (the range is then taken on trust).
+// covered.  lookup(a) returns the AllocRange holding a.  Returns 0 when q itself is
+// unknown, the end of the last adjoining allocation otherwise, and UINTPTR_MAX when
+// more than max_pieces would have to be followed (the range is then taken on trust).
+// *last, if given, receives the last allocation the walk looked at.
 template <class Lookup>
-uintptr_t covered_end(uintptr_t q, uintptr_t need, Lookup lookup, int max_pieces = 1 << 16)
+uintptr_t covered_end(uintptr_t q, uintptr_t need, Lookup lookup, int max_pieces = 1 << 16,
+                      AllocRange *last = nullptr)
 {
     uintptr_t cur = q;
     for (int i = 0; i < max_pieces; ++i) {
-        const uintptr_t end = lookup(cur);
-        if (end <= cur) return i == 0 ? 0 : cur;   // unknown memory after known pieces
-        if (end >= need) return end;
-        cur = end;
+        const AllocRange r = lookup(cur);
+        if (r.end <= cur) return i == 0 ? 0 : cur;   // unknown memory after known pieces
+        if (last) *last = r;
+        if (r.end >= need) return r.end;
+        cur = r.end;
     }
     return UINTPTR_MAX;
 }
 
-// Ends of the allocations holding recently seen pointers: a small direct-mapped table
-// keyed by pointer, so a call on the same buffers asks the runtime nothing.
+// The declared-extent check.  Every call asks the runtime for the allocation holding
+// the pointer (one lookup), so an allocation freed and made again at the same address,
+// smaller or larger, is always seen as it is now.  Only a range that runs on into
+// adjoining allocations (memory mapped in several pieces) needs a longer walk; its
+// result is kept in a small direct-mapped table keyed by pointer and reused while the
+// allocations holding the first and the last byte the walk reached are unchanged.
 struct ExtentCache {
     static constexpr int kEntries = 128;
     const void *key[kEntries] = {};
-    uintptr_t end[kEntries] = {};
+    AllocRange first[kEntries] = {};  // allocation holding the pointer when the walk ran
+    AllocRange last[kEntries] = {};   // last allocation the walk reached
+    uintptr_t end[kEntries] = {};     // how far the walk got
 
     // true when [q, q + bytes) lies inside memory the runtime has allocated or mapped
-    // without a gap, or the runtime does not know q.  A cached end that covers the
-    // range is trusted; anything else is looked up again first (an allocation freed
-    // and made again at the same address may have grown).
+    // without a gap, or the runtime does not know q.  *here, if given, receives the
+    // allocation holding q.
     template <class Lookup>
-    bool covers(const void *q, int64_t bytes, Lookup lookup)
+    bool covers(const void *q, int64_t bytes, Lookup lookup, AllocRange *here = nullptr)
     {
         const uintptr_t a = reinterpret_cast<uintptr_t>(q);
         const uintptr_t need = a + (uintptr_t)bytes;
+        const AllocRange r = lookup(a);
+        if (here) *here = r;
+        if (r.end <= a) return true;      // unknown to the runtime: taken on trust
+        if (r.end >= need) return true;   // one allocation holds the whole range
         const int i = (int)(((a >> 9) ^ (a >> 21)) % kEntries);
-        if (key[i] == q && end[i] >= need) return true;
-        const uintptr_t e = covered_end(a, need, lookup);
+        if (key[i] == q && first[i] == r && end[i] >= need && lookup(last[i].base) == last[i])
+            return true;
+        AllocRange l = r;
+        const uintptr_t e = covered_end(r.end, need, lookup, 1 << 16, &l);
+        const uintptr_t reach = e ? e : r.end;  // nothing adjoins: the first piece's end
         key[i] = q;
-        end[i] = e ? e : UINTPTR_MAX;
-        return !(e && e < need);
+        first[i] = r;
+        last[i] = l;
+        end[i] = reach;
+        return reach >= need;
+    }
+};
+
+// Kind of staging memory (host or device) last seen at one address, remembered
+// together with the allocation holding it, so that a new allocation at the same
+// address is looked at again.
+struct StagingKind {
+    const void *base = nullptr;
+    AllocRange alloc;
+    bool host = false;
+
+    template <class Query>
+    bool is_host(const void *b, const AllocRange &r, Query query_host)
+    {
+        if (b != base || !(r == alloc)) {
+            host = query_host(b);
+            base = b;
+            alloc = r;
+        }
+        return host;
     }
 };
 

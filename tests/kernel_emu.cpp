@@ -562,12 +562,13 @@ static std::vector<uint64_t> g_alloc_base, g_alloc_size;
 static int64_t g_lookups = 0;
 static kvx::ExtentCache g_cache;
 
-static uintptr_t fake_alloc_end(uintptr_t a)
+static kvx::AllocRange fake_alloc_range(uintptr_t a)
 {
     ++g_lookups;
     for (size_t i = 0; i < g_alloc_base.size(); ++i)
-        if (a >= g_alloc_base[i] && a - g_alloc_base[i] < g_alloc_size[i]) return g_alloc_base[i] + g_alloc_size[i];
-    return 0;
+        if (a >= g_alloc_base[i] && a - g_alloc_base[i] < g_alloc_size[i])
+            return kvx::AllocRange{g_alloc_base[i], g_alloc_base[i] + g_alloc_size[i]};
+    return kvx::AllocRange{};
 }
 
 extern "C" void emu_set_allocs(const uint64_t *bases, const uint64_t *sizes, int32_t n)
@@ -578,7 +579,7 @@ extern "C" void emu_set_allocs(const uint64_t *bases, const uint64_t *sizes, int
 
 extern "C" uint64_t emu_covered_end(uint64_t q, uint64_t need, int32_t max_pieces)
 {
-    return kvx::covered_end(q, need, fake_alloc_end, max_pieces);
+    return kvx::covered_end(q, need, fake_alloc_range, max_pieces);
 }
 
 extern "C" void emu_cache_reset() { g_cache = kvx::ExtentCache(); g_lookups = 0; }
@@ -586,7 +587,7 @@ extern "C" void emu_cache_reset() { g_cache = kvx::ExtentCache(); g_lookups = 0;
 extern "C" int32_t emu_cache_covers(uint64_t q, int64_t bytes, int64_t *lookups)
 {
     const int64_t before = g_lookups;
-    const bool ok = g_cache.covers(reinterpret_cast<const void *>(q), bytes, fake_alloc_end);
+    const bool ok = g_cache.covers(reinterpret_cast<const void *>(q), bytes, fake_alloc_range);
     *lookups = g_lookups - before;
     return ok ? 1 : 0;
 }

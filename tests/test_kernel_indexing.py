@@ -396,21 +396,43 @@ def test_extent_walk_follows_adjoining_allocations_and_stops_at_gaps(emu):
     del keep
 
 
-def test_extent_cache_answers_repeat_calls_and_rechecks_refusals(emu):
+def test_extent_check_sees_each_allocation_as_it_is_now(emu):
     MB = 1 << 20
     A = 0x7F0000000000
     n = ctypes.c_int64()
     emu.emu_cache_reset()
     keep = _allocs(emu, [(A, 4 * MB)])
     assert emu.emu_cache_covers(A, 4 * MB, ctypes.byref(n)) == 1 and n.value == 1
-    assert emu.emu_cache_covers(A, 2 * MB, ctypes.byref(n)) == 1 and n.value == 0    # cached end covers it
-    assert emu.emu_cache_covers(A, 4 * MB + 16, ctypes.byref(n)) == 0 and n.value >= 1
-    # the allocation is made again larger at the same address: a refusal is looked up afresh
+    assert emu.emu_cache_covers(A, 2 * MB, ctypes.byref(n)) == 1 and n.value == 1
+    assert emu.emu_cache_covers(A, 4 * MB + 16, ctypes.byref(n)) == 0
+    # freed and made again smaller at the same address: the old 4 MiB extent is refused
+    keep = _allocs(emu, [(A, 2 * MB)])
+    assert emu.emu_cache_covers(A, 4 * MB, ctypes.byref(n)) == 0
+    assert emu.emu_cache_covers(A, 2 * MB, ctypes.byref(n)) == 1
+    # made again larger: accepted
     keep = _allocs(emu, [(A, 8 * MB)])
-    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1 and n.value >= 1
-    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1 and n.value == 0
-    # memory the runtime does not know is taken on trust, and remembered as such
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1 and n.value == 1
+    # memory the runtime does not know is taken on trust
     B = A + 64 * MB
     assert emu.emu_cache_covers(B, 1 << 40, ctypes.byref(n)) == 1 and n.value == 1
-    assert emu.emu_cache_covers(B, 1 << 40, ctypes.byref(n)) == 1 and n.value == 0
+    del keep
+
+
+def test_extent_check_reuses_a_walk_over_pieces_while_its_ends_stand(emu):
+    MB = 1 << 20
+    A = 0x7F0000000000
+    n = ctypes.c_int64()
+    emu.emu_cache_reset()
+    keep = _allocs(emu, [(A, 2 * MB), (A + 2 * MB, 2 * MB), (A + 4 * MB, 2 * MB)])
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1 and n.value == 3   # walked
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1 and n.value == 2   # first + last checked
+    # the last piece unmapped and mapped again smaller: the walk runs again and refuses
+    keep = _allocs(emu, [(A, 2 * MB), (A + 2 * MB, 2 * MB), (A + 4 * MB, MB)])
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 0
+    # the first piece replaced by a smaller allocation (a gap after it): refused
+    keep = _allocs(emu, [(A, MB), (A + 2 * MB, 2 * MB), (A + 4 * MB, 2 * MB)])
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 0
+    # whole again
+    keep = _allocs(emu, [(A, 2 * MB), (A + 2 * MB, 2 * MB), (A + 4 * MB, 2 * MB)])
+    assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1
     del keep
