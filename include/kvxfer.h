@@ -211,7 +211,8 @@ KV_API int kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 
 /* Frees the handle and its device state, after waiting for the transfers it
  * queued that are still in flight (their fence events; other device work is not
- * waited for).  The caller's regions are untouched.  NULL is accepted. */
+ * waited for).  The caller's regions are untouched.  NULL is accepted.
+ * No passage: library infrastructure (the handle's lifetime). */
 KV_API int kv_pool_destroy(kv_pool *pool);
 
 /* Block allocator (a host bitmap of free blocks, preallocated at create time, no
@@ -223,6 +224,7 @@ KV_API int kv_pool_destroy(kv_pool *pool);
  * nothing is freed. */
 KV_API int kv_pool_alloc_blocks(kv_pool *pool, int32_t n, int32_t *out_ids);
 KV_API int kv_pool_free_blocks(kv_pool *pool, int32_t n, const int32_t *ids);
+/* Free blocks left in the allocator (same source as the two calls above). */
 KV_API int kv_pool_free_count(const kv_pool *pool, int64_t *out);
 
 /* ---- calls -------------------------------------------------------------------- */
@@ -230,19 +232,25 @@ KV_API int kv_pool_free_count(const kv_pool *pool, int64_t *out);
 /* Host-only dry run: validates a prospective call exactly as kv_gather_chunks /
  * kv_scatter_chunks do (shapes, alignment, span ranges, slot sizes, one slot per
  * chunk) and reports its sizes.  Makes no HIP call, so the allocation-extent
- * checks (Conventions above) are left to the transfer itself; info may be NULL. */
+ * checks (Conventions above) are left to the transfer itself; info may be NULL.
+ * No passage of its own: it is the host-side part of the transfer calls below
+ * (their call decomposition, Tutti summary, Q2 "Design 1"), run without a launch. */
 KV_API int kv_check_transfer(const kv_pool_desc *desc, const kv_span *spans, int32_t n_spans,
                       const kv_chunk_spec *spec, kv_transfer_info *info);
 
 /* Bytes of a chunk holding `tokens` tokens (1 <= tokens <= chunk_tokens) in the
- * spec's layout. */
+ * spec's layout (the two chunk layouts of the Data model above: Strata guide,
+ * "Two-Dimensional Memory Layout Decoupling", items 1 and 2), so a caller can size
+ * staging slots. */
 KV_API int kv_chunk_bytes(const kv_pool_desc *desc, const kv_chunk_spec *spec, int64_t tokens,
                    int64_t *out);
 
 /* Host-side check of the block tables of a call, given host copies of them
  * (host_tables[i] holds spans[i].table_len ids): every id of every referenced
  * page lies in [0, num_blocks) (else KV_ERR_RANGE) and, for KV_SCATTER, no pool
- * page receives two writers (else KV_ERR_DUP).  Gather may read a page twice. */
+ * page receives two writers (else KV_ERR_DUP).  Gather may read a page twice.
+ * No passage: the pages are silent on duplicate targets; this checks the
+ * precondition the library states for scatter (one writer per pool page). */
 KV_API int kv_validate_targets(const kv_pool_desc *desc, const kv_span *spans, int32_t n_spans,
                         const int32_t *const *host_tables, int32_t direction);
 
@@ -283,7 +291,9 @@ KV_API int kv_scatter_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_
 
 /* Synchronizes `stream`, then reads and clears the pool's sticky device error
  * word.  *out_bits receives KV_DEVERR_* bits (0 if none); the return value is
- * KV_ERR_DEVICE when any bit was set, else KV_OK. */
+ * KV_ERR_DEVICE when any bit was set, else KV_OK.
+ * No passage: library infrastructure (failure detection: how a bad block id the
+ * kernel skipped is reported to the caller). */
 KV_API int kv_pool_get_error(kv_pool *pool, hipStream_t stream, int32_t *out_bits);
 
 /* Kernel timing.  After kv_pool_timing_start, every transfer records a HIP
@@ -293,6 +303,8 @@ KV_API int kv_pool_get_error(kv_pool *pool, hipStream_t stream, int32_t *out_bit
  * kv_pool_timing_read_each does the same but writes each launch's time, in launch
  * order, to ms_each[0 .. min(cap, *launches)) (caller-owned; may be null when cap
  * is 0). */
+/* No passage: library infrastructure (measurement of the kernel alone, as the
+ * pages' bandwidth figures are rates of the transfer itself). */
 KV_API int kv_pool_timing_start(kv_pool *pool);
 KV_API int kv_pool_timing_read(kv_pool *pool, double *total_ms, int64_t *launches);
 KV_API int kv_pool_timing_read_each(kv_pool *pool, double *ms_each, int64_t cap, int64_t *launches);
@@ -307,11 +319,13 @@ KV_API int kv_pool_timing_read_each(kv_pool *pool, double *ms_each, int64_t cap,
  * kv_chunk_spec.base. */
 KV_API int kv_ring_create(int64_t slot_bytes, int64_t n_slots, int32_t flags, kv_ring **out);
 
-/* Host and device addresses of slot i (0 <= i < n_slots); either out may be NULL. */
+/* Host and device addresses of slot i (0 <= i < n_slots); either out may be NULL.
+ * Same source as kv_ring_create. */
 KV_API int kv_ring_slot(const kv_ring *ring, int64_t i, void **host_ptr, void **dev_ptr);
 
 /* Frees the pinned memory; the caller must have synchronized every transfer
- * that uses it.  NULL is accepted. */
+ * that uses it.  NULL is accepted.  No passage: library infrastructure (the
+ * ring's lifetime). */
 KV_API int kv_ring_destroy(kv_ring *ring);
 
 /* Slot fencing, for using the ring as a queue between the GPU and the host (slot
@@ -329,17 +343,19 @@ KV_API int kv_ring_stream_wait(kv_ring *ring, int64_t first, int64_t count, hipS
 
 /* ---- misc ------------------------------------------------------------------------ */
 
-/* Static description of a KV_* return code. */
+/* Static description of a KV_* return code.  No passage: library infrastructure
+ * (error reporting). */
 KV_API const char *kv_strerror(int code);
 
 /* Library version: major*10000 + minor*100 + patch (KV_VERSION of the header the
- * library was built with). */
+ * library was built with).  No passage: library infrastructure. */
 #define KV_VERSION 200
 KV_API int kv_version(void);
 
 /* The hipError_t of the last HIP runtime call that failed inside the library on
  * the calling thread (0 if none), and in *where (if not NULL) the call's text.
- * Lets a caller that got KV_ERR_HIP see which call failed and why. */
+ * Lets a caller that got KV_ERR_HIP see which call failed and why.  No passage:
+ * library infrastructure (failure detection). */
 KV_API int kv_last_hip_error(const char **where);
 
 #ifdef __cplusplus

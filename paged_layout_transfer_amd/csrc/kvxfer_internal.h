@@ -19,6 +19,7 @@
 //   in-chunk index, page-first chunk  [pages][CL][KV]: (pi * CL + li) * KV + kv
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "kvxfer.h"
@@ -112,7 +113,9 @@ constexpr int kWavesPerBlock = KVX_WAVES_PER_BLOCK;
 constexpr int kThreads = 64 * kWavesPerBlock;
 
 // Per-span launch record, uploaded once per call (64 bytes: one scalar 16-dword load).
-struct alignas(64) SpanDev {
+// Its alignment is that of its widest field, so the copies of it in the kernel
+// arguments (Launch::inl, 8-byte aligned) are properly aligned objects.
+struct alignas(8) SpanDev {
     const int32_t *table;  // device block table
     int64_t tile_begin;    // first global tile id of this span
     int64_t t_end;         // one past the last token
@@ -184,6 +187,7 @@ struct Launch {
     // unused): 64-byte SpanDev images, read by the kernel from its argument memory
     uint64_t inl[KVX_INLINE_SPANS * sizeof(SpanDev) / sizeof(uint64_t)];
 };
+static_assert(offsetof(Launch, inl) % alignof(SpanDev) == 0, "inline span records must be aligned SpanDev objects");
 
 // Kernel-internal page layout values: head-major pages staged through LDS in token
 // slabs, and in head-group slabs (hm_lds_head_slab).

@@ -255,6 +255,20 @@ def kv_last_hip_error() -> tuple[int, str]:
     return int(code), (where.value or b"").decode()
 
 
+def hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime library this process already has mapped -- the one this
+    library and torch are bound to -- for direct runtime calls (memory queries,
+    copies, CU-masked streams).  A second copy loaded by soname would be a separate
+    runtime that sees no device, so there is no fallback: if none is mapped,
+    RuntimeError."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64.so" in path:
+                return ctypes.CDLL(path)
+    raise RuntimeError("no HIP runtime is mapped in this process")
+
+
 def ring_host_array(ring: int, nbytes: int) -> np.ndarray:
     """A numpy uint8 view of a ring's host mapping (first nbytes), for filling and reading."""
     host, _ = kv_ring_slot(ring, 0)

@@ -14,14 +14,8 @@ from paged_layout_transfer_amd import kvxfer as K
 def hip_runtime():
     """The HIP runtime library this process already uses (the copy torch loaded, which
     the transfer library shares), for direct runtime calls from tests."""
-    import ctypes
     device()
-    with open("/proc/self/maps") as f:
-        for line in f:
-            path = line.split()[-1]
-            if "libamdhip64.so" in path:
-                return ctypes.CDLL(path)
-    return ctypes.CDLL("libamdhip64.so")
+    return K.hip_runtime()
 
 
 def device():
