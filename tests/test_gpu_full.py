@@ -1,12 +1,18 @@
 """Full-size parity: every workload at its stated size, in the launch configuration
 bench.py times (default grid, HBM or pinned-host staging as the workload says),
-checked against the oracle on sampled layers and requests.
+compared with the oracle byte for byte over the whole call: every layer of every
+request, both directions.
 
-A sampled check runs the oracle on one request with its chunks numbered from 0
-(the same call restricted to that request) and one layer.  The positions the
-oracle writes are found by running it over two different initial fills; the GPU
-must hold the oracle's bytes there.  For scatter, every byte of the sampled
-layer that no request writes must still hold the sentinel.
+Gather: the staging buffer starts at the sentinel on the GPU and in the oracle's
+copy; the oracle runs over the host copy of the pool, a batch of layers at a time
+(so the host holds a bounded slice of the pool), and the whole staging buffer
+must then match.  Scatter: the staging buffer holds seeded random bytes and the
+pool starts at the sentinel on both sides; for each batch of layers the oracle
+scatters into sentinel regions and the GPU's regions of those layers must match
+in full, so a byte written where no request names it fails too.
+
+The pinned-host workload (80 layers through a ring of 4-layer windows) is checked
+window by window, both directions, every window.
 """
 from __future__ import annotations
 
@@ -19,6 +25,9 @@ from paged_layout_transfer_amd import kvxfer as K
 from paged_layout_transfer_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
+
+SLICE = 1 << 30            # bytes per device-to-host comparison slice
+REGION_BUDGET = 24 << 30   # host bytes of pool regions held per oracle batch
 
 
 def say(*a):
@@ -35,8 +44,31 @@ def resolve(name):
     return w, pool
 
 
-def n_chunks_of(w, t0, t1):
-    return (w["num_layers"] // w["chunk_layers"]) * -(-(t1 - t0) // w["chunk_tokens"])
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """A flat uint8 device tensor copied to a new host array, a slice at a time."""
+    out = np.empty(t.numel(), dtype=np.uint8)
+    ho = torch.from_numpy(out)
+    for a in range(0, t.numel(), SLICE):
+        ho[a:a + SLICE].copy_(t[a:a + SLICE])
+    return out
+
+
+def assert_device_equals(exp: np.ndarray, t: torch.Tensor, what: str):
+    """exp (host) == t (device), compared a slice at a time; names the first differing byte."""
+    assert exp.size == t.numel()
+    for a in range(0, exp.size, SLICE):
+        got = t[a:a + SLICE].cpu().numpy()
+        e = exp[a:a + SLICE]
+        if not np.array_equal(got, e):
+            i = int(np.flatnonzero(got != e)[0])
+            raise AssertionError("%s: first difference at byte %d (gpu %d, oracle %d)" % (
+                what, a + i, got[i], e[i]))
+
+
+def layer_batches(pool):
+    per_layer = pool["num_kv"] * pool["num_blocks"] * pool["block_stride"]
+    n = max(1, min(pool["num_layers"], REGION_BUDGET // per_layer))
+    return [(l0, min(l0 + n, pool["num_layers"])) for l0 in range(0, pool["num_layers"], n)]
 
 
 class Setup:
@@ -69,113 +101,63 @@ class Setup:
         del self.P, self.tabs
         torch.cuda.empty_cache()
 
-    def rows_of(self, layer):
-        return [self.P[layer * self.KV + k].cpu().numpy() for k in range(self.KV)]
-
-    def sub(self, r):
-        """Request r alone, its chunks numbered from 0, and the slice of the full
-        staging buffer its chunks occupy."""
-        tbl, t0, t1, fc = self.spans_h[r]
-        n = n_chunks_of(self.w, t0, t1)
-        sb = self.chunks["slot_bytes"]
-        return (tbl, t0, t1, 0), dict(self.chunks, n_slots=n), (fc * sb, (fc + n) * sb)
+    def host_regions(self, l0, l1, fill=None):
+        """Regions list for the oracle: layers [l0, l1) as host arrays (the GPU's bytes,
+        or `fill` everywhere), None elsewhere."""
+        regs = [None] * (self.L * self.KV)
+        for i in range(l0 * self.KV, l1 * self.KV):
+            regs[i] = to_host(self.P[i]) if fill is None else np.full(self.row, fill, dtype=np.uint8)
+        return regs
 
 
-def gather_check(S, stg, layer, requests):
-    rows = [None] * (S.L * S.KV)
-    for k, r in enumerate(S.rows_of(layer)):
-        rows[layer * S.KV + k] = r
-    for r in requests:
-        span, chunks, (lo, hi) = S.sub(r)
-        a = np.zeros(hi - lo, dtype=np.uint8)
-        b = np.full(hi - lo, 0xFF, dtype=np.uint8)
-        oracle.gather(S.pool, rows, [span], chunks, a, only_layers=(layer, layer + 1))
-        oracle.gather(S.pool, rows, [span], chunks, b, only_layers=(layer, layer + 1))
-        m = a == b
-        assert m.any()
-        got = stg[lo:hi].cpu().numpy()
-        assert np.array_equal(got[m], a[m]), "gather: request %d layer %d" % (r, layer)
+HBM_WORKLOADS = ["llama8b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
+                 "hnd_rows24"]
 
 
-def scatter_check(S, stg, layer, requests):
-    """GPU pool started at the sentinel; stg is the staging buffer the scatter read."""
-    got = S.rows_of(layer)
-    pool, bs, stride = S.pool, S.pool["block_size"], S.pool["block_stride"]
-    written = np.zeros(pool["num_blocks"], dtype=bool)
-    for tbl, t0, t1, _ in S.spans_h:
-        written[tbl[t0 // bs: -(-t1 // bs)]] = True
-    for k in range(S.KV):
-        blocks = got[k].reshape(pool["num_blocks"], stride)
-        assert np.all(blocks[~written] == W.SENTINEL), "scatter wrote a block no request names"
-    # the sampled requests own distinct blocks, so one pair of oracle rows serves them all
-    ea = [None] * (S.L * S.KV)
-    eb = [None] * (S.L * S.KV)
-    for k in range(S.KV):
-        ea[layer * S.KV + k] = np.zeros(S.row, dtype=np.uint8)
-        eb[layer * S.KV + k] = np.full(S.row, 0xFF, dtype=np.uint8)
-    own = np.zeros(pool["num_blocks"], dtype=bool)
-    for r in requests:
-        span, chunks, (lo, hi) = S.sub(r)
-        src = stg[lo:hi].cpu().numpy()
-        oracle.scatter(S.pool, ea, [span], chunks, src, only_layers=(layer, layer + 1))
-        oracle.scatter(S.pool, eb, [span], chunks, src, only_layers=(layer, layer + 1))
-        tbl, t0, t1, _ = span
-        own[tbl[t0 // bs: -(-t1 // bs)]] = True
-    for k in range(S.KV):
-        a, b = ea[layer * S.KV + k], eb[layer * S.KV + k]
-        m = a == b
-        assert m.any()
-        assert np.array_equal(got[k][m], a[m]), "scatter: layer %d kv %d" % (layer, k)
-        # inside the sampled requests' blocks, bytes no request writes stay at the sentinel
-        rest = (~m).reshape(pool["num_blocks"], stride) & own[:, None]
-        assert np.all(got[k].reshape(pool["num_blocks"], stride)[rest] == W.SENTINEL)
-
-
-HBM_CASES = {
-    "llama8b": dict(layers=[0, 31], requests=[0]),
-    "mixed": dict(layers=[0, 31], requests=[0, 21, 42, 63]),
-    "mla_fp8": dict(layers=[0, 60], requests=[0]),
-    "int8_kv": dict(layers=[0, 60], requests=[0]),
-    "llama8b_hnd": dict(layers=[0, 31], requests=[0]),
-    "fp8_hnd_d64": dict(layers=[0, 31], requests=[0]),
-    "llama8b_tp8": dict(layers=[0, 31], requests=[0]),
-    "hnd_rows24": dict(layers=[0, 31], requests=[0]),
-}
-
-
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", list(HBM_CASES))
-def test_full_size_hbm(name):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", HBM_WORKLOADS)
+def test_full_size_hbm_every_layer(name):
     S = Setup(name)
     try:
-        c = HBM_CASES[name]
-        say(name, "pool %.1f GiB, staging %.1f GiB, %d requests" % (
-            S.P.numel() / 2**30, S.plan["slot_bytes"] * S.plan["n_chunks"] / 2**30, len(S.spans_h)))
+        nbytes = S.plan["slot_bytes"] * S.plan["n_chunks"]
+        say(name, "pool %.1f GiB, staging %.1f GiB, %d requests, %d oracle threads" % (
+            S.P.numel() / 2**30, nbytes / 2**30, len(S.spans_h), oracle.max_threads()))
         W.device_fill_(S.P.view(-1), S.w["fill"], S.w["k"])
-        stg = torch.empty(S.plan["slot_bytes"] * S.plan["n_chunks"], dtype=torch.uint8, device=S.dev)
+        stg = torch.full((nbytes,), W.SENTINEL, dtype=torch.uint8, device=S.dev)
         spec = K.make_chunk_spec(S.chunks["layout"], S.chunks["chunk_layers"], S.chunks["chunk_tokens"],
                                  0, S.L, stg, S.chunks["slot_bytes"], S.chunks["n_slots"])
         say(name, "gather")
         K.kv_gather_chunks(S.h, S.spans_d, spec, S.stream)
         assert K.kv_pool_get_error(S.h, S.stream) == 0
-        for layer in c["layers"]:
-            gather_check(S, stg, layer, c["requests"])
+        exp = np.full(nbytes, W.SENTINEL, dtype=np.uint8)
+        for l0, l1 in layer_batches(S.pool):
+            say(name, "gather oracle layers %d-%d" % (l0, l1 - 1))
+            oracle.gather(S.pool, S.host_regions(l0, l1), S.spans_h, S.chunks, exp, only_layers=(l0, l1))
+        assert_device_equals(exp, stg, "%s gather" % name)
+        del exp
+
         say(name, "scatter")
         W.device_fill_(stg, "bytes", 200 + S.w["k"])
+        src = to_host(stg)
         S.P.fill_(W.SENTINEL)
         K.kv_scatter_chunks(S.h, S.spans_d, spec, S.stream)
         assert K.kv_pool_get_error(S.h, S.stream) == 0
-        for layer in c["layers"]:
-            scatter_check(S, stg, layer, c["requests"])
-        del stg
+        for l0, l1 in layer_batches(S.pool):
+            say(name, "scatter oracle layers %d-%d" % (l0, l1 - 1))
+            regs = S.host_regions(l0, l1, fill=W.SENTINEL)
+            oracle.scatter(S.pool, regs, S.spans_h, S.chunks, src, only_layers=(l0, l1))
+            for i in range(l0 * S.KV, l1 * S.KV):
+                assert_device_equals(regs[i], S.P[i], "%s scatter layer %d kv %d" % (name, i // S.KV, i % S.KV))
+                regs[i] = None
+        del stg, src
     finally:
         S.close()
 
 
-@pytest.mark.timeout(600)
-def test_full_size_llama70b_pinned_ring():
+@pytest.mark.timeout(900)
+def test_full_size_llama70b_pinned_ring_every_window():
     """The 128K-token 70B-shaped context through a pinned host ring of 4-layer windows
-    (1024 slots of 2 MiB), both directions, every window moved, three checked."""
+    (1024 slots of 2 MiB), both directions, every window checked in full."""
     S = Setup("llama70b")
     ring = None
     try:
@@ -188,7 +170,7 @@ def test_full_size_llama70b_pinned_ring():
         ring_dev = K.kv_ring_slot(ring, 0)[1]
         ring_host = K.ring_host_array(ring, slot * n_slots)
         W.device_fill_(S.P.view(-1), w["fill"], w["k"])
-        checked = (0, 10, 19)
+        span = S.spans_h[0]
 
         def spec(i):
             return K.make_chunk_spec(K.KV_LAYER_FIRST, 1, w["chunk_tokens"], i * win, (i + 1) * win,
@@ -197,22 +179,18 @@ def test_full_size_llama70b_pinned_ring():
         def window_chunks(i):
             return dict(S.chunks, layer_begin=i * win, layer_end=(i + 1) * win, n_slots=n_slots)
 
-        say("llama70b gather through the ring")
+        say("llama70b gather through the ring, %d windows" % (S.L // win))
         for i in range(S.L // win):
+            ring_host[:] = W.SENTINEL
             K.kv_gather_chunks(S.h, S.spans_d, spec(i), S.stream)
             assert K.kv_pool_get_error(S.h, S.stream) == 0
-            if i in checked:
-                layer = i * win
-                rows = [None] * (S.L * S.KV)
-                for k, r in enumerate(S.rows_of(layer)):
-                    rows[layer * S.KV + k] = r
-                a = np.zeros(slot * n_slots, dtype=np.uint8)
-                b = np.full(slot * n_slots, 0xFF, dtype=np.uint8)
-                span = S.spans_h[0]
-                oracle.gather(S.pool, rows, [span], window_chunks(i), a, only_layers=(layer, layer + 1))
-                oracle.gather(S.pool, rows, [span], window_chunks(i), b, only_layers=(layer, layer + 1))
-                m = a == b
-                assert m.any() and np.array_equal(ring_host[m], a[m]), "ring gather window %d" % i
+            exp = np.full(slot * n_slots, W.SENTINEL, dtype=np.uint8)
+            oracle.gather(S.pool, S.host_regions(i * win, (i + 1) * win), [span], window_chunks(i), exp,
+                          only_layers=(i * win, (i + 1) * win))
+            if not np.array_equal(ring_host, exp):
+                j = int(np.flatnonzero(ring_host != exp)[0])
+                raise AssertionError("ring gather window %d: first difference at byte %d" % (i, j))
+            say("gather window %d ok" % i)
         say("llama70b scatter through the ring")
         rnd = torch.empty(slot * n_slots, dtype=torch.uint8, device=S.dev)
         W.device_fill_(rnd, "bytes", 203)
@@ -223,15 +201,14 @@ def test_full_size_llama70b_pinned_ring():
             K.kv_scatter_chunks(S.h, S.spans_d, spec(i), S.stream)
         assert K.kv_pool_get_error(S.h, S.stream) == 0
         src = ring_host.copy()
-        for i in checked:
-            layer = i * win
-            got = S.rows_of(layer)
-            a = [None] * (S.L * S.KV)
-            for k in range(S.KV):
-                a[layer * S.KV + k] = np.full(S.row, W.SENTINEL, dtype=np.uint8)
-            oracle.scatter(S.pool, a, [S.spans_h[0]], window_chunks(i), src, only_layers=(layer, layer + 1))
-            for k in range(S.KV):
-                assert np.array_equal(got[k], a[layer * S.KV + k]), "ring scatter window %d kv %d" % (i, k)
+        for i in range(S.L // win):
+            l0, l1 = i * win, (i + 1) * win
+            regs = S.host_regions(l0, l1, fill=W.SENTINEL)
+            oracle.scatter(S.pool, regs, [span], window_chunks(i), src, only_layers=(l0, l1))
+            for r in range(l0 * S.KV, l1 * S.KV):
+                assert_device_equals(regs[r], S.P[r], "ring scatter window %d layer %d kv %d" % (
+                    i, r // S.KV, r % S.KV))
+            say("scatter window %d ok" % i)
     finally:
         if ring is not None:
             K.kv_ring_destroy(ring)

@@ -73,6 +73,25 @@ def test_many_random_cases_with_random_options():
                      max_workgroups=wg)
 
 
+@pytest.mark.parametrize("n_records", [15, 16, 17, 18, 40])
+def test_span_record_count_around_the_inline_limit(n_records):
+    """A call with at most 16 span records passes them in the kernel arguments; one with
+    more uploads them to the pool's device arena.  Whole-buffer parity on both sides of
+    that limit, both directions, both chunk layouts, with empty spans mixed in (an
+    empty span makes no record, so they must not count towards the limit)."""
+    for layout in (K.KV_LAYER_FIRST, K.KV_PAGE_FIRST):
+        rng = np.random.default_rng(70_000 + 10 * n_records + layout)
+        pool, spans, chunks = cases.make_case(rng, tok_multiple=16, n_spans=n_records, layout=layout,
+                                              max_bytes=16 << 20)
+        empty = (np.zeros(0, dtype=np.int32), 0, 0, 0)
+        for _ in range(int(rng.integers(1, 6))):
+            spans.insert(int(rng.integers(0, len(spans) + 1)), empty)
+        assert sum(1 for _, t0, t1, _ in spans if t1 > t0) == n_records
+        regions, staging = _random(pool, chunks, n_records)
+        for d in DIRS:
+            _compare(d, pool, spans, chunks, regions, staging, "records-%d-layout%d" % (n_records, layout))
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_medium_random_cases(seed):
     pool, spans, chunks = cases.make_case(np.random.default_rng(20_000 + seed), tok_multiple=16,

@@ -1,10 +1,13 @@
 """Many transfer calls queued back to back with no synchronisation in between.
 
-Each call moves one page of one request; 320 calls exceed the 256 calls the
-library keeps in flight, and every eighth call carries 4096 span records (one
-real span and 4095 empty ones), so the span-record arena wraps several times
-while earlier calls are still queued.  The result must equal the oracle's
-single call over all pages, in both directions.
+320 calls exceed the 256 calls the library keeps in flight.  Most move one
+three-page request; every eighth call carries 4096 one-page requests, i.e. 4096
+span records, which go through the pool's 4 MiB device span-record arena
+(256 KiB per such call), so the arena wraps several times while earlier calls are
+still queued and its stretches are reused only after their calls have finished.
+Every request owns distinct pages and staging slots, and some end in a partial
+page.  The result must equal the oracle's single call over all requests, in both
+directions.
 """
 from __future__ import annotations
 
@@ -19,11 +22,15 @@ from paged_layout_transfer_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def test_deep_queue_of_small_calls():
+def test_deep_queue_of_calls_through_the_record_arena():
     dev = torch.device("cuda", 0)
-    L, KV, H, D, E, bs, N, calls = 2, 2, 1, 64, 2, 16, 512, 320
+    L, KV, H, D, E, bs, calls = 2, 1, 1, 32, 2, 2, 320
     tok = H * D * E
-    slot = L * KV * bs * tok
+    big = K.KV_MAX_SPANS
+    n_req = (calls // 8) * big + (calls - calls // 8) * 1
+    n_pages = (calls // 8) * big + (calls - calls // 8) * 3
+    N = n_pages + 1000
+    slot = L * KV * bs * tok                 # one page of every layer per chunk
     pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
                 num_blocks=N, block_stride=bs * tok)
     rng = np.random.default_rng(90_000)
@@ -31,28 +38,38 @@ def test_deep_queue_of_small_calls():
     regions = rng.integers(0, 256, size=(L * KV, N * bs * tok), dtype=np.uint8)
     pool_d = torch.from_numpy(regions).to(dev)
     fresh_d = torch.full_like(pool_d, W.SENTINEL)
-    stg_d = torch.full((calls * slot,), W.SENTINEL, dtype=torch.uint8, device=dev)
     tab_d = torch.from_numpy(table).to(dev)
+
+    # requests: (t_begin, t_end, first_chunk) over the one shared table, pages in order
+    page = chunk = 0
+    call_spans, host_spans = [], []
+    for i in range(calls):
+        reqs = []
+        for _ in range(big if i % 8 == 0 else 1):
+            n = 1 if i % 8 == 0 else 3
+            t0 = page * bs
+            t1 = t0 + n * bs - int(rng.integers(0, 2))      # some end in a partial page
+            reqs.append((t0, t1, chunk))
+            page += n
+            chunk += n
+        call_spans.append(K.make_spans([(tab_d, N, t0, t1, fc) for t0, t1, fc in reqs]))
+        host_spans += [(table, t0, t1, fc) for t0, t1, fc in reqs]
+    assert page == n_pages and len(host_spans) == n_req
+    stg_d = torch.full((chunk * slot,), W.SENTINEL, dtype=torch.uint8, device=dev)
+    spec = K.make_chunk_spec(K.KV_LAYER_FIRST, L, bs, 0, L, stg_d, slot, chunk)
 
     def make(t):
         return K.kv_pool_create(K.make_pool_desc(L, KV, H, D, E, bs, N, bs * tok,
                                                  [t.data_ptr() + i * t.stride(0) for i in range(L * KV)]))
 
-    spec = K.make_chunk_spec(K.KV_LAYER_FIRST, L, bs, 0, L, stg_d, slot, calls)
-    span_sets = []
-    for i in range(calls):
-        real = (tab_d, N, i * bs, (i + 1) * bs, i)
-        if i % 8 == 0:
-            span_sets.append(K.make_spans([real] + [(tab_d, N, 0, 0, 0)] * (K.KV_MAX_SPANS - 1)))
-        else:
-            span_sets.append(K.make_spans([real]))
     src, dst = make(pool_d), make(fresh_d)
     stream = torch.cuda.current_stream()
     try:
-        print("[queue] %d gathers, then %d scatters, no sync between calls" % (calls, calls), flush=True)
-        for sp in span_sets:
+        print("[queue] %d gathers, then %d scatters, %d requests, no sync between calls" % (
+            calls, calls, n_req), flush=True)
+        for sp in call_spans:
             K.kv_gather_chunks(src, sp, spec, stream)
-        for sp in span_sets:
+        for sp in call_spans:
             K.kv_scatter_chunks(dst, sp, spec, stream)
         assert K.kv_pool_get_error(src, stream) == 0 and K.kv_pool_get_error(dst, stream) == 0
         torch.cuda.synchronize()
@@ -63,13 +80,12 @@ def test_deep_queue_of_small_calls():
         K.kv_pool_destroy(dst)
 
     chunks = dict(layout=0, chunk_layers=L, chunk_tokens=bs, layer_begin=0, layer_end=L,
-                  slot_bytes=slot, n_slots=calls)
-    spans = [(table, i * bs, (i + 1) * bs, i) for i in range(calls)]
-    exp_stg = np.full(calls * slot, W.SENTINEL, dtype=np.uint8)
-    oracle.gather(pool, regions, spans, chunks, exp_stg)
+                  slot_bytes=slot, n_slots=chunk)
+    exp_stg = np.full(chunk * slot, W.SENTINEL, dtype=np.uint8)
+    oracle.gather(pool, regions, host_spans, chunks, exp_stg)
     assert np.array_equal(got_stg, exp_stg)
     exp_pool = np.full_like(regions, W.SENTINEL)
-    oracle.scatter(pool, exp_pool, spans, chunks, exp_stg)
+    oracle.scatter(pool, exp_pool, host_spans, chunks, exp_stg)
     assert np.array_equal(got_pool, exp_pool)
 
 
