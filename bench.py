@@ -103,23 +103,105 @@ class DevicePool:
         self.h = None
 
 
-def written_mask_check(direction, pool, spans, chunks, host_regions, host_staging_in, got, layer):
-    """Compare one layer of a GPU result with the oracle.  For a gather, got is the GPU
-    staging buffer and the oracle's written bytes are found by running it over two
-    different fills; for a scatter, got is the list of that layer's GPU regions."""
+SLICE = 1 << 30
+
+
+def to_host(t):
+    """A flat uint8 device tensor copied to a new host array, a slice at a time."""
+    import numpy as np
+    import torch
+    out = np.empty(t.numel(), dtype=np.uint8)
+    ho = torch.from_numpy(out)
+    for a in range(0, t.numel(), SLICE):
+        ho[a:a + SLICE].copy_(t[a:a + SLICE])
+    return out
+
+
+def device_equals(exp, t) -> bool:
+    """exp (host array) equals the flat device tensor t, compared a slice at a time."""
+    import numpy as np
+    if exp.size != t.numel():
+        return False
+    return all(np.array_equal(exp[a:a + SLICE], t[a:a + SLICE].cpu().numpy()) for a in range(0, exp.size, SLICE))
+
+
+def host_cpu():
+    """CPU model and core counts of this host."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(cpu_model=model, nproc=os.cpu_count(), affinity=len(os.sched_getaffinity(0)))
+
+
+def full_parity(P, S, spans_d, spec, spans_h, chunks, pool, w, stream, single_budget_s):
+    """Whole-call parity of the workload against the oracle, every layer, both directions,
+    with the oracle timed on all host cores (the all-core CPU baseline) and, on a bounded
+    sample of layers, on one core.  Gather: the staging buffer starts at the sentinel on
+    both sides and must match in full; scatter: the pool starts at the sentinel on both
+    sides and every region must match in full."""
     import numpy as np
     import oracle
-    if direction == 0:
-        a = np.zeros(got.size, dtype=np.uint8)
-        b = np.full(got.size, 0xFF, dtype=np.uint8)
-        oracle.gather(pool, host_regions, spans, chunks, a, only_layers=(layer, layer + 1))
-        oracle.gather(pool, host_regions, spans, chunks, b, only_layers=(layer, layer + 1))
-        m = a == b
-        return int(m.sum()) > 0 and bool(np.array_equal(got[m], a[m]))
-    regs = [r.copy() if r is not None else None for r in host_regions]
-    oracle.scatter(pool, regs, spans, chunks, host_staging_in, only_layers=(layer, layer + 1))
-    kv = pool["num_kv"]
-    return all(np.array_equal(regs[layer * kv + k], got[k]) for k in range(kv))
+    from paged_layout_transfer_amd import kvxfer as K
+    from paged_layout_transfer_amd import workloads as W
+    L, KV = pool["num_layers"], pool["num_kv"]
+    threads = oracle.max_threads()
+    out = dict(threads=threads)
+    S.fill_(W.SENTINEL)
+    K.kv_gather_chunks(P.h, spans_d, spec, stream)
+    assert K.kv_pool_get_error(P.h, stream) == 0
+    regs = [to_host(P.t[i]) for i in range(L * KV)]
+    exp = np.full(S.numel(), W.SENTINEL, dtype=np.uint8)
+    t0 = time.perf_counter()
+    moved_g = oracle.gather(pool, regs, spans_h, chunks, exp)
+    out["gather_s"] = time.perf_counter() - t0
+    out["gather"] = device_equals(exp, S)
+    # one core: gather layer by layer until the budget is spent
+    oracle.set_threads(1)
+    one = dict(bytes=0, s=0.0, layers=0)
+    scratch = np.empty_like(exp)
+    for l in range(L):
+        if one["s"] >= single_budget_s / 2:
+            break
+        t0 = time.perf_counter()
+        one["bytes"] += oracle.gather(pool, regs, spans_h, chunks, scratch, only_layers=(l, l + 1))
+        one["s"] += time.perf_counter() - t0
+        one["layers"] += 1
+    g_layers = one["layers"]
+    del regs, exp, scratch
+    # scatter
+    W.device_fill_(S, "bytes", 100 + w["k"])
+    src = to_host(S)
+    P.t.fill_(W.SENTINEL)
+    K.kv_scatter_chunks(P.h, spans_d, spec, stream)
+    assert K.kv_pool_get_error(P.h, stream) == 0
+    regs = [np.full(P.t.shape[1], W.SENTINEL, dtype=np.uint8) for _ in range(L * KV)]
+    oracle.set_threads(threads)
+    t0 = time.perf_counter()
+    moved_s = oracle.scatter(pool, regs, spans_h, chunks, src)
+    out["scatter_s"] = time.perf_counter() - t0
+    out["scatter"] = all(device_equals(regs[i], P.t[i]) for i in range(L * KV))
+    oracle.set_threads(1)
+    s_layers = 0
+    t_one = 0.0
+    for l in range(L):
+        if t_one >= single_budget_s / 2:
+            break
+        t0 = time.perf_counter()
+        one["bytes"] += oracle.scatter(pool, regs, spans_h, chunks, src, only_layers=(l, l + 1))
+        t_one += time.perf_counter() - t0
+        s_layers += 1
+    one["s"] += t_one
+    oracle.set_threads(threads)
+    out["moved"] = moved_g + moved_s
+    out["single"] = dict(one, sample="gather of %d/%d layers then scatter of %d/%d layers" % (
+        g_layers, L, s_layers, L))
+    del regs, src
+    return out
 
 
 def hbm_leg(args, dev):
@@ -150,27 +232,17 @@ def hbm_leg(args, dev):
     assert info.payload_bytes == payload
     stream = torch.cuda.current_stream()
 
-    parity = {}
+    parity, cpu = {}, None
     if not args.skip_parity:
-        layer = L - 1
-        K.kv_gather_chunks(P.h, spans_d, spec, stream)
-        assert K.kv_pool_get_error(P.h, stream) == 0
-        host_regions = [None] * (L * KV)
-        for k in range(KV):
-            host_regions[layer * KV + k] = P.t[layer * KV + k].cpu().numpy()
-        got = S.cpu().numpy()
-        parity["gather"] = written_mask_check(0, pool, spans_h, chunks, host_regions, None, got, layer)
-        del got
-        W.device_fill_(S, "bytes", 100 + w["k"])
-        s_host = S.cpu().numpy()
-        K.kv_scatter_chunks(P.h, spans_d, spec, stream)
-        assert K.kv_pool_get_error(P.h, stream) == 0
-        got = [P.t[layer * KV + k].cpu().numpy() for k in range(KV)]
-        parity["scatter"] = written_mask_check(1, pool, spans_h, chunks, host_regions, s_host, got, layer)
-        log("parity (layer %d vs oracle): %s" % (layer, parity))
-        if not all(parity.values()):
+        log("parity: the whole call against the oracle, every layer, both directions")
+        fp = full_parity(P, S, spans_d, spec, spans_h, chunks, pool, w, stream, args.cpu_budget)
+        parity = {"gather": fp["gather"], "scatter": fp["scatter"], "layers": "all %d" % L,
+                  "compared": "whole staging buffer (gather) and every pool region (scatter)"}
+        log("parity: %s; oracle on %d threads %.2f s + %.2f s" % (parity, fp["threads"], fp["gather_s"],
+                                                                 fp["scatter_s"]))
+        if not (fp["gather"] and fp["scatter"]):
             raise SystemExit("parity check failed: %s" % parity)
-        del got, s_host, host_regions
+        cpu = fp
 
     def step(n, which=("g", "s")):
         for _ in range(n):
@@ -200,11 +272,7 @@ def hbm_leg(args, dev):
         K.kv_pool_timing_start(P.h)
         step(max(3, args.steps // 2), which)
         each = K.kv_pool_timing_read_each(P.h)
-        ms, n = float(each.sum()), each.size
-        per_dir[name] = dict(kernel_ms=ms / n, gbs=payload / (ms / n * 1e-3) / 1e9,
-                             hbm_frac=2 * payload / (ms / n * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             kernel_ms_median=float(np.median(each)), kernel_ms_min=float(each.min()),
-                             kernel_ms_max=float(each.max()), launches=n)
+        per_dir[name] = direction_roofline(payload, each)
 
     # The same call with each request's pages in the blocks the library's allocator
     # hands a fresh pool (lowest free ids first, so consecutive runs) instead of the
@@ -281,53 +349,61 @@ def hbm_leg(args, dev):
         achieved=2 * payload / avg_kernel_s / 1e9, per_dir=per_dir, parity=parity,
         d2d_copy_gbs=d2d_gbs, dma=dma, alloc_order=alloc_order, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
         name=args.workload)
-    # keep host copies for the CPU baseline (first layers), then free the device
-    res["host_sample"] = None
-    if args.cpu_baseline:
-        nl = min(L, args.cpu_layers)
-        res["host_sample"] = [P.t[i].cpu().numpy() if i < nl * KV else None for i in range(L * KV)]
-        res["host_sample_layers"] = nl
+    res["cpu"] = cpu
     P.close()
     del P, S, tabs
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(res, budget_s):
-    """The oracle, as it is, on the same step (gather then scatter of the whole
-    request), layer by layer until the time budget is spent."""
+def cpu_baseline(res):
+    """The oracle as it stands, timed on this host in the parity run of the same step
+    (gather then scatter of the whole request): on all cores over every layer, and on
+    one core over a bounded sample of layers."""
+    fp = res.get("cpu")
+    if not fp:
+        return None
+    one = fp["single"]
+    all_s = fp["gather_s"] + fp["scatter_s"]
+    out = dict(value=round(fp["moved"] / all_s / 1e9, 4), unit="GB/s", cores=fp["threads"], kind="oracle",
+               sample="gather then scatter of all %d layers of the %s workload (%.3f GB moved), C oracle with "
+                      "OpenMP over (span, layer) pairs on %d threads, %.1f s" % (
+                          res["pool"]["num_layers"], res["name"], fp["moved"] / 1e9, fp["threads"], all_s),
+               single_core=dict(value=round(one["bytes"] / one["s"] / 1e9, 4), unit="GB/s", cores=1,
+                                sample="%s of the %s workload (%.3f GB moved), %.1f s" % (
+                                    one["sample"], res["name"], one["bytes"] / 1e9, one["s"])))
+    out.update(host_cpu())
+    return out
+
+
+def direction_roofline(payload, each_ms):
+    """One direction's kernel times (ms per launch) as a roofline row: every payload byte
+    is read once and written once in HBM, so the algorithmic traffic per launch is
+    2 x payload; frac is that over the mean kernel time against the 8 TB/s peak."""
     import numpy as np
-    import oracle
-    from paged_layout_transfer_amd import workloads as W
-    w, pool, chunks = res["w"], res["pool"], res["chunks_spec"]
-    regions = res["host_sample"]
-    spans = [(t, t0, t1, fc) for t, (t0, t1), fc in
-             zip(w["block_tables"], w["requests"], W.staging_plan(w)["first_chunk"])]
-    buf = np.zeros(chunks["slot_bytes"] * chunks["n_slots"], dtype=np.uint8)
-    moved, spent, done = 0, 0.0, []
-    for name, fn in (("gather", oracle.gather), ("scatter", oracle.scatter)):
-        n = 0
-        for l in range(res["host_sample_layers"]):
-            if spent >= budget_s:
-                break
-            t0 = time.perf_counter()
-            moved += fn(pool, regions, spans, chunks, buf, only_layers=(l, l + 1))
-            spent += time.perf_counter() - t0
-            n += 1
-        done.append("%s of %d/%d layers" % (name, n, pool["num_layers"]))
-    return dict(value=round(moved / spent / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample="%s of the %s workload (%.3f GB moved), single-threaded C oracle, %.1f s" % (
-                    " then ".join(done), res["name"], moved / 1e9, spent))
+    each = np.asarray(each_ms, dtype=np.float64)
+    mean = float(each.mean())
+    return dict(kernel_ms=round(mean, 4), kernel_ms_median=round(float(np.median(each)), 4),
+                kernel_ms_min=round(float(each.min()), 4), kernel_ms_max=round(float(each.max()), 4),
+                launches=int(each.size), gbs=round(payload / (mean * 1e-3) / 1e9, 1),
+                achieved=round(2 * payload / (mean * 1e-3) / 1e9, 1),
+                hbm_frac=round(2 * payload / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                hbm_frac_of_median=round(2 * payload / (float(np.median(each)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 
 
-def other_workloads(dev, names, reps):
-    """Kernel-time throughput of the other HBM-staged workloads (parity for them is
-    covered by the test suite); each payload byte is read once and written once."""
+def other_workloads(dev, names, reps, before=()):
+    """Kernel-time throughput of the other HBM-staged workloads (their parity at full
+    size is covered by the test suite); each payload byte is read once and written
+    once."""
     import torch
     from paged_layout_transfer_amd import kvxfer as K
     from paged_layout_transfer_amd import workloads as W
     out = {}
     stream = torch.cuda.current_stream()
+    # the workloads' pools are allocated one after another in this process (each freed
+    # before the next); a pool's physical placement, which moves the scatter rate,
+    # depends on what was allocated before it, so each row names those workloads
+    allocated = list(before)
     for name in names:
         w, pool = resolve(name)
         plan = W.staging_plan(w)
@@ -340,18 +416,22 @@ def other_workloads(dev, names, reps):
         spec = K.make_chunk_spec(w["layout"], w["chunk_layers"], w["chunk_tokens"], 0, L, S,
                                  plan["slot_bytes"], plan["n_chunks"])
         info = K.kv_check_transfer(P.desc, spans, spec)
-        row = dict(payload_bytes=info.payload_bytes, requests=len(w["requests"]), tiles=info.tiles)
+        row = dict(payload_bytes=info.payload_bytes, requests=len(w["requests"]), tiles=info.tiles,
+                   pool_bytes=P.t.numel(), staging_bytes=S.numel(),
+                   pool_allocated_after=list(allocated))
         for dn, fn in (("gather", K.kv_gather_chunks), ("scatter", K.kv_scatter_chunks)):
             fn(P.h, spans, spec, stream)
             torch.cuda.synchronize()
             K.kv_pool_timing_start(P.h)
             for _ in range(reps):
                 fn(P.h, spans, spec, stream)
-            ms, n = K.kv_pool_timing_read(P.h)
+            each = K.kv_pool_timing_read_each(P.h)
             assert K.kv_pool_get_error(P.h, stream) == 0
-            t = ms / n * 1e-3
-            row[dn] = dict(kernel_ms=round(ms / n, 4), gbs=round(info.payload_bytes / t / 1e9, 1),
-                           hbm_frac=round(2 * info.payload_bytes / t / 1e9 / HBM_PEAK_GBS, 4))
+            row[dn] = direction_roofline(info.payload_bytes, each)
+        row["roofline"] = dict(bound="hbm", peak=HBM_PEAK_GBS, unit="GB/s",
+                               dominant=max(("gather", "scatter"), key=lambda d: row[d]["kernel_ms"]))
+        row["roofline"]["frac"] = row[row["roofline"]["dominant"]]["hbm_frac"]
+        allocated.append(name)
         out[name] = row
         log("%s: gather %.1f%%, scatter %.1f%% of HBM peak" % (
             name, 100 * row["gather"]["hbm_frac"], 100 * row["scatter"]["hbm_frac"]))
@@ -392,29 +472,39 @@ def host_leg(args, dev):
 
     parity = {}
     try:
-        # parity on the first window, layer 0, both directions
+        # parity on the first window (its layers whole), both directions: the ring and
+        # the window's regions start at the sentinel and must match the oracle in full
         spans_h = [(w["block_tables"][0], 0, T, 0)]
         chunks = dict(layout=0, chunk_layers=w["chunk_layers"], chunk_tokens=w["chunk_tokens"],
                       layer_begin=0, layer_end=win_layers, slot_bytes=slot, n_slots=n_slots)
         if not args.skip_parity:
+            import oracle
+            ring_host[:] = W.SENTINEL
             K.kv_gather_chunks(P.h, spans_d, spec_for(0), stream)
             assert K.kv_pool_get_error(P.h, stream) == 0
-            regs = [P.t[i].cpu().numpy() if i < KV else None for i in range(L * KV)]
-            parity["gather"] = written_mask_check(0, pool, spans_h, chunks, regs, None, ring_host.copy(), 0)
+            regs = [to_host(P.t[i]) if i < win_layers * KV else None for i in range(L * KV)]
+            exp = np.full(slot * n_slots, W.SENTINEL, dtype=np.uint8)
+            oracle.gather(pool, regs, spans_h, chunks, exp, only_layers=(0, win_layers))
+            parity["gather"] = bool(np.array_equal(ring_host, exp))
             rnd = torch.empty(slot * n_slots, dtype=torch.uint8, device=dev)
             W.device_fill_(rnd, "bytes", 103)
             ring_host[:] = rnd.cpu().numpy()
             del rnd
+            P.t[:win_layers * KV].fill_(W.SENTINEL)
             K.kv_scatter_chunks(P.h, spans_d, spec_for(0), stream)
             assert K.kv_pool_get_error(P.h, stream) == 0
-            got = [P.t[k].cpu().numpy() for k in range(KV)]
-            parity["scatter"] = written_mask_check(1, pool, spans_h, chunks, regs, ring_host.copy(), got, 0)
-            log("host-path parity (layer 0 vs oracle): %s" % parity)
-            if not all(parity.values()):
+            regs = [np.full(P.t.shape[1], W.SENTINEL, dtype=np.uint8) if i < win_layers * KV else None
+                    for i in range(L * KV)]
+            oracle.scatter(pool, regs, spans_h, chunks, ring_host.copy(), only_layers=(0, win_layers))
+            parity["scatter"] = all(device_equals(regs[i], P.t[i]) for i in range(win_layers * KV))
+            parity["checked"] = "window 0 (layers 0-%d) whole, both directions" % (win_layers - 1)
+            del regs, exp
+            log("host-path parity: %s" % parity)
+            if not (parity["gather"] and parity["scatter"]):
                 raise SystemExit("host-path parity failed: %s" % parity)
 
         # link reference: one large hipMemcpy each way between ring memory and HBM
-        hip = ctypes.CDLL("libamdhip64.so")
+        hip = K.hip_runtime()
         hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                        ctypes.c_void_p]
         dbuf = torch.empty(slot * n_slots, dtype=torch.uint8, device=dev)
@@ -434,13 +524,13 @@ def host_leg(args, dev):
             link[name] = best
         del dbuf
 
-        def run_pass(fn, windows, wg=0):
+        def run_pass(fn, windows, wg=0, each=False):
             K.kv_pool_timing_start(P.h)
             for i in range(windows):
                 fn(P.h, spans_d, spec_for((i * win_layers) % L, wg), stream)
-            ms, n = K.kv_pool_timing_read(P.h)
+            t = K.kv_pool_timing_read_each(P.h)
             assert K.kv_pool_get_error(P.h, stream) == 0
-            return ms, n
+            return (float(t.sum()), t.size, t) if each else (float(t.sum()), t.size)
 
         dma = {}
         if args.dma_baseline:
@@ -469,13 +559,22 @@ def host_leg(args, dev):
 
         windows = L // win_layers if args.host_windows <= 0 else args.host_windows
         out = {}
+        roof = dict(bound="host link", unit="GB/s",
+                    peak_is="the link rate measured in this run by one large hipMemcpy in the same direction "
+                            "between ring memory and HBM")
         for name, fn, ref in (("scatter", K.kv_scatter_chunks, "h2d"), ("gather", K.kv_gather_chunks, "d2h")):
             run_pass(fn, 1)  # warm-up window
-            ms, n = run_pass(fn, windows)
+            ms, n, each = run_pass(fn, windows, each=True)
             moved = payload_layer * win_layers * windows
             gbs = moved / (ms * 1e-3) / 1e9
             out[name] = dict(gbs=gbs, link_gbs=link[ref], link_frac=gbs / link[ref],
                              bytes=moved, kernel_ms=ms, launches=n)
+            per = payload_layer * win_layers          # bytes one launch (one window) moves
+            roof[name] = dict(achieved=round(gbs, 2), peak=round(link[ref], 2), frac=round(gbs / link[ref], 4),
+                              bytes_per_launch=per, launch_ms_mean=round(float(each.mean()), 4),
+                              launch_ms_median=round(float(np.median(each)), 4),
+                              launch_ms_min=round(float(each.min()), 4), launch_ms_max=round(float(each.max()), 4),
+                              launches=int(each.size))
         sweep = {}
         if args.sweep:
             for wg in (1, 2, 4, 8, 16, 32, 64, 32768):
@@ -490,7 +589,7 @@ def host_leg(args, dev):
                              "request, 2 MiB chunks (1 layer x 512 tokens) through a pinned host ring of "
                              "%d slots (%d layers per window); library default grid for host staging "
                              "(16 workgroups); sweep_gbs keys are max_workgroups" % (n_slots, win_layers),
-                    payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep,
+                    payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep, roofline=roof,
                     per_tile_dma=dma, interference=interference, **out)
     finally:
         K.kv_ring_destroy(ring)
@@ -500,7 +599,8 @@ def host_leg(args, dev):
 
 
 def _hip():
-    lib = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    from paged_layout_transfer_amd import kvxfer as K
+    lib = K.hip_runtime()  # the runtime torch and the library are bound to
     lib.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
                                                  ctypes.POINTER(ctypes.c_uint32)]
     lib.hipStreamDestroy.argtypes = [ctypes.c_void_p]
@@ -585,6 +685,8 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
     io_cus = list(range(8))
     h_io, io = masked(dev, io_cus)
     h_cmp, cmp = masked(dev, [i for i in range(n_cu) if i not in io_cus])
+    # compute alone on all CUs but two: the footprint a 2-workgroup transfer leaves it
+    h_c254, cmp254 = masked(dev, range(2, n_cu))
     out = {"cus": n_cu, "io_cus": io_cus}
     try:
         for kind, n in reps.items():
@@ -592,7 +694,12 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
             work(kind, 3, cmp)
             torch.cuda.synchronize()
             alone, _ = measure(kind, n, whole_c)
-            row = {"alone_ms": round(alone, 4)}
+            work(kind, 3, cmp254)
+            torch.cuda.synchronize()
+            alone_less2, _ = measure(kind, n, cmp254)
+            row = {"alone_ms": round(alone, 4),
+                   "alone_on_%d_cus_ms" % (n_cu - 2): round(alone_less2, 4),
+                   "alone_on_%d_cus_slowdown" % (n_cu - 2): round(alone_less2 / alone - 1, 4)}
             for wg in (2, 0, 32768):
                 t, gbs = measure(kind, n, whole_c, whole_t, wg)
                 row["shared_grid_%s" % (wg if wg else "default16")] = {
@@ -610,7 +717,7 @@ def interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_lay
         assert K.kv_pool_get_error(P.h, whole_t) == 0
     finally:
         torch.cuda.synchronize()
-        for h in (h_io, h_cmp, h_wc, h_wt):
+        for h in (h_io, h_cmp, h_c254, h_wc, h_wt):
             destroy_stream(h)
     log("interference: " + json.dumps(out))
     del ops, x
@@ -773,17 +880,21 @@ def pipeline_leg(args, dev):
         torch.cuda.empty_cache()
 
 
-def traffic_for(algorithmic_bytes_per_launch):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source and on launches of the same algorithmic size."""
+def traffic_for(direction, algorithmic_bytes_per_launch):
+    """HBM bytes per launch of one direction from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the calibration copy's factor),
+    if it was taken on the current kernel source and on launches of the same
+    algorithmic size."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     t = json.load(open(TRAFFIC_FILE))
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    if t.get("algorithmic_bytes_per_launch") != algorithmic_bytes_per_launch:
+    if t.get("algorithmic_bytes_per_launch") != algorithmic_bytes_per_launch or direction not in t:
         return None
-    return t.get("bytes_per_launch")
+    cal = t["calibration"]
+    d = t[direction]
+    return int(round((d["fetch_kib"] * cal["fetch_scale"] + d["write_kib"] * cal["write_scale"]) * 1024))
 
 
 def main():
@@ -798,8 +909,8 @@ def main():
     ap.add_argument("--host-windows", type=int, default=0, help="0 = the whole 80-layer context")
     ap.add_argument("--ring-layers", type=int, default=4, help="layers per ring window")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
-    ap.add_argument("--cpu-layers", type=int, default=32)
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=16.0,
+                    help="seconds of single-core oracle time (gather and scatter halves)")
     ap.add_argument("--no-other-workloads", dest="others", action="store_false",
                     help="skip the other workloads and the allocator-ordered table")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
@@ -826,19 +937,41 @@ def main():
     dev = torch.device("cuda", 0)
 
     res = hbm_leg(args, dev)
-    log("hbm leg: %.1f GB/s moved, kernel avg %.3f ms, %.1f%% of HBM peak" % (
-        res["value"], res["kernel_ms_avg"], 100 * res["achieved"] / HBM_PEAK_GBS))
-    cpu = cpu_baseline(res, args.cpu_budget) if args.cpu_baseline else None
-    res.pop("host_sample", None)
+    log("hbm leg: %.1f GB/s moved, gather %.1f%%, scatter %.1f%% of HBM peak" % (
+        res["value"], 100 * res["per_dir"]["gather"]["hbm_frac"], 100 * res["per_dir"]["scatter"]["hbm_frac"]))
+    cpu = cpu_baseline(res) if args.cpu_baseline else None
     host = host_leg(args, dev) if args.host_path else None
+    before = [args.workload] + (["llama70b"] if args.host_path else [])
     others = other_workloads(dev, ["mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
-                                  "hnd_rows24"], 5) \
+                                  "hnd_rows24"], 5, before) \
         if args.others else None
     pipeline = pipeline_leg(args, dev) if args.pipeline else None
 
     w = res["w"]
+    per_dir = res["per_dir"]
+    # the roofline is quoted for the dominant kernel: the direction with the most GPU time
+    dom = max(per_dir, key=lambda d: per_dir[d]["kernel_ms"])
     # the committed counter summary covers the default workload only
-    traffic = traffic_for(2 * res["payload"]) if args.workload == "llama8b" else None
+    traffic = traffic_for(dom, 2 * res["payload"]) if args.workload == "llama8b" else None
+    roofline = {
+        "bound": "hbm",
+        "achieved": per_dir[dom]["achieved"],
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": per_dir[dom]["hbm_frac"],
+        "traffic": traffic,
+        "kernel": "kvx::tile_copy, %s direction (%s chunks): the longer of the step's two launches, "
+                  "%d launches averaged" % (dom, "layer-first" if w["layout"] == 0 else "page-first",
+                                            per_dir[dom]["launches"]),
+        "directions": {d: {k: per_dir[d][k] for k in ("achieved", "hbm_frac", "kernel_ms", "kernel_ms_median",
+                                                       "kernel_ms_min", "kernel_ms_max", "launches")}
+                       for d in per_dir},
+        "target_frac": 0.70,
+        "below_target": sorted(d for d in per_dir if per_dir[d]["hbm_frac"] < 0.70),
+        "note": "scatter writes each 32 KiB page as an isolated block; its rate depends on where the "
+                "pool's blocks sit (see allocator_ordered_blocks for the same call into the blocks the "
+                "library's allocator hands a fresh pool)",
+    }
     out = {
         "metric": METRIC,
         "value": round(res["value"], 2),
@@ -859,18 +992,9 @@ def main():
             "payload_bytes_each_way": res["payload"], "tiles_per_launch": res["tiles"],
             "chunks": res["chunks"],
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(res["achieved"], 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "kvx::tile_copy (gather and scatter, %s), %d launches averaged" % (
-                "layer-first" if w["layout"] == 0 else "page-first", res["launches"]),
-        },
+        "roofline": roofline,
         "cpu_baseline": cpu,
-        "breakdown": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res["per_dir"].items()},
+        "breakdown": per_dir,
         "d2d_memcpy_gbs": round(res["d2d_copy_gbs"], 1),
         "allocator_ordered_blocks": res["alloc_order"],
         "per_tile_dma": res["dma"],
