@@ -90,6 +90,9 @@ namespace kvx {
 #ifndef KVX_HM_LDS_SLICE
 #define KVX_HM_LDS_SLICE 8192  // LDS bytes per wave, head-major rows not of whole 16-byte vectors
 #endif
+#ifndef KVX_HM_LDS_POOL_NT
+#define KVX_HM_LDS_POOL_NT 1   // nontemporal pool-side words on the LDS-staged head-major paths
+#endif
 #ifndef KVX_HM_LDS_UNROLL
 #define KVX_HM_LDS_UNROLL 8    // 4-byte words per lane in flight, same pages
 #endif

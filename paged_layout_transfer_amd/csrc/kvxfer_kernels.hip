@@ -361,6 +361,20 @@ __device__ __forceinline__ void st_word(gword *p, uint32_t v)
     else *p = v;
 }
 
+// Pool-side words of the LDS-staged paths.  A slab boundary can split a pool line
+// between two slabs of one wave, so whether those accesses bypass the caches is a
+// separate choice (KVX_HM_LDS_POOL_NT).
+template <bool NT>
+__device__ __forceinline__ uint32_t ld_pool_word(const gword *p)
+{
+    return ld_word<NT && KVX_HM_LDS_POOL_NT>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_pool_word(gword *p, uint32_t v)
+{
+    st_word<NT && KVX_HM_LDS_POOL_NT>(p, v);
+}
+
 // Head-major pages whose head rows are not whole 16-byte vectors (rows of rd 4-byte
 // words): slabs [s0, s1) of all heads x tj tokens (hm_lds_tokens) pass through this
 // wave's LDS slice, which holds a slab in chunk (token-major) order, so the chunk side
@@ -416,7 +430,7 @@ __device__ __forceinline__ void copy_head_major_lds(uint32_t *lds, uint8_t *bloc
                 // every lane loads (word 0 of the block where it has nothing to move): a
                 // load behind a lane-dependent branch would wait for all earlier ones
 #pragma unroll
-                for (int u = 0; u < U; ++u) x[u] = ld_word<NT>(pool + (ok[u] ? pw[u] : 0u));
+                for (int u = 0; u < U; ++u) x[u] = ld_pool_word<NT>(pool + (ok[u] ? pw[u] : 0u));
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     if (ok[u]) lds[lw[u]] = x[u];
@@ -426,7 +440,7 @@ __device__ __forceinline__ void copy_head_major_lds(uint32_t *lds, uint8_t *bloc
                     if (ok[u]) x[u] = lds[lw[u]];
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    if (ok[u]) st_word<NT>(pool + pw[u], x[u]);
+                    if (ok[u]) st_pool_word<NT>(pool + pw[u], x[u]);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -500,7 +514,7 @@ __device__ __forceinline__ void hm_lds_scatter_heads(uint32_t *lds, uint8_t *blo
                 if (ok[u]) x[u] = lds[w + 64u * u];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (ok[u]) st_word<NT>(pool + pw[u], x[u]);
+                if (ok[u]) st_pool_word<NT>(pool + pw[u], x[u]);
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -540,7 +554,7 @@ __device__ __forceinline__ void hm_lds_gather_heads(uint32_t *lds, const uint8_t
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (ok[u]) x[u] = ld_word<NT>(pool + pw[u]);
+                if (ok[u]) x[u] = ld_pool_word<NT>(pool + pw[u]);
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (ok[u]) lds[w + 64u * u] = x[u];

@@ -13,7 +13,7 @@ values, so random bytes of the stated element width are used.
 
 Seeds: table/length seed 1000 + k and data seed k for workload k
 (tiny 1, llama8b 2, llama70b 3, mixed 4, mla_fp8 5, int8_kv 6, llama8b_hnd 7,
-fp8_hnd_d64 8, llama8b_tp8 9, hnd_rows24 10).  page_layout (default 0) is the pool's in-page order: 0 token-major
+fp8_hnd_d64 8, llama8b_tp8 9, hnd_rows24 10, hnd_h100_r12 11).  page_layout (default 0) is the pool's in-page order: 0 token-major
 [block_size][H][D], 1 head-major [H][block_size][D].
 """
 from __future__ import annotations
@@ -76,7 +76,21 @@ WORKLOADS: dict[str, dict] = {
                        block_size=64, num_blocks=4096, tokens=32768, fill="bf16_uniform",
                        layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm",
                        page_layout=1),
+    # Many heads with short rows of 4-byte words: 100 heads x 6 bf16 dims = 12-byte rows,
+    # 16-token pages (a token is 1200 bytes, a page 18.75 KiB per (layer, K/V)).
+    "hnd_h100_r12": dict(k=11, num_layers=32, num_kv=2, num_heads=100, head_dim=6, elem_bytes=2,
+                         block_size=16, num_blocks=16384, tokens=32768, fill="bf16_uniform",
+                         layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm",
+                         page_layout=1),
 }
+
+
+def token_major_twin(name: str) -> dict:
+    """The same workload with token-major pages (page_layout 0): same shape, seeds,
+    tables and chunks, so its rate is the reference a head-major pool is judged by."""
+    w = dict(WORKLOADS[name])
+    w["page_layout"] = 0
+    return w
 
 
 def table_rng(k: int) -> np.random.Generator:
