@@ -108,6 +108,7 @@ extern "C" {
 #define KV_ERR_HIP (-6)    /* a HIP runtime call failed (no device, launch failure, ...) */
 #define KV_ERR_DEVICE (-7) /* kv_pool_get_error: the device reported a bad block id */
 #define KV_ERR_DUP (-8)    /* KV_FLAG_VALIDATE: a scatter writes one pool page twice */
+#define KV_ERR_SCRATCH (-9) /* kv_transfer_chunks_noalloc: more regions than its static scratch holds */
 
 /* ---- chunk layouts, in-page layouts, directions, flags ----------------- */
 #define KV_LAYER_FIRST 0
@@ -268,6 +269,28 @@ KV_API int kv_gather_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans
  * KV_FLAG_VALIDATE); then every written byte has exactly one writer. */
 KV_API int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                       const kv_chunk_spec *spec, hipStream_t stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): kv_gather_chunks (direction KV_GATHER) or
+ * kv_scatter_chunks (KV_SCATTER) with the same data model, validation, kernels and
+ * results, but no allocation of any kind on any call, the first included.  The call's
+ * region table and span records go to a static device array of 264.25 KiB that each
+ * device the library runs on holds until the process ends (one stream-ordered
+ * host-to-device copy per call from a host image the pool made at kv_pool_create; the
+ * copy has taken the image's bytes when the call returns), instead of the pool's
+ * arena.  Limits beyond the other entry points': num_layers*num_kv <= 1024 (else
+ * KV_ERR_SCRATCH), and KV_FLAG_VALIDATE is refused (KV_ERR_ARG: its table check
+ * copies to the host).  Every call on one device shares that device's array, which
+ * keeps the last call's contents: calls that overlap on one device (different
+ * streams, or other threads, with no ordering between them) race and must not be
+ * made; calls on one stream are ordered and safe.  A block id out of range is
+ * skipped, as in the other entry points, and its KV_DEVERR_* bit OR-ed into
+ * *err_word, a caller-owned device int32 (4-byte aligned) that the caller clears
+ * and reads; err_word may be NULL to ignore such ids.  kv_pool_get_error does not
+ * see these calls.  Returns after enqueueing. */
+KV_API int kv_transfer_chunks_noalloc(kv_pool *pool, int32_t direction, const kv_span *spans,
+                                      int32_t n_spans, const kv_chunk_spec *spec, int32_t *err_word,
+                                      hipStream_t stream);
 
 /* The conventional engine, for comparison: the same transfer done by the copy
  * engine as one hipMemcpyAsync per (layer, kv, page) tile, issued from the host on

@@ -296,6 +296,8 @@ struct kv_pool {
     // validation scratch (no allocation on the call path)
     std::vector<SpanPlan> plans;
     std::vector<SlotRange> ranges;
+    // host image of the static device scratch (kv_transfer_chunks_noalloc), made at create
+    std::vector<uint64_t> scr_image;
     // device state, created on the first transfer
     int device = -1;
     uint8_t **d_regions = nullptr;
@@ -571,6 +573,72 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     return arena_commit(p, off, rec_bytes, stream);
 }
 
+// The transfer without any allocation: the region table and the span records go to
+// the device's static scratch (one stream-ordered copy from the pool's host image of
+// it, made at create), the error bits to the caller's word.  Nothing is fenced: calls
+// on one stream are ordered, calls that overlap on one device share the scratch.
+int transfer_noalloc(kv_pool *p, int direction, const kv_span *spans, int32_t n_spans,
+                     const kv_chunk_spec *spec, int32_t *err_word, hipStream_t stream)
+{
+    if (!p || (direction != KV_GATHER && direction != KV_SCATTER)) return KV_ERR_ARG;
+    kv_transfer_info info;
+    int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
+    if (rc) return rc;
+    if (spec->flags & KV_FLAG_VALIDATE) return KV_ERR_ARG;  // its table check copies to the host
+    const int64_t n_regions = (int64_t)p->desc.num_layers * p->desc.num_kv;
+    if (n_regions > KVX_SCR_MAX_REGIONS) return KV_ERR_SCRATCH;
+    if (err_word && (reinterpret_cast<uintptr_t>(err_word) & 3u)) return KV_ERR_ALIGN;
+    if (info.tiles == 0) return KV_OK;
+    kvx::AllocRange staging;
+    rc = check_buffers(p, spans, n_spans, spec, true, &staging);
+    if (rc) return rc;
+    if (err_word && check_extent(p->extents, err_word, sizeof(int32_t))) return KV_ERR_RANGE;
+    int dev = -1;
+    if (!HIP_OK(hipGetDevice(&dev))) return KV_ERR_HIP;
+    int herr = 0;
+    uint8_t *scr = static_cast<uint8_t *>(kvx::scratch_address(dev, &herr));
+    if (!scr) {
+        g_hip_error = herr;
+        g_hip_where = "hipGetSymbolAddress(scratch)";
+        return KV_ERR_HIP;
+    }
+
+    uint8_t *img = reinterpret_cast<uint8_t *>(p->scr_image.data());
+    std::memcpy(img + KVX_SCR_REGIONS_OFF, p->bases.data(), (size_t)n_regions * sizeof(void *));
+    kvx::SpanDev *h = reinterpret_cast<kvx::SpanDev *>(img + KVX_SCR_RECORDS_OFF);
+    kvx::Launch a;
+    uint32_t n_rec = 0;
+    rc = prepare_with(&p->desc, spans, n_spans, spec, h, &n_rec, &a, &info, p->plans.data(), p->ranges.data());
+    if (rc) return rc;
+    const bool inline_records = n_rec <= KVX_INLINE_SPANS;
+    if (inline_records) std::memcpy(a.inl, h, n_rec * sizeof(kvx::SpanDev));
+    const int64_t end = inline_records ? KVX_SCR_REGIONS_OFF + n_regions * (int64_t)sizeof(void *)
+                                       : KVX_SCR_RECORDS_OFF + n_rec * (int64_t)sizeof(kvx::SpanDev);
+    // The image is pageable host memory: the runtime has taken its bytes when the copy
+    // call returns, so the next call may rewrite it.
+    if (!HIP_OK(hipMemcpyAsync(scr + KVX_SCR_REGIONS_OFF, img + KVX_SCR_REGIONS_OFF,
+                               (size_t)(end - KVX_SCR_REGIONS_OFF), hipMemcpyHostToDevice, stream)))
+        return KV_ERR_HIP;
+    a.regions = reinterpret_cast<uint8_t *const *>(scr + KVX_SCR_REGIONS_OFF);
+    a.spans = inline_records ? nullptr : reinterpret_cast<const kvx::SpanDev *>(scr + KVX_SCR_RECORDS_OFF);
+    a.err = err_word ? err_word : reinterpret_cast<int32_t *>(scr);
+    a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
+    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
+    uint32_t grid = kvx::default_grid(kvx::work_items(a));
+    if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
+    else if (staging_in_host_memory(p, spec->base, staging)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
+
+    const bool timed = p->timing && p->n_timed < kMaxTimed;
+    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
+    if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))
+        return KV_ERR_HIP;
+    if (timed) {
+        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;
+        ++p->n_timed;
+    }
+    return KV_OK;
+}
+
 // One hipMemcpyAsync per tile, addresses from the same tile resolution the kernel
 // uses, block ids from host tables.
 int transfer_dma(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
@@ -673,6 +741,7 @@ int kv_pool_create(const kv_pool_desc *desc, kv_pool **out)
         p->blocks.init(desc->num_blocks);
         p->plans.resize(KV_MAX_SPANS);
         p->ranges.resize(KV_MAX_SPANS);
+        p->scr_image.assign(KVX_SCR_BYTES / sizeof(uint64_t), 0);
     } catch (...) {
         delete p;
         return KV_ERR_OOM;
@@ -780,6 +849,12 @@ int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                       const kv_chunk_spec *spec, hipStream_t stream)
 {
     return transfer(pool, spans, n_spans, spec, stream, KV_SCATTER);
+}
+
+int kv_transfer_chunks_noalloc(kv_pool *pool, int32_t direction, const kv_span *spans, int32_t n_spans,
+                               const kv_chunk_spec *spec, int32_t *err_word, hipStream_t stream)
+{
+    return transfer_noalloc(pool, direction, spans, n_spans, spec, err_word, stream);
 }
 
 int kv_gather_chunks_dma(kv_pool *pool, const kv_span *spans, int32_t n_spans,
@@ -957,6 +1032,7 @@ const char *kv_strerror(int code)
     case KV_ERR_HIP: return "HIP runtime error";
     case KV_ERR_DEVICE: return "the device reported a block id out of range";
     case KV_ERR_DUP: return "scatter writes one pool page twice";
+    case KV_ERR_SCRATCH: return "the call needs more than the static device scratch holds";
     default: return "unknown error";
     }
 }

@@ -192,6 +192,17 @@ struct Launch {
 };
 static_assert(offsetof(Launch, inl) % alignof(SpanDev) == 0, "inline span records must be aligned SpanDev objects");
 
+// The static device scratch of kv_transfer_chunks_noalloc (kvxfer_kernels.hip):
+//   [0, 256)                 a sink for the error bits when the caller passes no error word
+//   [KVX_SCR_REGIONS_OFF, +8 * KVX_SCR_MAX_REGIONS)   the call's region table
+//   [KVX_SCR_RECORDS_OFF, +64 * KV_MAX_SPANS)         the call's span records (when more
+//                                                     than KVX_INLINE_SPANS)
+#define KVX_SCR_MAX_REGIONS 1024
+#define KVX_SCR_REGIONS_OFF 256
+#define KVX_SCR_RECORDS_OFF (KVX_SCR_REGIONS_OFF + 8 * KVX_SCR_MAX_REGIONS)
+#define KVX_SCR_BYTES (KVX_SCR_RECORDS_OFF + 64 * KV_MAX_SPANS)
+#define KVX_MAX_DEVICES 64
+
 // Kernel-internal page layout values: head-major pages staged through LDS in token
 // slabs, and in head-group slabs (hm_lds_head_slab).
 #define KVX_PAGE_HM_LDS 2
@@ -476,5 +487,9 @@ int launch_tile_copy(int direction, const Launch &a, uint32_t grid, hipStream_t 
 
 // Default grid for a call of `items` work items (tiles x parts).
 uint32_t default_grid(int64_t items);
+
+// Device address of the static scratch on `device` (which must be current), looked up
+// once per device; nullptr with *hip_error set if the lookup fails (kernel file).
+void *scratch_address(int device, int *hip_error);
 
 }  // namespace kvx

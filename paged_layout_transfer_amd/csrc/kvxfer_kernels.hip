@@ -28,10 +28,38 @@
 // 128K-token 70B-shaped transfer exceeds).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kvxfer.h"
 #include "kvxfer_internal.h"
 
+// Device memory of kv_transfer_chunks_noalloc, for callers that cannot allocate: the
+// region table and span records of one call (layout in kvxfer_internal.h, KVX_SCR_*).
+// Each device the library runs on holds its own copy until the process ends; host code
+// reaches it only through the address scratch_address() looked up on that device.
+static __device__ __align__(256) uint8_t scratch[KVX_SCR_BYTES];
+
 namespace kvx {
+
+void *scratch_address(int device, int *hip_error)
+{
+    static std::atomic<void *> addr[KVX_MAX_DEVICES];
+    if (device < 0 || device >= KVX_MAX_DEVICES) {
+        *hip_error = (int)hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void *p = addr[device].load(std::memory_order_acquire);
+    if (p) return p;
+    // the caller has made `device` current; the symbol resolves to that device's copy
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        *hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    addr[device].store(p, std::memory_order_release);
+    return p;
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

@@ -60,6 +60,8 @@ _sig("kv_validate_targets", ctypes.c_int, ctypes.POINTER(kv_pool_desc), ctypes.P
      ctypes.POINTER(_P), _I32)
 _sig("kv_gather_chunks", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
 _sig("kv_scatter_chunks", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
+_sig("kv_transfer_chunks_noalloc", ctypes.c_int, _P, _I32, ctypes.POINTER(kv_span), _I32,
+     ctypes.POINTER(kv_chunk_spec), _P, _P)
 _sig("kv_gather_chunks_dma", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
 _sig("kv_scatter_chunks_dma", ctypes.c_int, _P, ctypes.POINTER(kv_span), _I32, ctypes.POINTER(kv_chunk_spec), _P)
 _sig("kv_pool_get_error", ctypes.c_int, _P, _P, ctypes.POINTER(_I32))
@@ -79,7 +81,8 @@ _sig("kv_last_hip_error", ctypes.c_int, ctypes.POINTER(ctypes.c_char_p))
 LIBRARY_PATH = _LIB_PATH
 EXPORTED = ("kv_pool_create", "kv_pool_destroy", "kv_pool_alloc_blocks", "kv_pool_free_blocks",
             "kv_pool_free_count", "kv_check_transfer", "kv_chunk_bytes", "kv_validate_targets",
-            "kv_gather_chunks", "kv_scatter_chunks", "kv_gather_chunks_dma", "kv_scatter_chunks_dma",
+            "kv_gather_chunks", "kv_scatter_chunks", "kv_transfer_chunks_noalloc",
+            "kv_gather_chunks_dma", "kv_scatter_chunks_dma",
             "kv_pool_get_error", "kv_pool_timing_start",
             "kv_pool_timing_read", "kv_pool_timing_read_each", "kv_ring_create", "kv_ring_slot", "kv_ring_destroy",
             "kv_ring_record", "kv_ring_wait", "kv_ring_stream_wait",
@@ -168,6 +171,16 @@ def kv_gather_chunks(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None
 def kv_scatter_chunks(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:
     _check(_lib.kv_scatter_chunks(pool, spans, _nspans(spans), ctypes.byref(spec), _stream(stream)),
            "kv_scatter_chunks")
+
+
+def kv_transfer_chunks_noalloc(pool: int, direction: int, spans, spec: kv_chunk_spec, err_word=None,
+                               stream=None) -> None:
+    """Gather or scatter with no allocation (static device scratch); err_word is a
+    caller-owned device int32 (address or tensor) that receives KV_DEVERR_* bits, or None."""
+    _check(_lib.kv_transfer_chunks_noalloc(pool, direction, spans, _nspans(spans), ctypes.byref(spec),
+                                           _addr(err_word) if err_word is not None else None,
+                                           _stream(stream)),
+           "kv_transfer_chunks_noalloc")
 
 
 def kv_gather_chunks_dma(pool: int, spans, spec: kv_chunk_spec, stream=None) -> None:

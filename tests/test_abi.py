@@ -58,7 +58,7 @@ def test_header_constants_match_binding():
 def test_version_and_strerror():
     assert K.kv_version() == K.KV_VERSION
     codes = [K.KV_OK, K.KV_ERR_ARG, K.KV_ERR_ALIGN, K.KV_ERR_RANGE, K.KV_ERR_OOM, K.KV_ERR_RING,
-             K.KV_ERR_HIP, K.KV_ERR_DEVICE, K.KV_ERR_DUP]
+             K.KV_ERR_HIP, K.KV_ERR_DEVICE, K.KV_ERR_DUP, K.KV_ERR_SCRATCH]
     msgs = [K.kv_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert K.kv_strerror(12345) == "unknown error"
@@ -339,3 +339,30 @@ def test_ring_functions_reject_null_handles():
         assert fn(*args) == K.KV_ERR_ARG
     assert K._lib.kv_ring_destroy(None) == K.KV_OK
     assert K._lib.kv_pool_destroy(None) == K.KV_OK
+
+
+def test_noalloc_entry_refuses_before_any_hip_call():
+    """The no-allocation entry point's own limits are checked on the host first: a bad
+    direction, KV_FLAG_VALIDATE (its table check copies to the host), more regions than
+    its static scratch holds, a misaligned error word; an empty call is a no-op."""
+    h = K.kv_pool_create(_desc())
+    try:
+        sp = K.make_spans([_span()])
+        for direction, spec, err, code in ((7, _spec(), None, K.KV_ERR_ARG),
+                                           (K.KV_GATHER, _spec(flags=K.KV_FLAG_VALIDATE), None, K.KV_ERR_ARG),
+                                           (K.KV_SCATTER, _spec(), FAKE + 2, K.KV_ERR_ALIGN)):
+            with pytest.raises(K.KvError) as e:
+                K.kv_transfer_chunks_noalloc(h, direction, sp, spec, err)
+            assert e.value.code == code
+        K.kv_transfer_chunks_noalloc(h, K.KV_GATHER, K.make_spans([_span(t1=0)]), _spec())
+    finally:
+        K.kv_pool_destroy(h)
+    L = 513  # 1026 regions
+    big = K.kv_pool_create(_desc(L=L, bases=[FAKE + i * (1 << 24) for i in range(2 * L)]))
+    try:
+        with pytest.raises(K.KvError) as e:
+            K.kv_transfer_chunks_noalloc(big, K.KV_SCATTER, K.make_spans([_span()]),
+                                         _spec(chunk_layers=L, layer_end=L, slot_bytes=L * 2 * 256 * 256))
+        assert e.value.code == K.KV_ERR_SCRATCH
+    finally:
+        K.kv_pool_destroy(big)

@@ -1,0 +1,123 @@
+"""kv_transfer_chunks_noalloc (static device scratch, no allocation) against the
+allocating entry points kv_gather_chunks / kv_scatter_chunks, through the C ABI.
+
+Each case runs the same call both ways on identical device inputs and compares the
+whole pool and the whole staging buffer byte for byte (and with the oracle).  Two
+noalloc calls are queued back to back on one stream with no synchronisation: the
+first with more span records than ride in the kernel arguments (so they go through
+the static scratch), the second a smaller call, which reuses the scratch the first
+one left behind.  A block id out of range must set the caller's error word.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import cases
+import oracle
+from paged_layout_transfer_amd import kvxfer as K
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        raise RuntimeError("needs a ROCm GPU")
+    return torch.device("cuda", 0)
+
+
+class Call:
+    """One case's inputs on the device, twice (one copy per entry point)."""
+
+    def __init__(self, pool, spans, chunks, seed, dev):
+        rng = np.random.default_rng(seed)
+        self.pool, self.spans, self.chunks = pool, spans, chunks
+        self.regions = cases.regions_for(pool, rng)
+        self.staging = cases.staging_for(chunks, rng=rng)
+        self.tabs = [torch.from_numpy(np.ascontiguousarray(t, dtype=np.int32)).to(dev) for t, _, _, _ in spans]
+        self.sp = K.make_spans([(tb.data_ptr(), tb.numel(), t0, t1, fc)
+                                for tb, (_, t0, t1, fc) in zip(self.tabs, spans)])
+        self.sides = []
+        for _ in range(2):
+            buf = torch.from_numpy(self.regions.copy()).to(dev)
+            stg = torch.from_numpy(self.staging.copy()).to(dev)
+            bases = [buf.data_ptr() + i * buf.stride(0) for i in range(buf.shape[0])]
+            desc = K.make_pool_desc(pool["num_layers"], pool["num_kv"], pool["num_heads"], pool["head_dim"],
+                                    pool["elem_bytes"], pool["block_size"], pool["num_blocks"],
+                                    pool["block_stride"], bases, pool.get("page_layout", 0))
+            spec = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"],
+                                     chunks["layer_begin"], chunks["layer_end"], stg, chunks["slot_bytes"],
+                                     chunks["n_slots"])
+            self.sides.append(dict(buf=buf, stg=stg, h=K.kv_pool_create(desc), spec=spec))
+
+    def close(self):
+        for s in self.sides:
+            K.kv_pool_destroy(s["h"])
+
+    def results(self):
+        return [(s["buf"].cpu().numpy(), s["stg"].cpu().numpy()) for s in self.sides]
+
+    def expected(self, direction):
+        regs, stg = self.regions.copy(), self.staging.copy()
+        oracle.transfer(direction, self.pool, [regs[i] for i in range(regs.shape[0])], self.spans, self.chunks, stg)
+        return regs, stg
+
+
+def _case(seed, n_spans, medium):
+    return cases.make_case(np.random.default_rng(seed), tok_multiple=16, n_spans=n_spans, medium=medium,
+                           max_bytes=(32 << 20) if medium else (4 << 20), head_major=None)
+
+
+@pytest.mark.parametrize("direction", [K.KV_GATHER, K.KV_SCATTER])
+def test_noalloc_matches_the_allocating_entry_point_on_two_calls_in_a_row(direction):
+    dev = _dev()
+    stream = torch.cuda.current_stream()
+    big = Call(*_case(81_000 + direction, 40, True), seed=1 + direction, dev=dev)
+    small = Call(*_case(82_000 + direction, 3, False), seed=3 + direction, dev=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    fn = K.kv_gather_chunks if direction == K.KV_GATHER else K.kv_scatter_chunks
+    try:
+        torch.cuda.synchronize()
+        print("[noalloc] %s: 40-record call then 3-record call, no sync between" % (
+            "gather" if direction == K.KV_GATHER else "scatter"), flush=True)
+        for c in (big, small):
+            fn(c.sides[0]["h"], c.sp, c.sides[0]["spec"], stream)
+        for c in (big, small):
+            K.kv_transfer_chunks_noalloc(c.sides[1]["h"], direction, c.sp, c.sides[1]["spec"], err, stream)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert K.kv_pool_get_error(big.sides[0]["h"], stream) == 0
+        for c in (big, small):
+            (r0, s0), (r1, s1) = c.results()
+            assert np.array_equal(s1, s0), "staging differs from the allocating entry point"
+            assert np.array_equal(r1, r0), "pool differs from the allocating entry point"
+            er, es = c.expected(direction)
+            assert np.array_equal(s1, es) and np.array_equal(r1, er), "differs from the oracle"
+    finally:
+        big.close()
+        small.close()
+
+
+def test_noalloc_reports_a_bad_block_id_in_the_callers_word():
+    dev = _dev()
+    stream = torch.cuda.current_stream()
+    pool, spans, chunks = _case(83_000, 2, False)
+    tbl, t0, t1, fc = spans[0]
+    bad = tbl.copy()
+    bad[t0 // pool["block_size"]] = pool["num_blocks"] + 5
+    spans[0] = (bad, t0, t1, fc)
+    c = Call(pool, spans, chunks, seed=9, dev=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    try:
+        torch.cuda.synchronize()
+        print("[noalloc] poisoned block id, both entry points", flush=True)
+        K.kv_gather_chunks(c.sides[0]["h"], c.sp, c.sides[0]["spec"], stream)
+        K.kv_transfer_chunks_noalloc(c.sides[1]["h"], K.KV_GATHER, c.sp, c.sides[1]["spec"], err, stream)
+        torch.cuda.synchronize()
+        assert int(err.item()) == K.KV_DEVERR_BLOCK_RANGE
+        assert K.kv_pool_get_error(c.sides[0]["h"], stream) == K.KV_DEVERR_BLOCK_RANGE
+        (r0, s0), (r1, s1) = c.results()
+        assert np.array_equal(s1, s0) and np.array_equal(r1, r0)
+    finally:
+        c.close()
