@@ -244,6 +244,10 @@ int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
             a->hm_tj = kvx::hm_lds_tokens(row, tok_bytes(d), (uint32_t)d->block_size);
             a->hm_m_rd = kvx::magic_u16(a->hm_rd);
             a->hm_m_run = kvx::magic_u16(a->hm_tj * a->hm_rd);
+            if (kvx::hm_page_ok(a->page_layout, row, tok_bytes(d), tok_bytes(d) * d->block_size)) {
+                a->hm_page = 1;
+                a->hm_m_brd = kvx::magic_u16((uint32_t)d->block_size * a->hm_rd);
+            }
             for (int dir = 0; dir < 2; ++dir) {
                 kvx::hm_lds_head_slab(dir, H, row, tok_bytes(d), (uint32_t)d->block_size, &a->hm_hg[dir],
                                       &a->hm_htj[dir]);
@@ -556,7 +560,7 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     a.spans = inline_records ? nullptr : dd;
     a.err = p->d_err;
 
-    a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
+    a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
@@ -622,7 +626,7 @@ int transfer_noalloc(kv_pool *p, int direction, const kv_span *spans, int32_t n_
     a.regions = reinterpret_cast<uint8_t *const *>(scr + KVX_SCR_REGIONS_OFF);
     a.spans = inline_records ? nullptr : reinterpret_cast<const kvx::SpanDev *>(scr + KVX_SCR_RECORDS_OFF);
     a.err = err_word ? err_word : reinterpret_cast<int32_t *>(scr);
-    a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
+    a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);

@@ -90,6 +90,12 @@ namespace kvx {
 #ifndef KVX_HM_LDS_SLICE
 #define KVX_HM_LDS_SLICE 8192  // LDS bytes per wave, head-major rows not of whole 16-byte vectors
 #endif
+#ifndef KVX_HM_PAGE_SLICE
+#define KVX_HM_PAGE_SLICE 20480  // LDS bytes per wave, head-major pages of 4-byte-word rows moved whole
+#endif
+#ifndef KVX_HM_PAGE_GROUP
+#define KVX_HM_PAGE_GROUP 8      // 16-byte vectors per lane in flight, same pages
+#endif
 #ifndef KVX_HM_LDS_POOL_NT
 #define KVX_HM_LDS_POOL_NT 1   // nontemporal pool-side words on the LDS-staged head-major paths
 #endif
@@ -186,6 +192,11 @@ struct Launch {
     uint32_t hm_htj[2];
     uint64_t hm_m_hrun[2];
     uint64_t hm_m_hgrp[2];
+    // head-major pages of 4-byte-word rows moved a whole page at a time (hm_page_ok), with
+    // the multiplier dividing by the words of one head's page (block_size * hm_rd)
+    uint32_t hm_page;
+    uint32_t hm_pad_;
+    uint64_t hm_m_brd;
     // the span records themselves when n_spans <= KVX_INLINE_SPANS (spans is then
     // unused): 64-byte SpanDev images, read by the kernel from its argument memory
     uint64_t inl[KVX_INLINE_SPANS * sizeof(SpanDev) / sizeof(uint64_t)];
@@ -204,9 +215,10 @@ static_assert(offsetof(Launch, inl) % alignof(SpanDev) == 0, "inline span record
 #define KVX_MAX_DEVICES 64
 
 // Kernel-internal page layout values: head-major pages staged through LDS in token
-// slabs, and in head-group slabs (hm_lds_head_slab).
+// slabs, in head-group slabs (hm_lds_head_slab), and a whole page at a time (hm_page_ok).
 #define KVX_PAGE_HM_LDS 2
 #define KVX_PAGE_HM_LDS_HEADS 3
+#define KVX_PAGE_HM_LDS_PAGE 4
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
 // vector q of that head's row -- and its offset (in vectors) inside a head-major
@@ -320,6 +332,13 @@ __host__ __device__ constexpr uint32_t split_shift_for(int dir, int64_t tile_byt
     return sh;
 }
 
+// log2 of the parts each tile of a prepared call is split into for direction dir: a
+// head-major page moved whole through one wave's slice (hm_page) is never split.
+__host__ __device__ inline uint32_t launch_split_shift(const Launch &a, int dir)
+{
+    return a.hm_page ? 0u : split_shift_for(dir, a.tile_bytes);
+}
+
 // Head-major pages whose head rows are 256 bytes (16 vectors, one 16-lane row of a
 // wave) with heads and page tokens in multiples of 4 are moved in blocks of 4 tokens x
 // 4 heads: four 1 KiB accesses on each side, transposed in registers in between.
@@ -342,6 +361,15 @@ __host__ __device__ inline uint32_t hm_t4_units(uint32_t n_tok, uint32_t heads)
 __host__ __device__ constexpr bool hm_lds_ok(uint32_t page_layout, int64_t row, int64_t tok)
 {
     return page_layout == KV_PAGE_HEAD_MAJOR && row % 16 != 0 && row % 4 == 0 && tok <= KVX_HM_LDS_SLICE;
+}
+
+// Head-major pages of 4-byte-word rows whose page is larger than a token slab's slice
+// but fits a page slice are moved a whole page at a time: the block is one contiguous
+// run of tile_bytes, read or written in 16-byte vectors, and transposed in LDS; so no
+// pool line is split between slabs.
+__host__ __device__ constexpr bool hm_page_ok(uint32_t page_layout, int64_t row, int64_t tok, int64_t tile)
+{
+    return hm_lds_ok(page_layout, row, tok) && tile > KVX_HM_LDS_SLICE && tile <= KVX_HM_PAGE_SLICE;
 }
 
 // Tokens per LDS slab (a slab is all heads of whole tokens: one contiguous run of the
@@ -419,6 +447,32 @@ __host__ __device__ constexpr uint64_t magic_u16(uint32_t d)
 __host__ __device__ inline uint32_t mdiv(uint32_t n, uint64_t m)
 {
     return (uint32_t)(((uint64_t)n * m) >> 32);
+}
+
+// Slice words of the four 4-byte words of pool vector v of a head-major page moved whole
+// (hm_page_ok), ~0u for a word of a token at or past n_tok.  Pool word w = (h*bs + j)*rd
+// + q of the block [H][bs][rd] goes to slice word (j*H + h)*rd + q of the tile in chunk
+// order [n_tok][H][rd]; the first word's h = w / (bs*rd) and j = (w - h*bs*rd) / rd are
+// multiply-high divisions (magic_u16: exact, as w < 2^16), the next three follow by
+// carrying q into j and j into h.
+__host__ __device__ inline void hm_page_slice_words(const Launch &a, uint32_t v, uint32_t n_tok, uint32_t sw[4])
+{
+    const uint32_t H = a.hm_heads, rd = a.hm_rd, bs = a.block_size, brd = bs * rd;
+    const uint32_t w = 4u * v;
+    uint32_t h = mdiv(w, a.hm_m_brd);
+    const uint32_t r = w - h * brd;
+    uint32_t j = mdiv(r, a.hm_m_rd);
+    uint32_t q = r - j * rd;
+    for (int c = 0; c < 4; ++c) {
+        sw[c] = j < n_tok ? (j * H + h) * rd + q : ~0u;
+        if (++q == rd) {
+            q = 0;
+            if (++j == bs) {
+                j = 0;
+                ++h;
+            }
+        }
+    }
 }
 
 // Segment size for a gather over tiles of tile_bytes (0: one tile per wave item).

@@ -613,6 +613,95 @@ __device__ __forceinline__ void hm_lds_gather_heads(uint32_t *lds, const uint8_t
     }
 }
 
+// Head-major pages of 4-byte-word rows moved a whole page at a time (hm_page_ok): the
+// block, [H][bs][rd] words, is one contiguous run of tile_bytes, and the tile of n_tok
+// tokens one contiguous run of n_tok*H*rd words in the chunk, [n_tok][H][rd].  Both
+// runs are moved in 16-byte vectors, KVX_HM_PAGE_GROUP of them per lane in flight, and
+// the transposition is done by where each 4-byte word goes in this wave's LDS slice,
+// which holds the tile in chunk order (hm_page_slice_words).
+// Gather reads the whole block (the buffer range keeps the loads inside it) and drops
+// words of tokens past n_tok; scatter writes whole pool vectors when the page is full,
+// and single words of the tile's tokens when it is partial.  Only this wave uses its
+// slice and a wave's LDS accesses complete in order, so wave_barrier only keeps the
+// compiler from moving accesses across a phase boundary.
+template <int DIR, bool NT>
+__device__ __forceinline__ void copy_head_major_page(uint32_t *lds, uint8_t *block, uint8_t *chunk_tile,
+                                                     uint32_t n_tok, uint32_t lane, const Launch &a)
+{
+    constexpr int G = KVX_HM_PAGE_GROUP;           // 16-byte vectors per lane in flight
+    const uint32_t bs = a.block_size;
+    const uint32_t page_vec = (uint32_t)(a.tile_bytes >> 4);
+    const uint32_t tile_vec = n_tok * a.tok / 16u;
+    if (DIR == KV_GATHER) {
+        const BufSide<kGatherPoolPol<NT>> in(block, page_vec * 16u);
+        const BufSide<kGatherChunkPol<NT>> out(chunk_tile, tile_vec * 16u);
+        for (uint32_t v0 = lane; v0 < page_vec; v0 += 64u * G) {
+            u32x4 x[G];
+#pragma unroll
+            for (int k = 0; k < G; ++k) x[k] = in.load(v0 + 64u * k);  // past the block: dropped by the range
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const uint32_t v = v0 + 64u * k;
+                if (v < page_vec) {
+                    uint32_t sw[4];
+                    hm_page_slice_words(a, v, n_tok, sw);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (sw[c] != ~0u) lds[sw[c]] = x[k][c];
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (uint32_t v0 = lane; v0 < tile_vec; v0 += 64u * G)
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const uint32_t v = v0 + 64u * k;
+                if (v < tile_vec) out.store(v, *(const u32x4 *)(lds + 4u * v));
+            }
+        __builtin_amdgcn_wave_barrier();
+        return;
+    }
+    const PtrSide<NT> in{as_global(chunk_tile)};
+    for (uint32_t v0 = lane; v0 < tile_vec; v0 += 64u * G) {
+        u32x4 x[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const uint32_t v = v0 + 64u * k;
+            x[k] = in.load(v < tile_vec ? v : tile_vec - 1u);  // clamped: no load behind a lane-dependent branch
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (v0 + 64u * k < tile_vec) *(u32x4 *)(lds + 4u * (v0 + 64u * k)) = x[k];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (n_tok == bs) {  // a full page: every pool vector is the tile's
+        gvec *const pool = as_global(block);
+        for (uint32_t v0 = lane; v0 < page_vec; v0 += 64u * G)
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const uint32_t v = v0 + 64u * k;
+                if (v < page_vec) {
+                    uint32_t sw[4];
+                    hm_page_slice_words(a, v, n_tok, sw);
+                    u32x4 y;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) y[c] = lds[sw[c]];
+                    st<NT>(pool + v, y);
+                }
+            }
+    } else {            // a partial page: only the words of the tile's tokens
+        gword *const pool = (gword *)block;
+        for (uint32_t v = lane; v < page_vec; v += 64u) {
+            uint32_t sw[4];
+            hm_page_slice_words(a, v, n_tok, sw);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (sw[c] != ~0u) st_pool_word<NT>(pool + 4u * v + c, lds[sw[c]]);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 // SEG = 0: the tile walk; SEG = 2, 4 or 8: the segment walk (gather of token-major
 // pages), in groups of SEG vectors per lane (gather_seg_unroll).
 template <int DIR, int LAYOUT, int PAGE, bool NT, int SEG>
@@ -672,6 +761,12 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         uint32_t first, count;
         uint8_t *block = as_const(a.regions)[t.region] + (int64_t)blk * a.block_stride;
         uint8_t *chunk_tile = a.chunk_base + t.chunk_off;
+        if constexpr (PAGE == KVX_PAGE_HM_LDS_PAGE) {
+            // a whole page per wave (tiles of at most KVX_HM_PAGE_SLICE bytes are never split)
+            __shared__ __attribute__((aligned(16))) uint32_t pages[kWavesPerBlock][KVX_HM_PAGE_SLICE / 4];
+            copy_head_major_page<DIR, NT>(pages[wave], block, chunk_tile, t.nbytes / a.tok, lane, a);
+            continue;
+        }
         if constexpr (PAGE == KVX_PAGE_HM_LDS || PAGE == KVX_PAGE_HM_LDS_HEADS) {
             // parts of a split tile are ranges of slabs
             __shared__ __attribute__((aligned(16))) uint32_t slices[kWavesPerBlock][KVX_HM_LDS_SLICE / 4];
@@ -738,6 +833,7 @@ template <int DIR, int LAYOUT>
 static const void *pick_page(const Launch &a)
 {
     if (a.page_layout == KV_PAGE_HEAD_MAJOR) {
+        if (a.hm_page) return pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS_PAGE>(a);
         if (a.hm_lds && a.hm_hg[DIR]) return pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS_HEADS>(a);
         return a.hm_lds ? pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS>(a)
                         : pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a);

@@ -118,17 +118,20 @@ def staging_for(chunks: dict, fill: int | None = None, rng: np.random.Generator 
     return np.full(n, 0xA5 if fill is None else fill, dtype=np.uint8)
 
 
-# H, D, E, bs: head rows not of whole 16-byte vectors (4-byte words), staged through LDS
-# in 8 KiB slabs of all heads x tokens: a whole page; tokens cut to whole pool lines
-# (20 x 12-byte rows: 34 fit, 32 taken, pages of 64; 16 x 24-byte rows: 21 fit, 16
-# taken); too few for a whole line (4 x 100-byte rows: 20 fit, 32 would be needed);
-# one token (64 x 100-byte rows).  Where a token slab would split pool lines (100 x
-# 12-byte rows: 6 tokens fit, 32 would be needed; 128 x 8-byte rows: 8 fit, 16
-# needed), scatter takes slabs of whole pages of a group of heads (25 of 100, 32 of
-# 128), and so does gather where the group's chunk runs are whole lines (32 x 8 bytes).
+# H, D, E, bs: head rows not of whole 16-byte vectors (4-byte words), staged through LDS.
+# Pages of at most 8 KiB go in token slabs of a whole page; pages of 8-20 KiB a whole page
+# at a time in 16-byte vectors (20 x 12-byte rows, pages of 64; 100 x 12-byte rows,
+# pages of 16; 32 x 8-byte rows, pages of 48; 24 x 12-byte rows, pages of 64); larger
+# pages in 8 KiB slabs of all heads x tokens, tokens cut to whole pool lines (16 x
+# 24-byte rows: 21 fit, 16 taken); too few for a whole line (4 x 100-byte rows: 20 fit,
+# 32 would be needed); one token (64 x 100-byte rows).  Where a token slab would split
+# pool lines (100 x 12-byte rows in pages of 32: 6 tokens fit, 32 would be needed; 128 x
+# 8-byte rows: 8 fit, 16 needed), scatter takes slabs of whole pages of a group of heads
+# (20 of 100, 32 of 128), and so does gather where the group's chunk runs are whole lines
+# (32 x 8 bytes).
 HM_LDS_SHAPES = [(4, 2, 2, 16), (2, 4, 2, 16), (4, 6, 2, 8), (8, 8, 1, 16), (4, 10, 2, 32), (2, 12, 2, 64),
                  (16, 12, 2, 64), (20, 3, 4, 64), (64, 100, 1, 4), (2, 1, 8, 16), (128, 8, 1, 32),
-                 (4, 100, 1, 128), (100, 6, 2, 16)]
+                 (4, 100, 1, 128), (100, 6, 2, 16), (100, 6, 2, 32), (32, 2, 4, 48), (24, 3, 4, 64)]
 
 
 def head_major_case(rng: np.random.Generator, H: int, D: int, E: int, bs: int):

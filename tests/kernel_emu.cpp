@@ -70,7 +70,7 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     for (int32_t i = 0; i < n_spans; ++i)
         if (spans[i].t_end > spans[i].t_begin) tlen.push_back(spans[i].table_len);
 
-    a.split_shift = kvx::split_shift_for(direction, a.tile_bytes);
+    a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
@@ -151,8 +151,9 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     // numbered in chunk order), and every slice word read was written in the same slab
     const int64_t twords = a.tile_bytes / 4;
     std::vector<uint64_t> wwritten(a.hm_lds ? (size_t)((info.tiles * twords + 63) / 64) : 0, 0);
-    std::vector<uint32_t> slice(KVX_HM_LDS_SLICE / 4);
-    std::vector<int64_t> tag(KVX_HM_LDS_SLICE / 4, -1);
+    const size_t slice_words = (size_t)std::max(KVX_HM_LDS_SLICE, KVX_HM_PAGE_SLICE) / 4;
+    std::vector<uint32_t> slice(slice_words);
+    std::vector<int64_t> tag(slice_words, -1);
     int64_t gen = 0;
     const int64_t step = (int64_t)grid * kvx::kWavesPerBlock;
     const int64_t nreg = (int64_t)d->num_layers * d->num_kv;
@@ -183,6 +184,83 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
                     continue;
                 }
                 uint32_t first, count;
+                if (a.page_layout == KV_PAGE_HEAD_MAJOR && a.hm_page) {
+                    // the kernel's whole-page walk: 16-byte vectors on both sides, words placed
+                    // in the slice by hm_page_slice_words, which is checked against plain division
+                    const uint32_t n_tok = t.nbytes / a.tok, H = a.hm_heads, rd = a.hm_rd, bs = a.block_size;
+                    const uint32_t page_vec = (uint32_t)(a.tile_bytes / 16), tile_vec = n_tok * a.tok / 16;
+                    if (split != 1 || a.tile_bytes > KVX_HM_PAGE_SLICE || a.tile_bytes != (int64_t)H * bs * rd * 4 ||
+                        poff + a.tile_bytes > region_bytes[t.region]) {
+                        ++*violations;
+                        continue;
+                    }
+                    uint8_t *block = static_cast<uint8_t *>(d->bases[t.region]) + poff;
+                    uint8_t *tile_p = a.chunk_base + t.chunk_off;
+                    auto mark = [&](int64_t word) {  // chunk-order word of this tile
+                        const uint64_t bit = (uint64_t)(tile * twords + word);
+                        if (wwritten[bit / 64] >> (bit % 64) & 1u) ++*violations;
+                        wwritten[bit / 64] |= 1ull << (bit % 64);
+                    };
+                    auto words_of = [&](uint32_t v, uint32_t sw[4]) {
+                        kvx::hm_page_slice_words(a, v, n_tok, sw);
+                        for (uint32_t c = 0; c < 4; ++c) {
+                            const uint32_t w = 4 * v + c, h = w / (bs * rd), j = w % (bs * rd) / rd, q = w % rd;
+                            const uint32_t want = j < n_tok ? (j * H + h) * rd + q : ~0u;
+                            if (sw[c] != want) ++*violations;
+                            if (sw[c] != ~0u && (int64_t)sw[c] * 4 >= KVX_HM_PAGE_SLICE) ++*violations;
+                        }
+                    };
+                    ++gen;
+                    if (direction == KV_GATHER) {
+                        for (uint32_t v = 0; v < page_vec; ++v) {  // pool vectors -> slice
+                            uint32_t sw[4];
+                            words_of(v, sw);
+                            for (int c = 0; c < 4; ++c) {
+                                if (sw[c] == ~0u || (int64_t)sw[c] * 4 >= KVX_HM_PAGE_SLICE) continue;
+                                if (tag[sw[c]] == gen) ++*violations;  // two words into one place
+                                if (copy) std::memcpy(&slice[sw[c]], block + (4ll * v + c) * 4, 4);
+                                tag[sw[c]] = gen;
+                            }
+                        }
+                        for (uint32_t v = 0; v < tile_vec; ++v) {  // slice -> chunk vectors
+                            if (t.chunk_off + (v + 1) * 16ll > staging_bytes || (v + 1) * 16ll > KVX_HM_PAGE_SLICE) {
+                                ++*violations;
+                                continue;
+                            }
+                            bool fresh = true;
+                            for (int k = 0; k < 4; ++k) fresh = fresh && tag[4 * v + k] == gen;
+                            if (!fresh) { ++*violations; continue; }
+                            if (copy) std::memcpy(tile_p + v * 16ll, &slice[4 * v], 16);
+                            for (int k = 0; k < 4; ++k) mark(4ll * v + k);
+                        }
+                    } else {
+                        for (uint32_t v = 0; v < tile_vec; ++v) {  // chunk vectors -> slice
+                            if (t.chunk_off + (v + 1) * 16ll > staging_bytes || (v + 1) * 16ll > KVX_HM_PAGE_SLICE) {
+                                ++*violations;
+                                continue;
+                            }
+                            if (copy) std::memcpy(&slice[4 * v], tile_p + v * 16ll, 16);
+                            for (int k = 0; k < 4; ++k) tag[4 * v + k] = gen;
+                        }
+                        for (uint32_t v = 0; v < page_vec; ++v) {  // slice -> pool, whole or by word
+                            uint32_t sw[4];
+                            words_of(v, sw);
+                            for (int c = 0; c < 4; ++c) {
+                                if (sw[c] == ~0u) {
+                                    if (n_tok == bs) ++*violations;  // a full page stores every word
+                                    continue;
+                                }
+                                if ((int64_t)sw[c] * 4 >= KVX_HM_PAGE_SLICE || tag[sw[c]] != gen) {
+                                    ++*violations;
+                                    continue;
+                                }
+                                if (copy) std::memcpy(block + (4ll * v + c) * 4, &slice[sw[c]], 4);
+                                mark(sw[c]);
+                            }
+                        }
+                    }
+                    continue;
+                }
                 if (a.page_layout == KV_PAGE_HEAD_MAJOR && a.hm_lds && a.hm_hg[direction]) {
                     // the kernel's head-group slabs, lane by lane and phase by phase; the
                     // slice holds a slab in pool order, the chunk side is walked in chunk order
@@ -545,6 +623,11 @@ extern "C" int emu_gather_seg_unroll(int64_t tile_bytes, int64_t seg_bytes)
 {
     return kvx::gather_seg_unroll(tile_bytes, seg_bytes);
 }
+extern "C" int32_t emu_hm_page_ok(int64_t row, int64_t tok, int64_t tile)
+{
+    return kvx::hm_page_ok(KV_PAGE_HEAD_MAJOR, row, tok, tile) ? 1 : 0;
+}
+
 extern "C" uint32_t emu_hm_lds_tokens(int64_t row, int64_t tok, uint32_t block_size)
 {
     return kvx::hm_lds_tokens(row, tok, block_size);

@@ -330,7 +330,7 @@ def test_head_major_pool_cases(seed):
                  dma=seed % 4 == 0)
 
 
-@pytest.mark.parametrize("seed", range(26))
+@pytest.mark.parametrize("seed", range(32))
 def test_head_major_lds_cases(seed):
     """Head-major pages whose head rows are not whole 16-byte vectors (4 to 100 bytes),
     moved through LDS slabs: every slab shape of the list twice, odd seeds staged in pinned

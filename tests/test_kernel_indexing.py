@@ -41,6 +41,8 @@ def _build_emu(tmp_path_factory, defines=()):
     lib.emu_arena.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
     lib.emu_gather_seg_unroll.restype = ctypes.c_int
     lib.emu_gather_seg_unroll.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    lib.emu_hm_page_ok.restype = ctypes.c_int32
+    lib.emu_hm_page_ok.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.emu_hm_lds_tokens.restype = ctypes.c_uint32
     lib.emu_hm_lds_tokens.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32]
     lib.emu_hm_lds_head_slab.restype = None
@@ -293,7 +295,7 @@ def test_emulated_head_major_blocks_match_oracle(emu, seed):
 LDS_SHAPES = cases.HM_LDS_SHAPES
 
 
-@pytest.mark.parametrize("seed", range(26))
+@pytest.mark.parametrize("seed", range(32))
 def test_emulated_head_major_lds_matches_oracle(emu, seed):
     """Head-major pages whose rows are not whole 16-byte vectors take the LDS slab walk
     (the kernel's lanes, magic-multiply divisions and slice indices replayed on the CPU):
@@ -303,7 +305,7 @@ def test_emulated_head_major_lds_matches_oracle(emu, seed):
     _copy_case(emu, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
 
 
-@pytest.mark.parametrize("seed", range(13))
+@pytest.mark.parametrize("seed", range(16))
 def test_emulated_head_major_lds_split_match_oracle(emu_split, seed):
     """The same with tiles split between waves (parts are ranges of slabs)."""
     rng = np.random.default_rng(36_000 + seed)
@@ -329,6 +331,19 @@ def test_lds_slab_tokens(emu, row, heads, bs, tj):
     got = emu.emu_hm_lds_tokens(row, row * heads, bs)
     assert got == tj
     assert got * row * heads <= 8192 and 1 <= got <= bs
+
+
+@pytest.mark.parametrize("row,heads,bs,whole", [
+    (12, 100, 16, True),    # 19200-byte pages: more than a token slab's 8 KiB, within 20 KiB
+    (12, 20, 64, True),     # 15360
+    (8, 32, 48, True),      # 12288
+    (8, 8, 16, False),      # 1 KiB pages fit a token slab whole already
+    (24, 16, 64, False),    # 24 KiB pages: token slabs
+    (12, 100, 32, False),   # 37.5 KiB pages: token and head-group slabs
+    (16, 100, 16, False),   # rows of whole 16-byte vectors take no LDS at all
+])
+def test_whole_page_rule(emu, row, heads, bs, whole):
+    assert bool(emu.emu_hm_page_ok(row, row * heads, row * heads * bs)) == whole
 
 
 @pytest.mark.parametrize("row,heads,bs,gather,scatter", [
