@@ -111,7 +111,7 @@ class Setup:
 
 
 HBM_WORKLOADS = ["llama8b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
-                 "hnd_rows24"]
+                 "hnd_rows24", "hnd_h100_r12"]
 
 
 @pytest.mark.timeout(900)
