@@ -275,7 +275,7 @@ def hbm_leg(args, dev):
     per_dir = {}
     for name, which in (("gather", ("g",)), ("scatter", ("s",))):
         K.kv_pool_timing_start(P.h)
-        step(max(3, args.steps // 2), which)
+        step(max(10, args.steps), which)
         each = K.kv_pool_timing_read_each(P.h)
         per_dir[name] = direction_roofline(payload, each)
 
@@ -294,7 +294,7 @@ def hbm_leg(args, dev):
         for name, fn in (("gather", K.kv_gather_chunks), ("scatter", K.kv_scatter_chunks)):
             fn(P.h, spans_a, spec, stream)
             K.kv_pool_timing_start(P.h)
-            for _ in range(max(3, args.steps // 2)):
+            for _ in range(max(10, args.steps)):
                 fn(P.h, spans_a, spec, stream)
             each = K.kv_pool_timing_read_each(P.h)
             alloc_order[name] = dict(kernel_ms_median=round(float(np.median(each)), 4),
@@ -1012,7 +1012,7 @@ def main():
     before = [args.workload] + (["llama70b"] if args.host_path else [])
     hm = ["llama8b_hnd", "fp8_hnd_d64", "hnd_rows24", "hnd_h100_r12"]
     names = ["mixed", "mla_fp8", "int8_kv", "llama8b_tp8"] + [x for n in hm for x in (n, n + ":token_major")]
-    others = other_workloads(dev, names, 5, before) if args.others else None
+    others = other_workloads(dev, names, 10, before) if args.others else None
     pipeline = pipeline_leg(args, dev) if args.pipeline else None
     placement = placement_leg(args, dev) if args.placement else None
 
