@@ -510,6 +510,28 @@ int check_buffers(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_ch
     return KV_OK;
 }
 
+// The launch of a prepared call (regions, spans and err set): the split and segment
+// choices, the grid (capped by max_workgroups, or small for host staging), and the
+// timing events around the kernel when timing is on.
+int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_spec *spec,
+                    const kvx::AllocRange &staging, hipStream_t stream)
+{
+    a.split_shift = kvx::launch_split_shift(a, direction);
+    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
+    uint32_t grid = kvx::default_grid(kvx::work_items(a));
+    if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
+    else if (staging_in_host_memory(p, spec->base, staging)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
+    const bool timed = p->timing && p->n_timed < kMaxTimed;
+    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
+    if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))
+        return KV_ERR_HIP;
+    if (timed) {
+        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;
+        ++p->n_timed;
+    }
+    return KV_OK;
+}
+
 int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
              hipStream_t stream, int direction)
 {
@@ -559,21 +581,7 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     a.regions = p->d_regions;
     a.spans = inline_records ? nullptr : dd;
     a.err = p->d_err;
-
-    a.split_shift = kvx::launch_split_shift(a, direction);
-    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
-    uint32_t grid = kvx::default_grid(kvx::work_items(a));
-    if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
-    else if (staging_in_host_memory(p, spec->base, staging)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
-
-    const bool timed = p->timing && p->n_timed < kMaxTimed;
-    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return fail();
-    if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))
-        return fail();
-    if (timed) {
-        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return fail();
-        ++p->n_timed;
-    }
+    if (launch_prepared(p, a, direction, spec, staging, stream)) return fail();
     return arena_commit(p, off, rec_bytes, stream);
 }
 
@@ -626,21 +634,7 @@ int transfer_noalloc(kv_pool *p, int direction, const kv_span *spans, int32_t n_
     a.regions = reinterpret_cast<uint8_t *const *>(scr + KVX_SCR_REGIONS_OFF);
     a.spans = inline_records ? nullptr : reinterpret_cast<const kvx::SpanDev *>(scr + KVX_SCR_RECORDS_OFF);
     a.err = err_word ? err_word : reinterpret_cast<int32_t *>(scr);
-    a.split_shift = kvx::launch_split_shift(a, direction);
-    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
-    uint32_t grid = kvx::default_grid(kvx::work_items(a));
-    if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
-    else if (staging_in_host_memory(p, spec->base, staging)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
-
-    const bool timed = p->timing && p->n_timed < kMaxTimed;
-    if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
-    if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))
-        return KV_ERR_HIP;
-    if (timed) {
-        if (!HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed + 1], stream))) return KV_ERR_HIP;
-        ++p->n_timed;
-    }
-    return KV_OK;
+    return launch_prepared(p, a, direction, spec, staging, stream);
 }
 
 // One hipMemcpyAsync per tile, addresses from the same tile resolution the kernel

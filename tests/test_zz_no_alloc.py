@@ -121,3 +121,33 @@ def test_noalloc_reports_a_bad_block_id_in_the_callers_word():
         assert np.array_equal(s1, s0) and np.array_equal(r1, r0)
     finally:
         c.close()
+
+
+def test_noalloc_calls_queued_behind_busy_work_keep_their_own_records():
+    """Two calls queued behind several milliseconds of other work on the stream, with no
+    synchronisation: each call's region table and span records come from the pool's one
+    host image, which the second call rewrites as soon as the first returns, so the
+    first call's copy must have taken its bytes by then.  Both results must equal the
+    allocating entry point's."""
+    dev = _dev()
+    stream = torch.cuda.current_stream()
+    a = Call(*_case(84_000, 40, True), seed=11, dev=dev)
+    b = Call(*_case(84_001, 40, True), seed=12, dev=dev)
+    busy = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    try:
+        torch.cuda.synchronize()
+        print("[noalloc] two 40-record scatters queued behind busy work", flush=True)
+        for c in (a, b):
+            K.kv_scatter_chunks(c.sides[0]["h"], c.sp, c.sides[0]["spec"], stream)
+        for _ in range(20):
+            busy.fill_(7)                       # ~20 passes over 1 GiB ahead of the calls
+        for c in (a, b):
+            K.kv_transfer_chunks_noalloc(c.sides[1]["h"], K.KV_SCATTER, c.sp, c.sides[1]["spec"], None, stream)
+        torch.cuda.synchronize()
+        for c in (a, b):
+            (r0, s0), (r1, s1) = c.results()
+            assert np.array_equal(r1, r0) and np.array_equal(s1, s0), "a queued call used another call's records"
+    finally:
+        a.close()
+        b.close()
+        del busy
