@@ -31,7 +31,12 @@ namespace kvx {
 #define KVX_WAVES_PER_BLOCK 4  // 256-thread workgroups of four 64-lane wavefronts
 #endif
 #ifndef KVX_GRID_CAP
-#define KVX_GRID_CAP 32768     // workgroups per launch at most; more tiles loop
+// Workgroups per launch at most (more work items loop).  At 2^20 every workload here
+// gets one work item per wave, so no wave resolves a second tile (span search, record
+// and block-id loads) in the middle of its life: measured on MI355X, the 64-request
+// mixed gather (1.65 M items, 12.6 per wave at a cap of 32768) +5 to +7 %, the others
+// within noise.
+#define KVX_GRID_CAP 1048576
 #endif
 #ifndef KVX_HOST_GRID_CAP
 #define KVX_HOST_GRID_CAP 16   // default workgroups when the staging is host memory

@@ -91,7 +91,15 @@ __device__ __forceinline__ const KVX_CONST SpanDev *span_records(const Launch &a
     return as_const(a.spans);
 }
 
-__device__ __forceinline__ SpanDev load_span(const KVX_CONST SpanDev *p)
+// A span record, read as one 16-dword scalar load: every field arrives with one wait,
+// instead of the few separate loads (and waits) the compiler makes of field accesses.
+// Measured on MI355X for the tile walk: the int8 page-first gather 73.6 -> 77.3 % of
+// HBM peak (the field-by-field form put one more scalar-memory round trip before each
+// tile's block-id load), other workloads within 0.3 %.
+// A span record read field by field (separate scalar loads as the compiler schedules
+// them).  The segment walk, which resolves one or two tile pieces per segment, keeps
+// this form: measured on MI355X, the single load below costs its MLA gather 1-1.5 %.
+__device__ __forceinline__ SpanDev load_span_fields(const KVX_CONST SpanDev *p)
 {
     SpanDev r;
     r.table = p->table;
@@ -104,6 +112,24 @@ __device__ __forceinline__ SpanDev load_span(const KVX_CONST SpanDev *p)
     r.n_tc = p->n_tc;
     r.per_lc = p->per_lc;
     r.per_tc = p->per_tc;
+    return r;
+}
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ SpanDev load_span(const KVX_CONST SpanDev *p)
+{
+    const u32x16 w = *(const KVX_CONST u32x16 *)p;
+    auto u64 = [&](int i) { return (uint64_t)w[i] | ((uint64_t)w[i + 1] << 32); };
+    SpanDev r;
+    r.table = (const int32_t *)u64(offsetof(SpanDev, table) / 4);
+    r.tile_begin = (int64_t)u64(offsetof(SpanDev, tile_begin) / 4);
+    r.t_end = (int64_t)u64(offsetof(SpanDev, t_end) / 4);
+    r.slot0 = (int64_t)u64(offsetof(SpanDev, slot0) / 4);
+    r.first_page = w[offsetof(SpanDev, first_page) / 4];
+    r.n_pages = w[offsetof(SpanDev, n_pages) / 4];
+    r.ppc = w[offsetof(SpanDev, ppc) / 4];
+    r.n_tc = w[offsetof(SpanDev, n_tc) / 4];
+    r.per_lc = w[offsetof(SpanDev, per_lc) / 4];
+    r.per_tc = w[offsetof(SpanDev, per_tc) / 4];
     return r;
 }
 
@@ -724,7 +750,7 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
             const int64_t x1 = x0 + a.seg_bytes < total ? x0 + a.seg_bytes : total;
             for (int64_t tile = x0 / T; tile * T < x1; ++tile) {
                 s = find_span(spans, s, a.n_spans, tile);
-                const SpanDev sp = load_span(spans + s);
+                const SpanDev sp = load_span_fields(spans + s);
                 const TileRef t = resolve_tile<LAYOUT>(a, sp, tile);
                 int64_t lo, hi;
                 segment_piece(tile, T, t.nbytes, x0, x1, &lo, &hi);
