@@ -109,6 +109,7 @@ extern "C" {
 #define KV_ERR_DEVICE (-7) /* kv_pool_get_error: the device reported a bad block id */
 #define KV_ERR_DUP (-8)    /* KV_FLAG_VALIDATE: a scatter writes one pool page twice */
 #define KV_ERR_SCRATCH (-9) /* kv_transfer_chunks_noalloc: more regions than its static scratch holds */
+#define KV_ERR_CAPTURE (-10) /* the stream is capturing a graph and this call cannot be captured */
 
 /* ---- chunk layouts, in-page layouts, directions, flags ----------------- */
 #define KV_LAYER_FIRST 0
@@ -260,7 +261,11 @@ KV_API int kv_validate_targets(const kv_pool_desc *desc, const kv_span *spans, i
  * `stream`, preceded by one small stream-ordered descriptor upload.  spans is a
  * host array of n_spans (1 .. KV_MAX_SPANS) entries; each block_table is a
  * device pointer.  n_spans == 0, or spans that are all empty, is a no-op.  Loads
- * and stores are nontemporal.  Returns after enqueueing. */
+ * and stores are nontemporal.  Returns after enqueueing.  Not for graph capture:
+ * while `stream` is capturing, the call is refused with KV_ERR_CAPTURE (its
+ * span-record arena is recycled under events the host waits on, and its first call
+ * on a pool allocates); capture kv_transfer_chunks_noalloc instead.  The same holds
+ * for kv_scatter_chunks. */
 KV_API int kv_gather_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                      const kv_chunk_spec *spec, hipStream_t stream);
 
@@ -287,7 +292,15 @@ KV_API int kv_scatter_chunks(kv_pool *pool, const kv_span *spans, int32_t n_span
  * skipped, as in the other entry points, and its KV_DEVERR_* bit OR-ed into
  * *err_word, a caller-owned device int32 (4-byte aligned) that the caller clears
  * and reads; err_word may be NULL to ignore such ids.  kv_pool_get_error does not
- * see these calls.  Returns after enqueueing. */
+ * see these calls.  Returns after enqueueing.
+ * Under HIP graph capture: a call with at most 16 non-empty spans carries its span
+ * records in the kernel arguments, and is captured as the copy of the pool's region
+ * table (which the graph reads from the pool's host image each time it runs, so the
+ * pool must outlive the graph) followed by the kernel; every replay repeats the
+ * call.  A call with more non-empty spans is refused with KV_ERR_CAPTURE while
+ * `stream` is capturing: the graph would read its records from the host image when
+ * it runs, after later calls have rewritten them.  Replays share the device's static
+ * array like any other call: a replay must not overlap another call on the device. */
 KV_API int kv_transfer_chunks_noalloc(kv_pool *pool, int32_t direction, const kv_span *spans,
                                       int32_t n_spans, const kv_chunk_spec *spec, int32_t *err_word,
                                       hipStream_t stream);

@@ -20,6 +20,7 @@ KV_ERR_HIP = -6
 KV_ERR_DEVICE = -7
 KV_ERR_DUP = -8
 KV_ERR_SCRATCH = -9
+KV_ERR_CAPTURE = -10
 KV_LAYER_FIRST = 0
 KV_PAGE_FIRST = 1
 KV_PAGE_TOKEN_MAJOR = 0

@@ -532,6 +532,15 @@ int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_sp
     return KV_OK;
 }
 
+// KV_ERR_CAPTURE if `stream` is capturing a graph (or its capture was invalidated),
+// KV_OK if not, KV_ERR_HIP if the runtime cannot tell.
+int refuse_capture(hipStream_t stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (!hip_ok(hipStreamIsCapturing(stream, &st), "hipStreamIsCapturing")) return KV_ERR_HIP;
+    return st == hipStreamCaptureStatusNone ? KV_OK : KV_ERR_CAPTURE;
+}
+
 int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_spec *spec,
              hipStream_t stream, int direction)
 {
@@ -541,6 +550,10 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
     if (rc) return rc;
     if (info.tiles == 0) return KV_OK;
+    // The arena is recycled under events the host waits on, and the first call on a
+    // pool allocates: neither may be captured into a graph.
+    rc = refuse_capture(stream);
+    if (rc) return rc;
     kvx::AllocRange staging;
     rc = check_buffers(p, spans, n_spans, spec, true, &staging);
     if (rc) return rc;
@@ -601,6 +614,14 @@ int transfer_noalloc(kv_pool *p, int direction, const kv_span *spans, int32_t n_
     if (n_regions > KVX_SCR_MAX_REGIONS) return KV_ERR_SCRATCH;
     if (err_word && (reinterpret_cast<uintptr_t>(err_word) & 3u)) return KV_ERR_ALIGN;
     if (info.tiles == 0) return KV_OK;
+    // Records beyond those the kernel arguments carry are copied from the pool's host
+    // image, which a captured copy would read only when the graph runs.
+    int32_t n_nonempty = 0;
+    for (int32_t i = 0; i < n_spans; ++i) n_nonempty += spans[i].t_end > spans[i].t_begin;
+    if (n_nonempty > KVX_INLINE_SPANS) {
+        rc = refuse_capture(stream);
+        if (rc) return rc;
+    }
     kvx::AllocRange staging;
     rc = check_buffers(p, spans, n_spans, spec, true, &staging);
     if (rc) return rc;
@@ -1031,6 +1052,7 @@ const char *kv_strerror(int code)
     case KV_ERR_DEVICE: return "the device reported a block id out of range";
     case KV_ERR_DUP: return "scatter writes one pool page twice";
     case KV_ERR_SCRATCH: return "the call needs more than the static device scratch holds";
+    case KV_ERR_CAPTURE: return "the stream is capturing a graph and this call cannot be captured";
     default: return "unknown error";
     }
 }

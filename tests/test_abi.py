@@ -58,7 +58,8 @@ def test_header_constants_match_binding():
 def test_version_and_strerror():
     assert K.kv_version() == K.KV_VERSION
     codes = [K.KV_OK, K.KV_ERR_ARG, K.KV_ERR_ALIGN, K.KV_ERR_RANGE, K.KV_ERR_OOM, K.KV_ERR_RING,
-             K.KV_ERR_HIP, K.KV_ERR_DEVICE, K.KV_ERR_DUP, K.KV_ERR_SCRATCH]
+             K.KV_ERR_HIP, K.KV_ERR_DEVICE, K.KV_ERR_DUP, K.KV_ERR_SCRATCH,
+             K.KV_ERR_CAPTURE]
     msgs = [K.kv_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert K.kv_strerror(12345) == "unknown error"

@@ -7,6 +7,11 @@ noalloc calls are queued back to back on one stream with no synchronisation: the
 first with more span records than ride in the kernel arguments (so they go through
 the static scratch), the second a smaller call, which reuses the scratch the first
 one left behind.  A block id out of range must set the caller's error word.
+
+Under graph capture: a noalloc call whose span records ride in the kernel arguments
+is captured and replayed (each replay after another pool's call has rewritten the
+device scratch, each checked against the allocating entry point); a noalloc call with
+more records, and the allocating entry points, are refused while the stream captures.
 """
 from __future__ import annotations
 
@@ -151,3 +156,90 @@ def test_noalloc_calls_queued_behind_busy_work_keep_their_own_records():
         a.close()
         b.close()
         del busy
+
+
+@pytest.mark.parametrize("mode", ["global", "relaxed"])
+@pytest.mark.parametrize("direction", [K.KV_GATHER, K.KV_SCATTER])
+def test_noalloc_call_replays_from_a_captured_graph(direction, mode):
+    dev = _dev()
+    c = Call(*_case(85_000 + direction, 3, False), seed=21 + direction, dev=dev)
+    other = Call(*_case(85_100 + direction, 2, False), seed=31 + direction, dev=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    name = "gather" if direction == K.KV_GATHER else "scatter"
+    ref, side = c.sides[0], c.sides[1]
+    dst = side["stg"] if direction == K.KV_GATHER else side["buf"]
+    start = dst.clone()
+    g = None
+    try:
+        stream = torch.cuda.current_stream()
+        fn = K.kv_gather_chunks if direction == K.KV_GATHER else K.kv_scatter_chunks
+        fn(ref["h"], c.sp, ref["spec"], stream)
+        torch.cuda.synchronize()
+        want_buf, want_stg = ref["buf"].cpu().numpy(), ref["stg"].cpu().numpy()
+        # one eager call first, so the pool's per-address caches are warm before capture
+        K.kv_transfer_chunks_noalloc(side["h"], direction, c.sp, side["spec"], err, stream)
+        dst.copy_(start)
+        torch.cuda.synchronize()
+        print("[noalloc] %s captured in %s mode, replayed 3 times" % (name, mode), flush=True)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cap, capture_error_mode=mode):
+            K.kv_transfer_chunks_noalloc(side["h"], direction, c.sp, side["spec"], err, cap)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            # eager work in between: another pool's call leaves its region table in the scratch
+            K.kv_transfer_chunks_noalloc(other.sides[1]["h"], direction, other.sp, other.sides[1]["spec"], None,
+                                         stream)
+            dst.copy_(start)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert int(err.item()) == 0
+            assert np.array_equal(side["buf"].cpu().numpy(), want_buf), "replay %d: pool differs" % rep
+            assert np.array_equal(side["stg"].cpu().numpy(), want_stg), "replay %d: staging differs" % rep
+    finally:
+        del g
+        c.close()
+        other.close()
+
+
+def test_capture_refuses_calls_that_cannot_replay():
+    """While a stream captures: the allocating entry points, and a noalloc call with more
+    span records than the kernel arguments carry, return KV_ERR_CAPTURE and enqueue
+    nothing; the capture itself stays valid, and the same calls made eagerly afterwards
+    match the oracle."""
+    dev = _dev()
+    c = Call(*_case(87_000, 40, True), seed=51, dev=dev)
+    x = torch.zeros(16, device=dev)
+    try:
+        torch.cuda.synchronize()
+        print("[noalloc] refused calls under capture", flush=True)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        codes = []
+        with torch.cuda.graph(g, stream=cap):
+            x.add_(1)
+            for call in (lambda: K.kv_gather_chunks(c.sides[0]["h"], c.sp, c.sides[0]["spec"], cap),
+                         lambda: K.kv_scatter_chunks(c.sides[0]["h"], c.sp, c.sides[0]["spec"], cap),
+                         lambda: K.kv_transfer_chunks_noalloc(c.sides[1]["h"], K.KV_GATHER, c.sp,
+                                                              c.sides[1]["spec"], None, cap)):
+                with pytest.raises(K.KvError) as e:
+                    call()
+                codes.append(e.value.code)
+        torch.cuda.synchronize()
+        assert codes == [K.KV_ERR_CAPTURE] * 3
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(x[0]) == 1.0
+        (r0, s0), (r1, s1) = c.results()
+        assert np.array_equal(r0, c.regions) and np.array_equal(s0, c.staging), "a refused call wrote"
+        assert np.array_equal(r1, c.regions) and np.array_equal(s1, c.staging), "a refused call wrote"
+        stream = torch.cuda.current_stream()
+        K.kv_gather_chunks(c.sides[0]["h"], c.sp, c.sides[0]["spec"], stream)
+        K.kv_transfer_chunks_noalloc(c.sides[1]["h"], K.KV_GATHER, c.sp, c.sides[1]["spec"], None, stream)
+        torch.cuda.synchronize()
+        er, es = c.expected(K.KV_GATHER)
+        for r, st in c.results():
+            assert np.array_equal(st, es) and np.array_equal(r, er)
+    finally:
+        c.close()
