@@ -358,6 +358,30 @@ EXTREMES = {
 }
 
 
+def test_blocks_past_4_gib_in_one_region():
+    """One 4.3 GiB region with 1 MiB between blocks: the spans' pages sit in blocks past
+    the 4 GiB offset and near the start, so every pool address needs the 64-bit product
+    of block id and stride (the chunk side is the same for either chunk layout, so
+    layer-first chunks only).  Both directions, whole region and staging compared."""
+    tok = 2 * 64 * 2
+    pool = dict(num_layers=1, num_kv=1, num_heads=2, head_dim=64, elem_bytes=2, block_size=16,
+                num_blocks=4400, block_stride=1 << 20, page_layout=0)
+    rng = np.random.default_rng(97_000)
+    far = rng.permutation(np.arange(4096, 4400))[:150]
+    near = rng.permutation(np.arange(0, 64))[:20]
+    ids = rng.permutation(np.concatenate([far, near])).astype(np.int32)
+    spans = [(ids[:100], 0, 100 * 16 - 5, 0), (ids[100:], 0, 70 * 16, 7)]
+    chunks = dict(layout=0, chunk_layers=1, chunk_tokens=256, layer_begin=0, layer_end=1,
+                  slot_bytes=256 * tok, n_slots=12)
+    regions = np.full((1, pool["num_blocks"] * pool["block_stride"]), 0xA5, dtype=np.uint8)
+    for b in ids:
+        o = int(b) * pool["block_stride"]
+        regions[0, o:o + 16 * tok] = rng.integers(0, 256, 16 * tok, dtype=np.uint8)
+    staging = cases.staging_for(chunks, rng=rng)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "past-4gib")
+
+
 @pytest.mark.parametrize("name", sorted(EXTREMES))
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("page_layout", [0, 1])
