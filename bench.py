@@ -306,6 +306,8 @@ def hbm_leg(args, dev):
         log("allocator-ordered blocks: gather %.1f%%, scatter %.1f%% of HBM peak" % (
             100 * alloc_order["gather"]["hbm_frac"], 100 * alloc_order["scatter"]["hbm_frac"]))
 
+    small = small_calls(P, tabs[0], w, pool, spec, chunks, S, stream) if args.small_calls else None
+
     # the conventional engine on the same call: one hipMemcpyAsync per tile
     dma = {}
     if args.dma_baseline:
@@ -352,7 +354,7 @@ def hbm_leg(args, dev):
         payload=payload, ms_per_step=ms_per_step, kernel_ms_avg=kern_ms / launches, launches=launches,
         value=2 * payload / (ms_per_step * 1e-3) / 1e9,
         achieved=2 * payload / avg_kernel_s / 1e9, per_dir=per_dir, parity=parity,
-        d2d_copy_gbs=d2d_gbs, dma=dma, alloc_order=alloc_order, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
+        d2d_copy_gbs=d2d_gbs, dma=dma, alloc_order=alloc_order, small_calls=small, tiles=info.tiles, chunks=info.chunks, w=w, pool=pool, chunks_spec=chunks,
         staging_bytes=plan["slot_bytes"] * plan["n_chunks"],
         name=args.workload)
     res["cpu"] = cpu
@@ -360,6 +362,71 @@ def hbm_leg(args, dev):
     del P, S, tabs
     torch.cuda.empty_cache()
     return res
+
+
+def small_calls(P, tab, w, pool, spec, chunks, S, stream, sizes=(1, 4, 16, 64, 256, 1024), calls=200):
+    """Per-call cost of small transfers: the first n pages of the workload's first
+    request, every layer, from 1 page up.  For each entry point: host microseconds to
+    enqueue one call and the rate when calls run back to back (a batch of `calls` calls
+    with no synchronisation between them and no timing events, wall time synchronised at
+    the end), then the kernel's median duration (a second batch with events around each
+    launch).  The per-tile copy-engine path is
+    timed alongside up to 64 pages."""
+    import numpy as np
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    from paged_layout_transfer_amd import workloads as W
+    L, KV, bs = pool["num_layers"], pool["num_kv"], pool["block_size"]
+    tok = W.token_bytes(w)
+    err = torch.zeros(1, dtype=torch.int32, device=S.device)
+    tab_h = np.ascontiguousarray(w["block_tables"][0], dtype=np.int32)
+    rows = []
+    for n in sizes:
+        t1 = min(n * bs, w["requests"][0][1])
+        sp = K.make_spans([(tab, tab.numel(), 0, t1, 0)])
+        moved = L * KV * t1 * tok
+        row = dict(pages=n, bytes=moved, tiles=L * KV * -(-t1 // bs))
+        entries = (("gather", lambda: K.kv_gather_chunks(P.h, sp, spec, stream)),
+                   ("scatter", lambda: K.kv_scatter_chunks(P.h, sp, spec, stream)),
+                   ("gather_noalloc", lambda: K.kv_transfer_chunks_noalloc(P.h, K.KV_GATHER, sp, spec, err, stream)),
+                   ("scatter_noalloc", lambda: K.kv_transfer_chunks_noalloc(P.h, K.KV_SCATTER, sp, spec, err,
+                                                                            stream)))
+        for name, call in entries:
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            # untimed batch: host cost and back-to-back rate with no events around the launches
+            t0 = time.perf_counter()
+            for _ in range(calls):
+                call()
+            host = time.perf_counter() - t0
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            # timed batch: each kernel's duration from events around its launch
+            K.kv_pool_timing_start(P.h)
+            for _ in range(calls):
+                call()
+            each = K.kv_pool_timing_read_each(P.h)
+            row[name] = dict(host_us=round(host / calls * 1e6, 2),
+                             kernel_us_median=round(float(np.median(each)) * 1e3, 2),
+                             back_to_back_us=round(wall / calls * 1e6, 2),
+                             gbs=round(moved * calls / wall / 1e9, 2))
+        if n <= 64:
+            sp_h = K.make_spans([(tab_h.ctypes.data, tab_h.size, 0, t1, 0)])
+            for name, fn in (("gather_dma", K.kv_gather_chunks_dma), ("scatter_dma", K.kv_scatter_chunks_dma)):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(5):
+                    fn(P.h, sp_h, spec, stream)
+                torch.cuda.synchronize()
+                wall = (time.perf_counter() - t0) / 5
+                row[name] = dict(back_to_back_us=round(wall * 1e6, 2), gbs=round(moved / wall / 1e9, 2))
+        assert K.kv_pool_get_error(P.h, stream) == 0 and int(err.item()) == 0
+        rows.append(row)
+        log("small calls, %d pages: gather %.1f us host / %.1f us kernel, back to back %.1f us per call" % (
+            n, row["gather"]["host_us"], row["gather"]["kernel_us_median"], row["gather"]["back_to_back_us"]))
+    return dict(workload="first n pages of the request, every layer and K/V, same chunk spec and staging as "
+                         "the step; %d calls per entry point and size" % calls, rows=rows)
 
 
 def cpu_baseline(res):
@@ -988,6 +1055,8 @@ def main():
                     help="skip the compute-beside-transfer measurement")
     ap.add_argument("--no-placement", dest="placement", action="store_false",
                     help="skip the scatter measured on pools of different physical placement")
+    ap.add_argument("--no-small-calls", dest="small_calls", action="store_false",
+                    help="skip the per-call cost of small transfers")
     ap.add_argument("--no-dma-baseline", dest="dma_baseline", action="store_false",
                     help="skip the per-tile hipMemcpyAsync comparison")
     args = ap.parse_args()
@@ -1066,6 +1135,7 @@ def main():
         "breakdown": per_dir,
         "d2d_memcpy_gbs": round(res["d2d_copy_gbs"], 1),
         "allocator_ordered_blocks": res["alloc_order"],
+        "small_calls": res["small_calls"],
         "per_tile_dma": res["dma"],
         "parity": res["parity"],
         "host_path": host,
