@@ -963,7 +963,8 @@ def placement_leg(args, dev):
     allocations (0 to 35 GiB held): the same kernel, table and staging buffer, so any
     spread is the pool's physical placement.  Ends with three scatters on the slowest
     and three on the fastest pool kept, in that order (the last six scatter launches of
-    the process), for per-channel counter passes."""
+    the process), for per-channel counter passes.  Before the pools: the same call with
+    the regions at chosen offsets of one large allocation (window_split)."""
     import numpy as np
     import torch
     from paged_layout_transfer_amd import kvxfer as K
@@ -980,6 +981,7 @@ def placement_leg(args, dev):
                              plan["n_chunks"])
     kept, holds, rates = [], [], []
     try:
+        split = window_split(pool, spans, spec, stream, payload, dev)
         for gb in (0, 5, 5, 5, 5, 5, 10):
             if gb:
                 holds.append(torch.empty(gb << 30, dtype=torch.uint8, device=dev))
@@ -1009,8 +1011,55 @@ def placement_leg(args, dev):
     fr = [r["scatter_hbm_frac"] for r in rates]
     out = dict(workload="llama8b scatter (shuffled table), one fresh pool after each growing hold; staging "
                         "buffer and table unchanged", pools=rates, min=min(fr), max=max(fr))
+    out["window_split"] = split
+    log("window split: %s" % split["layouts"])
     log("placement: scatter %.1f%% .. %.1f%% of HBM peak over %d pools" % (100 * min(fr), 100 * max(fr), len(fr)))
     return out
+
+
+def window_split(pool, spans, spec, stream, payload, dev):
+    """The same llama8b call with the pool's 64 regions laid out three ways inside one
+    96 GiB allocation: all packed at its start, half at its start and half 64 GiB
+    further, and all packed 64 GiB further.  Interleaved rounds; the median of each
+    layout's launches."""
+    import numpy as np
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    G = 1 << 30
+    n = pool["num_layers"] * pool["num_kv"]
+    row = pool["num_blocks"] * pool["block_stride"]
+    big = torch.empty(96 * G, dtype=torch.uint8, device=dev)
+    b = big.data_ptr()
+    layouts = {"packed_at_0": [b + r * row for r in range(n)],
+               "half_at_0_half_at_64GiB": [b + (0 if r < n // 2 else 64 * G) + r * row for r in range(n)],
+               "packed_at_64GiB": [b + 64 * G + r * row for r in range(n)]}
+    handles = {}
+    res = {}
+    try:
+        for name, bases in layouts.items():
+            handles[name] = K.kv_pool_create(K.make_pool_desc(
+                pool["num_layers"], pool["num_kv"], pool["num_heads"], pool["head_dim"], pool["elem_bytes"],
+                pool["block_size"], pool["num_blocks"], pool["block_stride"], bases))
+        for rnd in range(2):
+            for name, h in handles.items():
+                for d, fn in (("scatter", K.kv_scatter_chunks), ("gather", K.kv_gather_chunks)):
+                    fn(h, spans, spec, stream)
+                    K.kv_pool_timing_start(h)
+                    for _ in range(4):
+                        fn(h, spans, spec, stream)
+                    res.setdefault((name, d), []).extend(K.kv_pool_timing_read_each(h).tolist())
+        for h in handles.values():
+            assert K.kv_pool_get_error(h, stream) == 0
+    finally:
+        torch.cuda.synchronize()
+        for h in handles.values():
+            K.kv_pool_destroy(h)
+        del big
+        torch.cuda.empty_cache()
+    frac = {name: {d: round(2 * payload / (float(np.median(res[(name, d)])) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                   for d in ("scatter", "gather")} for name in layouts}
+    return dict(workload="llama8b call; the pool's regions (512 MiB each) at chosen offsets of one 96 GiB "
+                         "allocation", layouts=frac)
 
 
 def traffic_for(direction, algorithmic_bytes_per_launch):
