@@ -661,6 +661,11 @@ def host_leg(args, dev):
                     ms, n = run_pass(fn, 1, wg)
                     row[name] = round(payload_layer * win_layers / (ms * 1e-3) / 1e9, 2)
                 sweep[str(wg)] = row
+        both = duplex(dev, P, spans_d, w, L, win_layers, slot, n_slots, ring, ring_dev, payload_layer, link,
+                      {k: v["gbs"] for k, v in out.items()})
+        log("duplex: default grids %.1f GB/s, best %s workgroups %.1f GB/s, link both ways %.1f GB/s" % (
+            both["default_grid"]["aggregate_gbs"], both["best"]["workgroups"], both["best"]["aggregate_gbs"],
+            both["link_duplex"]["aggregate_gbs"]))
         interference = interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_layer) \
             if args.interference else None
         return dict(workload="llama70b: 80 layers x K/V x 8 x 128 bf16, 16-token pages, one 131072-token "
@@ -668,12 +673,108 @@ def host_leg(args, dev):
                              "%d slots (%d layers per window); library default grid for host staging "
                              "(16 workgroups); sweep_gbs keys are max_workgroups" % (n_slots, win_layers),
                     payload_bytes=payload_layer * L, link_gbs=link, parity=parity, sweep_gbs=sweep, roofline=roof,
-                    per_tile_dma=dma, interference=interference, **out)
+                    per_tile_dma=dma, interference=interference, duplex=both, **out)
     finally:
         K.kv_ring_destroy(ring)
         P.close()
         del P
         torch.cuda.empty_cache()
+
+
+def duplex(dev, P, spans_d, w, L, win_layers, slot, n_slots, ring, ring_dev, payload_layer, link, alone):
+    """Offload and reload at the same time over the host link: scatter windows of layers
+    [0, L/2) from the ring on one stream while gather windows of layers [L/2, L) go into
+    a second ring on another (disjoint layers, so no byte is touched by both); each stream
+    has a hardware queue of its own.  Against two concurrent 2 GiB hipMemcpyAsync, one
+    each way between the same kinds of memory."""
+    import torch
+    from paged_layout_transfer_amd import kvxfer as K
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    ring2 = K.kv_ring_create(slot, n_slots, K.KV_RING_COHERENT)
+    handles = []
+    try:
+        ring2_dev = K.kv_ring_slot(ring2, 0)[1]
+        (h1, s1), (h2, s2) = cu_masked_stream(dev, range(n_cu)), cu_masked_stream(dev, range(n_cu))
+        handles = [h1, h2]
+
+        def spec(l0, base, wg=0):
+            return K.make_chunk_spec(K.KV_LAYER_FIRST, w["chunk_layers"], w["chunk_tokens"], l0, l0 + win_layers,
+                                     base, slot, n_slots, wg)
+
+        half = L // 2
+        n = half // win_layers
+        moved = n * win_layers * payload_layer
+
+        def timed(enqueue_1, enqueue_2):
+            torch.cuda.synchronize()
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(s1)
+            s2.wait_event(e0)
+            enqueue_1()
+            enqueue_2()
+            e1.record(s1)
+            e2.record(s2)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1), e0.elapsed_time(e2)
+
+        def scatters(wg):
+            for i in range(n):
+                K.kv_scatter_chunks(P.h, spans_d, spec(i * win_layers, ring_dev, wg), s1)
+
+        def gathers(wg):
+            for i in range(n):
+                K.kv_gather_chunks(P.h, spans_d, spec(half + i * win_layers, ring2_dev, wg), s2)
+
+        K.kv_scatter_chunks(P.h, spans_d, spec(0, ring_dev), s1)
+        K.kv_gather_chunks(P.h, spans_d, spec(half, ring2_dev), s2)
+        ms1, ms2 = timed(lambda: scatters(0), lambda: gathers(0))
+        sweep = {}
+        for rep in range(3):
+            for wg_s, wg_g in ((16, 16), (8, 8), (8, 6), (8, 4), (6, 4), (6, 2), (4, 2), (10, 2), (6, 3), (5, 2)):
+                m1, m2 = timed(lambda: scatters(wg_s), lambda: gathers(wg_g))
+                sweep.setdefault("%d/%d" % (wg_s, wg_g), []).append(round(2 * moved / (max(m1, m2) * 1e-3) / 1e9, 2))
+        assert K.kv_pool_get_error(P.h, torch.cuda.current_stream()) == 0
+        # the link both ways at once: 2 GiB host->device from one ring, device->host into the other
+        hip = K.hip_runtime()
+        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+        nb = slot * n_slots
+        d1 = torch.empty(nb, dtype=torch.uint8, device=dev)
+        d2 = torch.empty(nb, dtype=torch.uint8, device=dev)
+        host1, host2 = K.kv_ring_slot(ring, 0)[0], K.kv_ring_slot(ring2, 0)[0]
+        best = None
+        for _ in range(3):
+            rc = []
+            m1, m2 = timed(lambda: rc.append(hip.hipMemcpyAsync(d1.data_ptr(), host1, nb, 1, s1.cuda_stream)),
+                           lambda: rc.append(hip.hipMemcpyAsync(host2, d2.data_ptr(), nb, 2, s2.cuda_stream)))
+            assert rc == [0, 0], rc
+            agg = 2 * nb / (max(m1, m2) * 1e-3) / 1e9
+            if best is None or agg > best[0]:
+                best = (agg, nb / (m1 * 1e-3) / 1e9, nb / (m2 * 1e-3) / 1e9)
+        del d1, d2
+        import statistics
+        agg = 2 * moved / (max(ms1, ms2) * 1e-3) / 1e9
+        med = {k: statistics.median(v) for k, v in sweep.items()}
+        top = max(med, key=med.get)
+        return dict(workload="%d windows of %d layers scattered from one ring on one stream while %d windows of "
+                             "the other layers are gathered into a second ring on another; workgroup_sweep keys "
+                             "are scatter/gather max_workgroups, values the aggregate GB/s of 3 rounds"
+                             % (n, win_layers, n),
+                    default_grid=dict(scatter_gbs=round(moved / (ms1 * 1e-3) / 1e9, 2),
+                                      gather_gbs=round(moved / (ms2 * 1e-3) / 1e9, 2), aggregate_gbs=round(agg, 2),
+                                      frac_of_link_duplex=round(agg / best[0], 4)),
+                    best=dict(workgroups=top, aggregate_gbs=round(med[top], 2),
+                              frac_of_link_duplex=round(med[top] / best[0], 4)),
+                    alone_gbs={k: round(v, 2) for k, v in alone.items()},
+                    link_duplex=dict(h2d_gbs=round(best[1], 2), d2h_gbs=round(best[2], 2),
+                                     aggregate_gbs=round(best[0], 2)),
+                    link_one_way=dict(h2d_gbs=round(link["h2d"], 2), d2h_gbs=round(link["d2h"], 2)),
+                    workgroup_sweep=sweep)
+    finally:
+        torch.cuda.synchronize()
+        for h in handles:
+            destroy_stream(h)
+        K.kv_ring_destroy(ring2)
 
 
 def _hip():

@@ -122,3 +122,75 @@ def test_ring_fencing_rejects_bad_ranges():
         torch.cuda.synchronize()
     finally:
         K.kv_ring_destroy(ring)
+
+
+@pytest.mark.parametrize("grids", [(0, 0), (6, 2)])
+def test_offload_and_reload_at_once_on_two_streams(grids):
+    """A reload (scatter of layers [0, 4) from one pinned ring) and an offload (gather of
+    layers [4, 8) into another) queued on two streams with nothing ordering them, so
+    both directions of the host link are in use at once; several windows each.  The
+    default grids and the 6 / 2 split that measured fastest for such a pair.  The
+    pool must equal the oracle's scatter of the reload rings (the offloaded layers and
+    every block outside the table unchanged), and each offload ring the oracle's
+    gather."""
+    dev = torch.device("cuda", 0)
+    L, KV, H, D, E, bs, N = 8, 2, 4, 64, 2, 16, 96
+    tok = H * D * E
+    T = 1000                        # 63 pages, last one partial
+    CT, CL, win = 256, 1, 2
+    n_tc = cases.cdiv(T, CT)
+    n_slots = win * n_tc
+    slot = CL * KV * CT * tok
+    pool = dict(num_layers=L, num_kv=KV, num_heads=H, head_dim=D, elem_bytes=E, block_size=bs,
+                num_blocks=N, block_stride=bs * tok)
+    rng = np.random.default_rng(80_500 + grids[0])
+    table = rng.permutation(N)[:cases.cdiv(T, bs)].astype(np.int32)
+    regions = rng.integers(0, 256, size=(L * KV, N * bs * tok), dtype=np.uint8)
+    src = rng.integers(0, 256, size=(L // 2 // win, slot * n_slots), dtype=np.uint8)   # per reload window
+    pool_d = torch.from_numpy(regions).to(dev)
+    tab_d = torch.from_numpy(table).to(dev)
+    h = K.kv_pool_create(K.make_pool_desc(L, KV, H, D, E, bs, N, bs * tok,
+                                          [pool_d.data_ptr() + i * pool_d.stride(0) for i in range(L * KV)]))
+    n_win = L // 2 // win
+    rings_in = [K.kv_ring_create(slot, n_slots) for _ in range(n_win)]
+    rings_out = [K.kv_ring_create(slot, n_slots) for _ in range(n_win)]
+    s_in, s_out = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        for i, r in enumerate(rings_in):
+            K.ring_host_array(r, slot * n_slots)[:] = src[i]
+        for r in rings_out:
+            K.ring_host_array(r, slot * n_slots)[:] = W.SENTINEL
+        spans = K.make_spans([(tab_d, tab_d.numel(), 0, T, 0)])
+
+        def spec(l0, ring, wg):
+            return K.make_chunk_spec(K.KV_LAYER_FIRST, CL, CT, l0, l0 + win, K.kv_ring_slot(ring, 0)[1], slot,
+                                     n_slots, wg)
+
+        torch.cuda.synchronize()
+        print("[gpu] reload layers 0-3 and offload layers 4-7 at once, grids %s" % (grids,), flush=True)
+        for i in range(n_win):
+            K.kv_scatter_chunks(h, spans, spec(i * win, rings_in[i], grids[0]), s_in)
+            K.kv_gather_chunks(h, spans, spec(L // 2 + i * win, rings_out[i], grids[1]), s_out)
+        torch.cuda.synchronize()
+        assert K.kv_pool_get_error(h, torch.cuda.current_stream()) == 0
+        got = pool_d.cpu().numpy()
+        exp = regions.copy()
+        for i in range(n_win):
+            ch = dict(layout=K.KV_LAYER_FIRST, chunk_layers=CL, chunk_tokens=CT, layer_begin=i * win,
+                      layer_end=(i + 1) * win, slot_bytes=slot, n_slots=n_slots)
+            oracle.scatter(pool, [exp[r] for r in range(L * KV)], [(table, 0, T, 0)], ch, src[i].copy(),
+                           only_layers=(i * win, (i + 1) * win))
+        assert np.array_equal(got, exp), "pool after the reload differs from the oracle"
+        for i in range(n_win):
+            ch = dict(layout=K.KV_LAYER_FIRST, chunk_layers=CL, chunk_tokens=CT, layer_begin=L // 2 + i * win,
+                      layer_end=L // 2 + (i + 1) * win, slot_bytes=slot, n_slots=n_slots)
+            want = np.full(slot * n_slots, W.SENTINEL, dtype=np.uint8)
+            oracle.gather(pool, [regions[r] for r in range(L * KV)], [(table, 0, T, 0)], ch, want,
+                          only_layers=(L // 2 + i * win, L // 2 + (i + 1) * win))
+            assert np.array_equal(K.ring_host_array(rings_out[i], slot * n_slots), want), \
+                "offload window %d differs from the oracle" % i
+    finally:
+        torch.cuda.synchronize()
+        for r in rings_in + rings_out:
+            K.kv_ring_destroy(r)
+        K.kv_pool_destroy(h)
