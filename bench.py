@@ -661,11 +661,13 @@ def host_leg(args, dev):
                     ms, n = run_pass(fn, 1, wg)
                     row[name] = round(payload_layer * win_layers / (ms * 1e-3) / 1e9, 2)
                 sweep[str(wg)] = row
-        both = duplex(dev, P, spans_d, w, L, win_layers, slot, n_slots, ring, ring_dev, payload_layer, link,
-                      {k: v["gbs"] for k, v in out.items()})
-        log("duplex: default grids %.1f GB/s, best %s workgroups %.1f GB/s, link both ways %.1f GB/s" % (
-            both["default_grid"]["aggregate_gbs"], both["best"]["workgroups"], both["best"]["aggregate_gbs"],
-            both["link_duplex"]["aggregate_gbs"]))
+        both = None
+        if args.duplex:
+            both = duplex(dev, P, spans_d, w, L, win_layers, slot, n_slots, ring, ring_dev, payload_layer, link,
+                          {k: v["gbs"] for k, v in out.items()})
+            log("duplex: default grids %.1f GB/s, best %s workgroups %.1f GB/s, link both ways %.1f GB/s" % (
+                both["default_grid"]["aggregate_gbs"], both["best"]["workgroups"], both["best"]["aggregate_gbs"],
+                both["link_duplex"]["aggregate_gbs"]))
         interference = interference_leg(args, dev, P, spans_d, spec_for, L, win_layers, payload_layer) \
             if args.interference else None
         return dict(workload="llama70b: 80 layers x K/V x 8 x 128 bf16, 16-token pages, one 131072-token "
@@ -1205,6 +1207,8 @@ def main():
                     help="skip the compute-beside-transfer measurement")
     ap.add_argument("--no-placement", dest="placement", action="store_false",
                     help="skip the scatter measured on pools of different physical placement")
+    ap.add_argument("--no-duplex", dest="duplex", action="store_false",
+                    help="skip the reload-and-offload-at-once measurement of the host path")
     ap.add_argument("--no-small-calls", dest="small_calls", action="store_false",
                     help="skip the per-call cost of small transfers")
     ap.add_argument("--no-dma-baseline", dest="dma_baseline", action="store_false",
@@ -1230,7 +1234,7 @@ def main():
     host = host_leg(args, dev) if args.host_path else None
     before = [args.workload] + (["llama70b"] if args.host_path else [])
     hm = ["llama8b_hnd", "fp8_hnd_d64", "hnd_rows24", "hnd_h100_r12"]
-    names = ["mixed", "mla_fp8", "int8_kv", "llama8b_tp8"] + [x for n in hm for x in (n, n + ":token_major")]
+    names = ["mixed", "mla_fp8", "int8_kv", "llama8b_tp8", "llama8b_tp2"] + [x for n in hm for x in (n, n + ":token_major")]
     others = other_workloads(dev, names, 10, before) if args.others else None
     pipeline = pipeline_leg(args, dev) if args.pipeline else None
     placement = placement_leg(args, dev) if args.placement else None

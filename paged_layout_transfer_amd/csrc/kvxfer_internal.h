@@ -57,16 +57,18 @@ namespace kvx {
 #ifndef KVX_SCATTER_PART_BYTES
 #define KVX_SCATTER_PART_BYTES 16384
 #endif
-// Gather of token-major pages whose tile size is not a power of two (and at least
-// SEG_MIN) runs over the call's tiles laid end to end in SEG_BYTES segments, one per
-// wave, instead of one tile per wave: each wave then writes one aligned 32 KiB piece
-// of the chunk stream, which measured 2-9 % faster for 24-40 KiB tiles on MI355X
-// (32 KiB tiles are the two schedules' common case; 16, 24 and 48 KiB segments lose).
+// Gather of token-major pages whose tiles are at least SEG_MIN bytes and either not a
+// power of two or smaller than a segment runs over the call's tiles laid end to end in
+// SEG_BYTES segments, one per wave, instead of one tile per wave: each wave then writes
+// one aligned 32 KiB piece of the chunk stream.  Measured on MI355X: 2-9 % faster for
+// 24-40 KiB tiles, 1.6 points for 12 KiB and 4 points for 16 KiB tiles; 4 KiB tiles
+// lose 7 points, so they keep a wave each (32 KiB tiles are the two schedules' common
+// case; 16, 24 and 48 KiB segments lose).
 #ifndef KVX_GATHER_SEG_BYTES
 #define KVX_GATHER_SEG_BYTES 32768
 #endif
 #ifndef KVX_GATHER_SEG_MIN
-#define KVX_GATHER_SEG_MIN 16384
+#define KVX_GATHER_SEG_MIN 8192
 #endif
 #ifndef KVX_MAX_SPLIT_SHIFT
 #define KVX_MAX_SPLIT_SHIFT 2     // at most 4 waves per tile
@@ -484,7 +486,8 @@ __host__ __device__ inline void hm_page_slice_words(const Launch &a, uint32_t v,
 __host__ __device__ constexpr uint32_t gather_seg_bytes(int dir, uint32_t page_layout, int64_t tile_bytes)
 {
     return (dir == KV_GATHER && page_layout == KV_PAGE_TOKEN_MAJOR && KVX_GATHER_SEG_BYTES > 0 &&
-            tile_bytes >= KVX_GATHER_SEG_MIN && (tile_bytes & (tile_bytes - 1)) != 0)
+            tile_bytes >= KVX_GATHER_SEG_MIN &&
+            ((tile_bytes & (tile_bytes - 1)) != 0 || tile_bytes < KVX_GATHER_SEG_BYTES))
                ? (uint32_t)KVX_GATHER_SEG_BYTES
                : 0u;
 }

@@ -84,7 +84,7 @@ def test_cpu_baseline_rate_is_bytes_moved_over_oracle_time():
     assert bench.cpu_baseline(dict(cpu=None)) is None
 
 
-@pytest.mark.parametrize("flag", ["--no-small-calls", "--no-placement", "--no-host-path"])
+@pytest.mark.parametrize("flag", ["--no-small-calls", "--no-placement", "--no-host-path", "--no-duplex"])
 def test_bench_flags_parse(flag):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "3", flag],
                        capture_output=True, text=True, timeout=120)
