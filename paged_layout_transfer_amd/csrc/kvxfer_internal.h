@@ -57,18 +57,34 @@ namespace kvx {
 #ifndef KVX_SCATTER_PART_BYTES
 #define KVX_SCATTER_PART_BYTES 16384
 #endif
+// Token-major tiles of SMALL_SPLIT_MIN bytes up to (not including) SMALL_GATHER_MAX
+// (gather) or SMALL_SCATTER_MAX (scatter) are split the same way into parts of about
+// SMALL_PART bytes: measured on MI355X, gathers of 8 and 12 KiB tiles gain 4 and 6
+// points that way (over one tile or one segment per wave), scatters of 8, 12 and 16 KiB
+// tiles 1.1, 1.4 and 2.3 points; a 20 KiB scatter loses 0.9.
+#ifndef KVX_SMALL_SPLIT_MIN
+#define KVX_SMALL_SPLIT_MIN 8192
+#endif
+#ifndef KVX_SMALL_GATHER_MAX
+#define KVX_SMALL_GATHER_MAX 16384
+#endif
+#ifndef KVX_SMALL_SCATTER_MAX
+#define KVX_SMALL_SCATTER_MAX 20480
+#endif
+#ifndef KVX_SMALL_PART
+#define KVX_SMALL_PART 2048
+#endif
 // Gather of token-major pages whose tiles are at least SEG_MIN bytes and either not a
 // power of two or smaller than a segment runs over the call's tiles laid end to end in
 // SEG_BYTES segments, one per wave, instead of one tile per wave: each wave then writes
 // one aligned 32 KiB piece of the chunk stream.  Measured on MI355X: 2-9 % faster for
-// 24-40 KiB tiles, 1.6 points for 12 KiB and 4 points for 16 KiB tiles; 4 KiB tiles
-// lose 7 points, so they keep a wave each (32 KiB tiles are the two schedules' common
-// case; 16, 24 and 48 KiB segments lose).
+// 24-40 KiB tiles and 4 points for 16 KiB tiles (32 KiB tiles are the two schedules'
+// common case; 16, 24 and 48 KiB segments lose).
 #ifndef KVX_GATHER_SEG_BYTES
 #define KVX_GATHER_SEG_BYTES 32768
 #endif
 #ifndef KVX_GATHER_SEG_MIN
-#define KVX_GATHER_SEG_MIN 8192
+#define KVX_GATHER_SEG_MIN 16384
 #endif
 #ifndef KVX_MAX_SPLIT_SHIFT
 #define KVX_MAX_SPLIT_SHIFT 2     // at most 4 waves per tile
@@ -340,10 +356,18 @@ __host__ __device__ constexpr uint32_t split_shift_for(int dir, int64_t tile_byt
 }
 
 // log2 of the parts each tile of a prepared call is split into for direction dir: a
-// head-major page moved whole through one wave's slice (hm_page) is never split.
+// head-major page moved whole through one wave's slice (hm_page) is never split, small
+// token-major tiles follow the SMALL_* rule, the rest split_shift_for.
 __host__ __device__ inline uint32_t launch_split_shift(const Launch &a, int dir)
 {
-    return a.hm_page ? 0u : split_shift_for(dir, a.tile_bytes);
+    if (a.hm_page) return 0u;
+    const int64_t small_max = dir == KV_GATHER ? KVX_SMALL_GATHER_MAX : KVX_SMALL_SCATTER_MAX;
+    if (a.page_layout == KV_PAGE_TOKEN_MAJOR && a.tile_bytes >= KVX_SMALL_SPLIT_MIN && a.tile_bytes < small_max) {
+        uint32_t sh = 0;
+        while (sh < KVX_MAX_SPLIT_SHIFT && a.tile_bytes >= ((int64_t)KVX_SMALL_PART << (sh + 1))) ++sh;
+        return sh;
+    }
+    return split_shift_for(dir, a.tile_bytes);
 }
 
 // Head-major pages whose head rows are 256 bytes (16 vectors, one 16-lane row of a

@@ -1,9 +1,9 @@
 // kvxfer_kernels.hip -- the gather/scatter tile-copy kernel for gfx950.
 //
 // One 64-lane wavefront copies one (layer, kv, page) tile -- or one part of a large
-// tile, or, for a gather over token-major tiles of 8 KiB or more that are not whole
-// 32 KiB segments, one 32 KiB segment of the tiles laid end to end -- per iteration
-// of a grid-stride loop.  Per
+// or 8-16 KiB tile, or, for a gather over token-major tiles of 16 KiB or more that are
+// not whole 32 KiB segments, one 32 KiB segment of the tiles laid end to end -- per
+// iteration of a grid-stride loop.  Per
 // tile it
 //   1. finds the span (binary search over the per-span tile prefix, wave-uniform,
 //      so it runs on the scalar unit with scalar loads),

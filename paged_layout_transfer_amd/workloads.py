@@ -13,7 +13,7 @@ values, so random bytes of the stated element width are used.
 
 Seeds: table/length seed 1000 + k and data seed k for workload k
 (tiny 1, llama8b 2, llama70b 3, mixed 4, mla_fp8 5, int8_kv 6, llama8b_hnd 7,
-fp8_hnd_d64 8, llama8b_tp8 9, hnd_rows24 10, hnd_h100_r12 11, llama8b_tp2 12).  page_layout (default 0) is the pool's in-page order: 0 token-major
+fp8_hnd_d64 8, llama8b_tp8 9, hnd_rows24 10, hnd_h100_r12 11, llama8b_tp2 12, llama8b_tp4 13).  page_layout (default 0) is the pool's in-page order: 0 token-major
 [block_size][H][D], 1 head-major [H][block_size][D].
 """
 from __future__ import annotations
@@ -58,6 +58,11 @@ WORKLOADS: dict[str, dict] = {
     # One GPU's share of the llama8b context under 8-way tensor parallelism: the 8 KV
     # heads split one per GPU, so 16-token pages of 1 head x 128 bf16 = 4 KiB tiles.
     "llama8b_tp8": dict(k=9, num_layers=32, num_kv=2, num_heads=1, head_dim=128, elem_bytes=2,
+                        block_size=16, num_blocks=16384, tokens=32768, fill="bf16_uniform",
+                        layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm"),
+    # One GPU's share under 4-way tensor parallelism: 2 KV heads per GPU, 16-token pages
+    # of 2 heads x 128 bf16 = 8 KiB tiles.
+    "llama8b_tp4": dict(k=13, num_layers=32, num_kv=2, num_heads=2, head_dim=128, elem_bytes=2,
                         block_size=16, num_blocks=16384, tokens=32768, fill="bf16_uniform",
                         layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm"),
     # One GPU's share under 2-way tensor parallelism: 4 KV heads per GPU, 16-token pages

@@ -163,6 +163,7 @@ REDUCED = {
     "int8_kv": dict(num_layers=3, chunk_layers=3, tokens=64 * 7 + 1, num_blocks=30),
     "llama8b_tp8": dict(num_layers=4, chunk_layers=2, tokens=16 * 37 + 9, num_blocks=80),
     "llama8b_tp2": dict(num_layers=4, chunk_layers=4, tokens=16 * 41 + 3, num_blocks=90),
+    "llama8b_tp4": dict(num_layers=4, chunk_layers=2, tokens=16 * 45 + 7, num_blocks=100),
 }
 
 
