@@ -11,7 +11,8 @@ one left behind.  A block id out of range must set the caller's error word.
 Under graph capture: a noalloc call whose span records ride in the kernel arguments
 is captured and replayed (each replay after another pool's call has rewritten the
 device scratch, each checked against the allocating entry point); a noalloc call with
-more records, and the allocating entry points, are refused while the stream captures.
+more records, and the allocating entry points, are refused while the stream captures;
+several calls captured into one graph replay in order.
 """
 from __future__ import annotations
 
@@ -242,4 +243,55 @@ def test_capture_refuses_calls_that_cannot_replay():
         for r, st in c.results():
             assert np.array_equal(st, es) and np.array_equal(r, er)
     finally:
+        c.close()
+
+
+def test_several_noalloc_calls_in_one_captured_graph():
+    """One call per layer chunk of a pool, each into its own staging buffer, captured in
+    order on one stream: each carries its own copy of the region table into the shared
+    device scratch and the graph's nodes run in capture order, so every replay equals
+    the same calls made eagerly through the allocating entry point, buffer for buffer."""
+    dev = _dev()
+    pool, spans, chunks = _case(88_044, 3, False)
+    c = Call(pool, spans, chunks, seed=61, dev=dev)
+    ref, side = c.sides[0], c.sides[1]
+    CL = chunks["chunk_layers"]
+    wins = [(lo, lo + CL) for lo in range(chunks["layer_begin"], chunks["layer_end"], CL)]
+    assert len(wins) >= 3
+    nbytes = chunks["slot_bytes"] * chunks["n_slots"]
+    start = torch.from_numpy(c.staging.copy()).to(dev)
+    ref_stg = [start.clone() for _ in wins]
+    side_stg = [start.clone() for _ in wins]
+    stream = torch.cuda.current_stream()
+    g = None
+
+    def spec(buf, lo, hi):
+        return K.make_chunk_spec(chunks["layout"], CL, chunks["chunk_tokens"], lo, hi, buf, chunks["slot_bytes"],
+                                 chunks["n_slots"])
+
+    try:
+        assert start.numel() == nbytes
+        for (lo, hi), b in zip(wins, ref_stg):
+            K.kv_gather_chunks(ref["h"], c.sp, spec(b, lo, hi), stream)
+        for (lo, hi), b in zip(wins, side_stg):  # warm the pool's caches outside capture
+            K.kv_transfer_chunks_noalloc(side["h"], K.KV_GATHER, c.sp, spec(b, lo, hi), None, stream)
+        torch.cuda.synchronize()
+        want = [b.cpu().numpy() for b in ref_stg]
+        print("[noalloc] %d gather windows captured in one graph" % len(wins), flush=True)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cap):
+            for (lo, hi), b in zip(wins, side_stg):
+                K.kv_transfer_chunks_noalloc(side["h"], K.KV_GATHER, c.sp, spec(b, lo, hi), None, cap)
+        for rep in range(3):
+            for b in side_stg:
+                b.copy_(start)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for w, (b, e) in enumerate(zip(side_stg, want)):
+                assert np.array_equal(b.cpu().numpy(), e), "replay %d, window %d differs" % (rep, w)
+            assert not all(np.array_equal(e, c.staging) for e in want)
+    finally:
+        del g
         c.close()
