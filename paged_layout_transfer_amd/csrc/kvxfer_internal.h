@@ -111,7 +111,7 @@ namespace kvx {
 #define KVX_HM_T4_UNITS 8      // 4x4 blocks (4 KiB each) in flight per wave, head-major pages
 #endif
 #ifndef KVX_HM_LDS_SLICE
-#define KVX_HM_LDS_SLICE 8192  // LDS bytes per wave, head-major rows not of whole 16-byte vectors
+#define KVX_HM_LDS_SLICE 8192  // LDS bytes per wave, head-major rows staged through LDS (hm_lds_ok)
 #endif
 #ifndef KVX_HM_PAGE_SLICE
 #define KVX_HM_PAGE_SLICE 20480  // LDS bytes per wave, head-major pages of 4-byte-word rows moved whole
@@ -198,7 +198,7 @@ struct Launch {
     uint32_t cached;       // 1: plain cached loads and stores (KV_FLAG_CACHED), else nontemporal
     uint32_t seg_bytes;    // > 0: gather in segments of this many bytes (gather_seg_bytes)
     uint32_t hm_t4;        // 1: head-major pages moved in 4-token x 4-head blocks (hm_t4_ok)
-    // head-major pages whose head rows are not whole 16-byte vectors (hm_lds_ok): row
+    // head-major pages whose rows are staged through LDS (hm_lds_ok): row
     // bytes, 4-byte words per row, tokens per LDS slab (hm_lds_tokens), and the
     // multipliers (magic_u16) that divide by hm_rd and by hm_tj * hm_rd
     uint32_t hm_lds;
@@ -386,15 +386,22 @@ __host__ __device__ inline uint32_t hm_t4_units(uint32_t n_tok, uint32_t heads)
     return ((n_tok + 3) / 4) * (heads / 4);
 }
 
-// Head-major pages whose head rows (row = D*E bytes) are not whole 16-byte vectors go
-// through a per-wave LDS slice in slabs of whole tokens: rows must be whole 4-byte
-// words and one token (all heads) must fit the slice.
+// Head-major pages whose head rows (row = D*E bytes) are not whole 16-byte vectors, or
+// are whole vectors but shorter than the 256 bytes of the 4 x 4 register transpose, go
+// through a per-wave LDS slice in slabs of whole tokens: rows must be whole 4-byte words
+// and one token (all heads) must fit the slice.  For rows of whole vectors the slabs
+// replace the per-lane cursor walk (copy_head_major), which measured on MI355X slower
+// on almost every such shape: 8 heads x 64-byte rows gather 66 -> 73 %, 8 heads x
+// 80-224-byte rows gather +2 to +9 and scatter +15 to +27 points, 16 heads x 32- or
+// 64-byte rows scatter +13 to +17; only 128-byte rows in 16-32 KiB pages lose 1-2
+// points.  Rows of whole vectors with a token larger than the slice keep the cursor walk.
 __host__ __device__ constexpr bool hm_lds_ok(uint32_t page_layout, int64_t row, int64_t tok)
 {
-    return page_layout == KV_PAGE_HEAD_MAJOR && row % 16 != 0 && row % 4 == 0 && tok <= KVX_HM_LDS_SLICE;
+    return page_layout == KV_PAGE_HEAD_MAJOR && (row % 16 != 0 || row < 256) && row % 4 == 0 &&
+           tok <= KVX_HM_LDS_SLICE;
 }
 
-// Head-major pages of 4-byte-word rows whose page is larger than a token slab's slice
+// Head-major pages of LDS-staged rows (hm_lds_ok) whose page is larger than a token slab's slice
 // but fits a page slice are moved a whole page at a time: the block is one contiguous
 // run of tile_bytes, read or written in 16-byte vectors, and transposed in LDS; so no
 // pool line is split between slabs.

@@ -430,8 +430,9 @@ __device__ __forceinline__ void st_pool_word(gword *p, uint32_t v)
     st_word<NT && KVX_HM_LDS_POOL_NT>(p, v);
 }
 
-// Head-major pages whose head rows are not whole 16-byte vectors (rows of rd 4-byte
-// words): slabs [s0, s1) of all heads x tj tokens (hm_lds_tokens) pass through this
+// Head-major pages staged through LDS (hm_lds_ok: rows of rd 4-byte words that are not
+// whole 16-byte vectors, or are but are shorter than 256 bytes): slabs [s0, s1) of all
+// heads x tj tokens (hm_lds_tokens) pass through this
 // wave's LDS slice, which holds a slab in chunk (token-major) order, so the chunk side
 // moves whole 16-byte vectors of the slab's contiguous run.  The pool side is the
 // slab's run of tj rows in each head, moved as 4-byte words with consecutive lanes on
