@@ -238,7 +238,8 @@ int prepare_with(const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
         const uint32_t H = (uint32_t)d->num_heads;
         a->hm_heads = H;
         a->hm_row = (uint32_t)row;
-        if (kvx::hm_lds_ok(a->page_layout, row, tok_bytes(d))) {
+        if (kvx::hm_lds_use(a->page_layout, row, tok_bytes(d), tok_bytes(d) * d->block_size, H,
+                            (uint32_t)d->block_size)) {
             a->hm_lds = 1;
             a->hm_rd = (uint32_t)(row / 4);
             a->hm_tj = kvx::hm_lds_tokens(row, tok_bytes(d), (uint32_t)d->block_size);

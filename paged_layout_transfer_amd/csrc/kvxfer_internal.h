@@ -401,6 +401,19 @@ __host__ __device__ constexpr bool hm_lds_ok(uint32_t page_layout, int64_t row, 
            tok <= KVX_HM_LDS_SLICE;
 }
 
+// Whether a head-major pool's pages go through the LDS slabs: the rows hm_lds_ok names,
+// and also longer rows of whole vectors (other than the 4 x 4 register-transpose case)
+// when the whole page fits one slab: measured on MI355X, 8 KiB pages of 2 x 256-byte or
+// 1 x 512-byte rows gather 67 -> 73-74 % that way (scatter -0.7), while 4 and 12 KiB
+// pages stay within 1.5 points either way and larger ones lose up to 2.
+__host__ __device__ constexpr bool hm_lds_use(uint32_t page_layout, int64_t row, int64_t tok, int64_t tile,
+                                              uint32_t heads, uint32_t block_size)
+{
+    return hm_lds_ok(page_layout, row, tok) ||
+           (page_layout == KV_PAGE_HEAD_MAJOR && row % 16 == 0 && tile <= KVX_HM_LDS_SLICE &&
+            !hm_t4_ok(page_layout, (uint32_t)(row / 16), heads, block_size));
+}
+
 // Head-major pages of LDS-staged rows (hm_lds_ok) whose page is larger than a token slab's slice
 // but fits a page slice are moved a whole page at a time: the block is one contiguous
 // run of tile_bytes, read or written in 16-byte vectors, and transposed in LDS; so no
