@@ -619,6 +619,25 @@ extern "C" int64_t emu_arena(int64_t size, const int64_t *sizes, int64_t n_calls
 }
 
 // The launch-shape rules of the library's host preparation, for direct checks.
+// The launch decisions for one call: out[0] split shift, out[1] segment bytes, out[2]
+// LDS-staged head-major rows, out[3] whole-page head-major path, out[4] 4 x 4 transpose.
+extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
+                               const kv_chunk_spec *spec, int64_t *out)
+{
+    static kvx::SpanDev records[KV_MAX_SPANS];
+    uint32_t n_rec = 0;
+    kvx::Launch a;
+    kv_transfer_info info;
+    const int rc = kvx::prepare_call(d, spans, n_spans, spec, records, &n_rec, &a, &info);
+    if (rc) return rc;
+    out[0] = kvx::launch_split_shift(a, direction);
+    out[1] = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
+    out[2] = a.hm_lds;
+    out[3] = a.hm_page;
+    out[4] = a.hm_t4;
+    return KV_OK;
+}
+
 extern "C" int emu_gather_seg_unroll(int64_t tile_bytes, int64_t seg_bytes)
 {
     return kvx::gather_seg_unroll(tile_bytes, seg_bytes);

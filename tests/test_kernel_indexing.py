@@ -39,6 +39,9 @@ def _build_emu(tmp_path_factory, defines=()):
                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.emu_arena.restype = ctypes.c_int64
     lib.emu_arena.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
+    lib.emu_launch_rule.restype = ctypes.c_int
+    lib.emu_launch_rule.argtypes = [ctypes.c_int, ctypes.POINTER(K.kv_pool_desc), ctypes.POINTER(K.kv_span),
+                                    ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.POINTER(ctypes.c_int64)]
     lib.emu_gather_seg_unroll.restype = ctypes.c_int
     lib.emu_gather_seg_unroll.argtypes = [ctypes.c_int64, ctypes.c_int64]
     lib.emu_hm_page_ok.restype = ctypes.c_int32
@@ -451,3 +454,64 @@ def test_extent_check_reuses_a_walk_over_pieces_while_its_ends_stand(emu):
     keep = _allocs(emu, [(A, 2 * MB), (A + 2 * MB, 2 * MB), (A + 4 * MB, 2 * MB)])
     assert emu.emu_cache_covers(A, 6 * MB, ctypes.byref(n)) == 1
     del keep
+
+
+FAKE_BASE = 1 << 40   # addresses are only formed, never dereferenced, by the launch rules
+
+
+def _rule(lib, direction, H, D, E, bs=16, page_layout=0):
+    """The launch decisions for a one-page call of a pool with H x D x E-byte rows."""
+    tok = H * D * E
+    desc = K.make_pool_desc(2, 2, H, D, E, bs, 4, bs * tok, [FAKE_BASE + i * (1 << 24) for i in range(4)],
+                            page_layout)
+    tab = np.arange(4, dtype=np.int32)
+    sp = K.make_spans([(tab.ctypes.data, 4, 0, bs, 0)])
+    spec = K.make_chunk_spec(K.KV_LAYER_FIRST, 2, bs, 0, 2, FAKE_BASE + (1 << 30), 2 * 2 * bs * tok, 1)
+    out = (ctypes.c_int64 * 5)()
+    assert lib.emu_launch_rule(direction, ctypes.byref(desc), sp, 1, ctypes.byref(spec), out) == 0
+    return dict(shift=out[0], seg=out[1], lds=out[2], page=out[3], t4=out[4])
+
+
+@pytest.mark.parametrize("H,D,E,gather,scatter", [
+    # token-major tiles: 4 KiB one wave; 8-12 KiB gathers and 8-16 KiB scatters in 4 parts
+    # of 2 KiB or more; 16-31 KiB gathers in 32 KiB segments; 20-32 KiB scatters whole;
+    # 64 KiB gathers in 2 parts, scatters in 4
+    (1, 128, 2, (0, 0), (0, 0)),
+    (2, 128, 2, (2, 0), (2, 0)),
+    (3, 128, 2, (2, 0), (2, 0)),
+    (4, 128, 2, (None, 32768), (2, 0)),
+    (5, 128, 2, (None, 32768), (0, 0)),
+    (8, 128, 2, (0, 0), (0, 0)),
+    (16, 128, 2, (1, 0), (2, 0)),
+    (9, 128, 2, (None, 32768), (0, 0)),
+])
+def test_token_major_launch_rules(emu, H, D, E, gather, scatter):
+    """The measured split and segment rules, pinned to worked tile sizes."""
+    for d, (shift, seg) in ((K.KV_GATHER, gather), (K.KV_SCATTER, scatter)):
+        r = _rule(emu, d, H, D, E)
+        assert r["seg"] == seg, (d, r)
+        if shift is not None:
+            assert r["shift"] == shift, (d, r)
+        assert not (r["lds"] or r["page"] or r["t4"])
+
+
+@pytest.mark.parametrize("H,D,E,bs,path", [
+    (8, 128, 2, 16, "t4"),        # 256-byte rows, heads and tokens multiples of 4
+    (8, 64, 1, 16, "lds"),        # 64-byte rows, 8 KiB page: token slab
+    (8, 64, 2, 16, "page"),       # 128-byte rows, 16 KiB page: whole page
+    (16, 64, 2, 16, "lds"),       # 128-byte rows, 32 KiB page: slabs
+    (2, 128, 2, 16, "lds"),       # 256-byte rows, 2 heads, 8 KiB page
+    (1, 256, 2, 16, "lds"),       # 512-byte rows, 8 KiB page
+    (3, 128, 2, 16, "cursor"),    # 256-byte rows, 12 KiB page, heads not a multiple of 4
+    (1, 128, 2, 32, "lds"),       # 256-byte rows, 1 head, 8 KiB page
+    (2, 256, 2, 16, "cursor"),    # 512-byte rows, 16 KiB page
+    (130, 32, 2, 16, "cursor"),   # 64-byte rows, but a token (8320 bytes) exceeds the slice
+    (64, 128, 2, 16, "t4"),       # 16 KiB tokens, 256-byte rows: the 4 x 4 transpose needs no slice
+    (6, 12, 2, 64, "page"),       # 24-byte rows (4-byte words), 9 KiB page: whole page
+])
+def test_head_major_path_rules(emu, H, D, E, bs, path):
+    """Which head-major path a pool takes, pinned to worked shapes (both directions)."""
+    for d in (K.KV_GATHER, K.KV_SCATTER):
+        r = _rule(emu, d, H, D, E, bs, page_layout=1)
+        got = "t4" if r["t4"] else "page" if r["page"] else "lds" if r["lds"] else "cursor"
+        assert got == path, (H, D, E, bs, r)
