@@ -1233,7 +1233,7 @@ def main():
     cpu = cpu_baseline(res) if args.cpu_baseline else None
     host = host_leg(args, dev) if args.host_path else None
     before = [args.workload] + (["llama70b"] if args.host_path else [])
-    hm = ["llama8b_hnd", "fp8_hnd_d64", "hnd_rows24", "hnd_h100_r12"]
+    hm = ["llama8b_hnd", "llama8b_hnd_tp4", "fp8_hnd_d64", "hnd_rows24", "hnd_h100_r12"]
     names = ["mixed", "mla_fp8", "int8_kv", "llama8b_tp8", "llama8b_tp4", "llama8b_tp2"] + [x for n in hm for x in (n, n + ":token_major")]
     others = other_workloads(dev, names, 10, before) if args.others else None
     pipeline = pipeline_leg(args, dev) if args.pipeline else None

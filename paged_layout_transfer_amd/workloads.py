@@ -13,7 +13,8 @@ values, so random bytes of the stated element width are used.
 
 Seeds: table/length seed 1000 + k and data seed k for workload k
 (tiny 1, llama8b 2, llama70b 3, mixed 4, mla_fp8 5, int8_kv 6, llama8b_hnd 7,
-fp8_hnd_d64 8, llama8b_tp8 9, hnd_rows24 10, hnd_h100_r12 11, llama8b_tp2 12, llama8b_tp4 13).  page_layout (default 0) is the pool's in-page order: 0 token-major
+fp8_hnd_d64 8, llama8b_tp8 9, hnd_rows24 10, hnd_h100_r12 11, llama8b_tp2 12, llama8b_tp4 13,
+llama8b_hnd_tp4 14).  page_layout (default 0) is the pool's in-page order: 0 token-major
 [block_size][H][D], 1 head-major [H][block_size][D].
 """
 from __future__ import annotations
@@ -70,6 +71,12 @@ WORKLOADS: dict[str, dict] = {
     "llama8b_tp2": dict(k=12, num_layers=32, num_kv=2, num_heads=4, head_dim=128, elem_bytes=2,
                         block_size=16, num_blocks=16384, tokens=32768, fill="bf16_uniform",
                         layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm"),
+    # One GPU's share under 4-way tensor parallelism with head-major pages: 2 heads of
+    # 256-byte rows per 16-token page (8 KiB).
+    "llama8b_hnd_tp4": dict(k=14, num_layers=32, num_kv=2, num_heads=2, head_dim=128, elem_bytes=2,
+                            block_size=16, num_blocks=16384, tokens=32768, fill="bf16_uniform",
+                            layout=LAYER_FIRST, chunk_layers=32, chunk_tokens=256, staging="hbm",
+                            page_layout=1),
     # The llama8b shape with head-major pages ([H][16][128] bf16: 256-byte head rows).
     "llama8b_hnd": dict(k=7, num_layers=32, num_kv=2, num_heads=8, head_dim=128, elem_bytes=2,
                         block_size=16, num_blocks=16384, tokens=32768, fill="bf16_uniform",

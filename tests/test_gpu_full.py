@@ -110,7 +110,7 @@ class Setup:
         return regs
 
 
-HBM_WORKLOADS = ["llama8b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8", "llama8b_tp4", "llama8b_tp2",
+HBM_WORKLOADS = ["llama8b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8", "llama8b_tp4", "llama8b_tp2", "llama8b_hnd_tp4",
                  "hnd_rows24", "hnd_h100_r12"]
 
 

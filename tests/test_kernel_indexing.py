@@ -142,7 +142,7 @@ def test_emulated_split_tiles_match_oracle(emu_split, seed):
 
 
 FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
-        "hnd_rows24", "hnd_h100_r12", "llama8b_tp2", "llama8b_tp4"]
+        "hnd_rows24", "hnd_h100_r12", "llama8b_tp2", "llama8b_tp4", "llama8b_hnd_tp4"]
 
 
 @pytest.mark.parametrize("name", FULL)
