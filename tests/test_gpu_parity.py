@@ -347,6 +347,17 @@ def test_head_major_lds_cases(seed):
                  dma=seed % 4 == 0, flags=flags)
 
 
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("name", sorted(cases.RULE_SHAPES))
+def test_launch_rule_boundaries(name, layout):
+    """Each launch path at the tile sizes around its rule, both chunk layouts, with 1-2
+    spans that start 0-2 pages in and end in a partial page; whole buffers compared."""
+    pool, spans, chunks = cases.rule_case(name, layout)
+    regions, staging = _random(pool, chunks, 98_500 + layout)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "rule-%s-%d" % (name, layout))
+
+
 EXTREMES = {
     # 1-token pages of 16-byte tokens: every tile is one vector
     "one_token_pages": dict(L=3, KV=2, H=1, D=16, E=1, bs=1, N=900, spans=[(0, 500), (0, 77)], CT=64, CL=3),

@@ -141,6 +141,15 @@ def test_emulated_split_tiles_match_oracle(emu_split, seed):
     _copy_case(emu_split, pool, spans, chunks, seed, max_workgroups=int(seed % 3))
 
 
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("name", sorted(cases.RULE_SHAPES))
+def test_emulated_launch_rule_shapes_match_oracle(emu, name, layout):
+    """The calls the GPU parity test runs at each launch rule's boundary: every access
+    inside its buffer and the bytes equal to the oracle's."""
+    pool, spans, chunks = cases.rule_case(name, layout)
+    _copy_case(emu, pool, spans, chunks, 98_500 + layout)
+
+
 FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
         "hnd_rows24", "hnd_h100_r12", "llama8b_tp2", "llama8b_tp4", "llama8b_hnd_tp4"]
 
