@@ -36,10 +36,11 @@
  * num_kv*block_size*tok with bases offset by kv*block_size*tok gives a per-layer
  * [num_blocks][num_kv][block_size][H][D] pool.
  * Placement (measured on MI355X, not part of the contract): scattered page writes
- * into a pool whose regions all lie in one 64 GiB window of the address space run
+ * into a pool whose regions all lie in one 64 GiB window of one plain allocation run
  * at about 68 % of HBM peak, and at about 80 % when the regions span two windows
- * (gathers lose 1-3 points there).  The caller chooses where regions live; a pool
- * larger than 64 GiB spans windows by its size alone.
+ * (gathers lose 1-3 points there).  What decides is the physical memory behind the
+ * addresses, which the library cannot see: the caller chooses where regions live,
+ * and a pool larger than 64 GiB spans windows by its size alone.
  *
  * Span.  (block_table, t_begin, t_end, first_chunk): tokens [t_begin, t_end)
  * of one request, whose token t lives at slot t % block_size of block
