@@ -512,16 +512,18 @@ int check_buffers(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_ch
 }
 
 // The launch of a prepared call (regions, spans and err set): the split and segment
-// choices, the grid (capped by max_workgroups, or small for host staging), and the
-// timing events around the kernel when timing is on.
+// choices, the grid (capped by max_workgroups, or small for host staging), the
+// workgroup order, and the timing events around the kernel when timing is on.
 int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_spec *spec,
                     const kvx::AllocRange &staging, hipStream_t stream)
 {
     a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
+    const bool host_staging = staging_in_host_memory(p, spec->base, staging);
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
-    else if (staging_in_host_memory(p, spec->base, staging)) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
+    else if (host_staging) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
+    a.xcd_remap = kvx::xcd_remap_for(direction, a, host_staging);
     const bool timed = p->timing && p->n_timed < kMaxTimed;
     if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
     if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))

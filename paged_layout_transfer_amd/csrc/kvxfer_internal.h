@@ -218,7 +218,9 @@ struct Launch {
     // head-major pages of 4-byte-word rows moved a whole page at a time (hm_page_ok), with
     // the multiplier dividing by the words of one head's page (block_size * hm_rd)
     uint32_t hm_page;
-    uint32_t hm_pad_;
+    // 1: the workgroups hand each XCD a contiguous eighth of the work items
+    // (launch_block, xcd_remap_for)
+    uint32_t xcd_remap;
     uint64_t hm_m_brd;
     // the span records themselves when n_spans <= KVX_INLINE_SPANS (spans is then
     // unused): 64-byte SpanDev images, read by the kernel from its argument memory
@@ -524,6 +526,34 @@ __host__ __device__ inline void hm_page_slice_words(const Launch &a, uint32_t v,
             }
         }
     }
+}
+
+// The gfx950 dispatcher hands a launch's workgroups to its 8 XCDs round robin
+// (workgroup b to XCD b % 8).  With remap, workgroup b instead takes the work of
+// workgroup (b % 8) * (G8 / 8) + b / 8, G8 = G rounded down to a multiple of 8 (the last
+// G % 8 keep their own): each XCD then walks one contiguous eighth of the items instead
+// of every eighth workgroup's share.  A permutation of [0, G), so every item is still
+// taken exactly once.
+__host__ __device__ constexpr uint32_t launch_block(uint32_t b, uint32_t G, uint32_t remap)
+{
+    return (remap == 0u || b >= (G & ~7u)) ? b : (b & 7u) * ((G & ~7u) >> 3) + (b >> 3);
+}
+
+// Whether a launch remaps its workgroups (launch_block): gathers into HBM staging of
+// tiles walked whole or in parts (not the segment walk), token-major tiles of at least
+// KVX_XCD_REMAP_MIN bytes or head-major pages through the 4 x 4 register transpose.
+// Measured on MI355X, in interleaved rounds in two processes each: gathers of 8, 32 and
+// 64 KiB token-major tiles and of 32 KiB head-major pages of 256-byte rows gain 0.8-2.4
+// points of HBM peak; 4 KiB tiles lose 2.5 and the LDS-staged head-major pages 2-3.5, and
+// scatters gain nothing (no consistent direction), so those keep the plain order.
+#ifndef KVX_XCD_REMAP_MIN
+#define KVX_XCD_REMAP_MIN 8192
+#endif
+__host__ __device__ inline uint32_t xcd_remap_for(int dir, const Launch &a, bool host_staging)
+{
+    if (dir != KV_GATHER || host_staging || a.seg_bytes || a.hm_lds) return 0u;
+    if (a.page_layout == KV_PAGE_TOKEN_MAJOR) return a.tile_bytes >= KVX_XCD_REMAP_MIN ? 1u : 0u;
+    return a.hm_t4 ? 1u : 0u;
 }
 
 // Segment size for a gather over tiles of tile_bytes (0: one tile per wave item).

@@ -771,10 +771,12 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     }
 
     // Work item = one of a tile's 2^split_shift parts; the waves of a workgroup take
-    // consecutive items, so a split tile is copied by neighbouring waves.
+    // consecutive items, so a split tile is copied by neighbouring waves.  Workgroups
+    // take their items in launch_block order (per XCD contiguous when a.xcd_remap).
     const uint32_t shift = a.split_shift;
     const int64_t items = a.total_tiles << shift;
-    for (int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wave; item < items; item += step) {
+    const uint32_t block = launch_block(blockIdx.x, gridDim.x, a.xcd_remap);
+    for (int64_t item = (int64_t)block * kWavesPerBlock + wave; item < items; item += step) {
         const int64_t tile = item >> shift;
         // tiles only grow along the loop, so the span search starts at the last span
         s = find_span(spans, s, a.n_spans, tile);

@@ -75,6 +75,7 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
         grid = (uint32_t)spec->max_workgroups;
+    a.xcd_remap = kvx::xcd_remap_for(direction, a, false);   // staging as if in HBM
     *grid_out = grid;
     const int64_t nreg_s = (int64_t)d->num_layers * d->num_kv;
     if (direction == KV_GATHER && a.page_layout == KV_PAGE_TOKEN_MAJOR && a.seg_bytes) {
@@ -159,9 +160,10 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
     const int64_t nreg = (int64_t)d->num_layers * d->num_kv;
 
     for (uint32_t b = 0; b < grid; ++b) {
+        const uint32_t block = kvx::launch_block(b, grid, a.xcd_remap);
         for (int w = 0; w < kvx::kWavesPerBlock; ++w) {
             uint32_t s = 0;
-            for (int64_t item = (int64_t)b * kvx::kWavesPerBlock + w; item < items; item += step) {
+            for (int64_t item = (int64_t)block * kvx::kWavesPerBlock + w; item < items; item += step) {
                 const int64_t tile = item / split;
                 s = kvx::find_span(records, s, n_rec, tile);
                 const kvx::SpanDev &sp = records[s];
@@ -620,7 +622,8 @@ extern "C" int64_t emu_arena(int64_t size, const int64_t *sizes, int64_t n_calls
 
 // The launch-shape rules of the library's host preparation, for direct checks.
 // The launch decisions for one call: out[0] split shift, out[1] segment bytes, out[2]
-// LDS-staged head-major rows, out[3] whole-page head-major path, out[4] 4 x 4 transpose.
+// LDS-staged head-major rows, out[3] whole-page head-major path, out[4] 4 x 4 transpose,
+// out[5] workgroups remapped per XCD (with the staging in HBM).
 extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
                                const kv_chunk_spec *spec, int64_t *out)
 {
@@ -635,6 +638,8 @@ extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_sp
     out[2] = a.hm_lds;
     out[3] = a.hm_page;
     out[4] = a.hm_t4;
+    a.seg_bytes = (uint32_t)out[1];
+    out[5] = kvx::xcd_remap_for(direction, a, false);
     return KV_OK;
 }
 
@@ -692,4 +697,9 @@ extern "C" int32_t emu_cache_covers(uint64_t q, int64_t bytes, int64_t *lookups)
     const bool ok = g_cache.covers(reinterpret_cast<const void *>(q), bytes, fake_alloc_range);
     *lookups = g_lookups - before;
     return ok ? 1 : 0;
+}
+
+extern "C" uint32_t emu_launch_block(uint32_t b, uint32_t grid, uint32_t remap)
+{
+    return kvx::launch_block(b, grid, remap);
 }

@@ -39,6 +39,8 @@ def _build_emu(tmp_path_factory, defines=()):
                                  ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.emu_arena.restype = ctypes.c_int64
     lib.emu_arena.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
+    lib.emu_launch_block.restype = ctypes.c_uint32
+    lib.emu_launch_block.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
     lib.emu_launch_rule.restype = ctypes.c_int
     lib.emu_launch_rule.argtypes = [ctypes.c_int, ctypes.POINTER(K.kv_pool_desc), ctypes.POINTER(K.kv_span),
                                     ctypes.c_int32, ctypes.POINTER(K.kv_chunk_spec), ctypes.POINTER(ctypes.c_int64)]
@@ -476,31 +478,33 @@ def _rule(lib, direction, H, D, E, bs=16, page_layout=0):
     tab = np.arange(4, dtype=np.int32)
     sp = K.make_spans([(tab.ctypes.data, 4, 0, bs, 0)])
     spec = K.make_chunk_spec(K.KV_LAYER_FIRST, 2, bs, 0, 2, FAKE_BASE + (1 << 30), 2 * 2 * bs * tok, 1)
-    out = (ctypes.c_int64 * 5)()
+    out = (ctypes.c_int64 * 6)()
     assert lib.emu_launch_rule(direction, ctypes.byref(desc), sp, 1, ctypes.byref(spec), out) == 0
-    return dict(shift=out[0], seg=out[1], lds=out[2], page=out[3], t4=out[4])
+    return dict(shift=out[0], seg=out[1], lds=out[2], page=out[3], t4=out[4], xcd=out[5])
 
 
 @pytest.mark.parametrize("H,D,E,gather,scatter", [
     # token-major tiles: 4 KiB one wave; 8-12 KiB gathers and 8-16 KiB scatters in 4 parts
     # of 2 KiB or more; 16-31 KiB gathers in 32 KiB segments; 20-32 KiB scatters whole;
-    # 64 KiB gathers in 2 parts, scatters in 4
-    (1, 128, 2, (0, 0), (0, 0)),
-    (2, 128, 2, (2, 0), (2, 0)),
-    (3, 128, 2, (2, 0), (2, 0)),
-    (4, 128, 2, (None, 32768), (2, 0)),
-    (5, 128, 2, (None, 32768), (0, 0)),
-    (8, 128, 2, (0, 0), (0, 0)),
-    (16, 128, 2, (1, 0), (2, 0)),
-    (9, 128, 2, (None, 32768), (0, 0)),
+    # 64 KiB gathers in 2 parts, scatters in 4.  (split shift, segment bytes, XCD remap):
+    # gathers of 8 KiB tiles or more outside the segment walk remap their workgroups
+    (1, 128, 2, (0, 0, 0), (0, 0, 0)),
+    (2, 128, 2, (2, 0, 1), (2, 0, 0)),
+    (3, 128, 2, (2, 0, 1), (2, 0, 0)),
+    (4, 128, 2, (None, 32768, 0), (2, 0, 0)),
+    (5, 128, 2, (None, 32768, 0), (0, 0, 0)),
+    (8, 128, 2, (0, 0, 1), (0, 0, 0)),
+    (16, 128, 2, (1, 0, 1), (2, 0, 0)),
+    (9, 128, 2, (None, 32768, 0), (0, 0, 0)),
 ])
 def test_token_major_launch_rules(emu, H, D, E, gather, scatter):
-    """The measured split and segment rules, pinned to worked tile sizes."""
-    for d, (shift, seg) in ((K.KV_GATHER, gather), (K.KV_SCATTER, scatter)):
+    """The measured split, segment and workgroup-order rules, pinned to worked tile sizes."""
+    for d, (shift, seg, xcd) in ((K.KV_GATHER, gather), (K.KV_SCATTER, scatter)):
         r = _rule(emu, d, H, D, E)
         assert r["seg"] == seg, (d, r)
         if shift is not None:
             assert r["shift"] == shift, (d, r)
+        assert r["xcd"] == xcd, (d, r)
         assert not (r["lds"] or r["page"] or r["t4"])
 
 
@@ -524,3 +528,19 @@ def test_head_major_path_rules(emu, H, D, E, bs, path):
         r = _rule(emu, d, H, D, E, bs, page_layout=1)
         got = "t4" if r["t4"] else "page" if r["page"] else "lds" if r["lds"] else "cursor"
         assert got == path, (H, D, E, bs, r)
+        # only the 4 x 4 gather remaps its workgroups per XCD
+        assert r["xcd"] == int(d == K.KV_GATHER and path == "t4"), (d, r)
+
+
+@pytest.mark.parametrize("grid", [1, 7, 8, 9, 15, 16, 17, 64, 100, 1000, 4096 + 5, 32768, 65535])
+def test_xcd_launch_order_is_a_permutation(emu, grid):
+    """Remapped workgroup ids cover [0, grid) exactly once; workgroups b and b + 8 (one
+    XCD's consecutive workgroups) take consecutive ids below the last grid % 8; without
+    the remap the order is the identity."""
+    got = [emu.emu_launch_block(b, grid, 1) for b in range(grid)]
+    assert sorted(got) == list(range(grid))
+    g8 = grid - grid % 8
+    for b in range(g8 - 8):
+        assert got[b + 8] == got[b] + 1
+    assert got[g8:] == list(range(g8, grid))
+    assert [emu.emu_launch_block(b, grid, 0) for b in range(grid)] == list(range(grid))
