@@ -467,7 +467,10 @@ def direction_roofline(payload, each_ms):
 def other_workloads(dev, names, reps, before=()):
     """Kernel-time throughput of the other HBM-staged workloads (their parity at full
     size is covered by the test suite); each payload byte is read once and written
-    once."""
+    once.  A head-major workload followed by its "<name>:token_major" twin is timed with
+    the twin on the same pool memory (a second handle over the same regions, token-major
+    pages), the two alternating in two rounds, so the ratio between them is not moved by
+    where the pool landed."""
     import torch
     from paged_layout_transfer_amd import kvxfer as K
     from paged_layout_transfer_amd import workloads as W
@@ -477,7 +480,12 @@ def other_workloads(dev, names, reps, before=()):
     # before the next); a pool's physical placement, which moves the scatter rate,
     # depends on what was allocated before it, so each row names those workloads
     allocated = list(before)
-    for name in names:
+    i = 0
+    while i < len(names):
+        name = names[i]
+        twin = name + ":token_major"
+        paired = i + 1 < len(names) and names[i + 1] == twin
+        i += 2 if paired else 1
         w, pool = resolve(name)
         plan = W.staging_plan(w)
         L, KV = pool["num_layers"], pool["num_kv"]
@@ -489,30 +497,44 @@ def other_workloads(dev, names, reps, before=()):
         spec = K.make_chunk_spec(w["layout"], w["chunk_layers"], w["chunk_tokens"], 0, L, S,
                                  plan["slot_bytes"], plan["n_chunks"])
         info = K.kv_check_transfer(P.desc, spans, spec)
-        row = dict(payload_bytes=info.payload_bytes, requests=len(w["requests"]), tiles=info.tiles,
-                   pool_bytes=P.t.numel(), staging_bytes=S.numel(),
-                   pool_allocated_after=list(allocated))
-        for dn, fn in (("gather", K.kv_gather_chunks), ("scatter", K.kv_scatter_chunks)):
-            fn(P.h, spans, spec, stream)
-            torch.cuda.synchronize()
-            K.kv_pool_timing_start(P.h)
-            for _ in range(reps):
-                fn(P.h, spans, spec, stream)
-            each = K.kv_pool_timing_read_each(P.h)
-            assert K.kv_pool_get_error(P.h, stream) == 0
-            row[dn] = direction_roofline(info.payload_bytes, each)
-        row["roofline"] = dict(bound="hbm", peak=HBM_PEAK_GBS, unit="GB/s",
-                               dominant=max(("gather", "scatter"), key=lambda d: row[d]["kernel_ms"]))
-        row["roofline"]["frac"] = row[row["roofline"]["dominant"]]["hbm_frac"]
-        allocated.append(name)
-        twin = name.split(":")[0]
-        if name.endswith(":token_major") and twin in out:
+        handles = {name: P.h}
+        if paired:
+            bases = [P.t.data_ptr() + r * P.t.stride(0) for r in range(L * KV)]
+            tdesc = K.make_pool_desc(L, KV, pool["num_heads"], pool["head_dim"], pool["elem_bytes"],
+                                     pool["block_size"], pool["num_blocks"], pool["block_stride"], bases, 0)
+            handles[twin] = K.kv_pool_create(tdesc)
+        each = {(n, dn): [] for n in handles for dn in ("gather", "scatter")}
+        rounds = 2 if paired else 1
+        for rnd in range(rounds):
+            for n, h in (handles.items() if rnd % 2 == 0 else reversed(list(handles.items()))):
+                for dn, fn in (("gather", K.kv_gather_chunks), ("scatter", K.kv_scatter_chunks)):
+                    fn(h, spans, spec, stream)
+                    torch.cuda.synchronize()
+                    K.kv_pool_timing_start(h)
+                    for _ in range(reps // rounds):
+                        fn(h, spans, spec, stream)
+                    each[(n, dn)].extend(K.kv_pool_timing_read_each(h).tolist())
+                    assert K.kv_pool_get_error(h, stream) == 0
+        for n in handles:
+            row = dict(payload_bytes=info.payload_bytes, requests=len(w["requests"]), tiles=info.tiles,
+                       pool_bytes=P.t.numel(), staging_bytes=S.numel(),
+                       pool_allocated_after=list(allocated))
+            if n == twin:
+                row["same_pool_as"] = name
+            for dn in ("gather", "scatter"):
+                row[dn] = direction_roofline(info.payload_bytes, each[(n, dn)])
+            row["roofline"] = dict(bound="hbm", peak=HBM_PEAK_GBS, unit="GB/s",
+                                   dominant=max(("gather", "scatter"), key=lambda d: row[d]["kernel_ms"]))
+            row["roofline"]["frac"] = row[row["roofline"]["dominant"]]["hbm_frac"]
+            out[n] = row
+            log("%s: gather %.1f%%, scatter %.1f%% of HBM peak" % (
+                n, 100 * row["gather"]["hbm_frac"], 100 * row["scatter"]["hbm_frac"]))
+        if paired:
             # a head-major pool is judged against the same workload with token-major pages
-            out[twin]["of_token_major_twin"] = {d: round(out[twin][d]["hbm_frac"] / row[d]["hbm_frac"], 4)
+            out[name]["of_token_major_twin"] = {d: round(out[name][d]["hbm_frac"] / out[twin][d]["hbm_frac"], 4)
                                                for d in ("gather", "scatter")}
-        out[name] = row
-        log("%s: gather %.1f%%, scatter %.1f%% of HBM peak" % (
-            name, 100 * row["gather"]["hbm_frac"], 100 * row["scatter"]["hbm_frac"]))
+            K.kv_pool_destroy(handles[twin])
+        allocated.append(name)
         P.close()
         del P, S, tabs
         torch.cuda.empty_cache()
