@@ -524,6 +524,7 @@ int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_sp
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
     else if (host_staging) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
     a.xcd_remap = kvx::xcd_remap_for(direction, a, host_staging);
+    a.scatter_buf = kvx::scatter_buffer_form(direction, a, host_staging);
     const bool timed = p->timing && p->n_timed < kMaxTimed;
     if (timed && !HIP_OK(hipEventRecord(p->t_ev[2 * p->n_timed], stream))) return KV_ERR_HIP;
     if (!hip_ok((hipError_t)kvx::launch_tile_copy(direction, a, grid, stream), "hipLaunchKernel(tile_copy)"))

@@ -135,6 +135,9 @@ namespace kvx {
 #ifndef KVX_GATHER_POOL_POL
 #define KVX_GATHER_POOL_POL KVX_POL_NT                   // gather's loads of pool pages
 #endif
+#ifndef KVX_SCATTER_POOL_POL
+#define KVX_SCATTER_POOL_POL (KVX_POL_NT | KVX_POL_SC1)  // buffer-form scatter's pool stores
+#endif
 #ifndef KVX_GATHER_CHUNK_POL
 #define KVX_GATHER_CHUNK_POL (KVX_POL_NT | KVX_POL_SC1)  // gather's stores into the chunk
 #endif
@@ -218,10 +221,14 @@ struct Launch {
     // head-major pages of 4-byte-word rows moved a whole page at a time (hm_page_ok), with
     // the multiplier dividing by the words of one head's page (block_size * hm_rd)
     uint32_t hm_page;
+    uint32_t hm_pad_;
+    uint64_t hm_m_brd;
     // 1: the workgroups hand each XCD a contiguous eighth of the work items
     // (launch_block, xcd_remap_for)
     uint32_t xcd_remap;
-    uint64_t hm_m_brd;
+    // 1: token-major scatter tiles split between waves go through buffer instructions,
+    // the pool stores with nt + sc1 (scatter_buffer_form; chooses the kernel, host only)
+    uint32_t scatter_buf;
     // the span records themselves when n_spans <= KVX_INLINE_SPANS (spans is then
     // unused): 64-byte SpanDev images, read by the kernel from its argument memory
     uint64_t inl[KVX_INLINE_SPANS * sizeof(SpanDev) / sizeof(uint64_t)];
@@ -240,10 +247,13 @@ static_assert(offsetof(Launch, inl) % alignof(SpanDev) == 0, "inline span record
 #define KVX_MAX_DEVICES 64
 
 // Kernel-internal page layout values: head-major pages staged through LDS in token
-// slabs, in head-group slabs (hm_lds_head_slab), and a whole page at a time (hm_page_ok).
+// slabs, in head-group slabs (hm_lds_head_slab), and a whole page at a time (hm_page_ok);
+// token-major pages whose split scatter tiles go through buffer instructions
+// (scatter_buffer_form).
 #define KVX_PAGE_HM_LDS 2
 #define KVX_PAGE_HM_LDS_HEADS 3
 #define KVX_PAGE_HM_LDS_PAGE 4
+#define KVX_PAGE_TM_SCATTER_BUF 5
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
 // vector q of that head's row -- and its offset (in vectors) inside a head-major
@@ -554,6 +564,20 @@ __host__ __device__ inline uint32_t xcd_remap_for(int dir, const Launch &a, bool
     if (dir != KV_GATHER || host_staging || a.seg_bytes || a.hm_lds) return 0u;
     if (a.page_layout == KV_PAGE_TOKEN_MAJOR) return a.tile_bytes >= KVX_XCD_REMAP_MIN ? 1u : 0u;
     return a.hm_t4 ? 1u : 0u;
+}
+
+// Whether a scatter's token-major tiles go through buffer instructions, the pool stores
+// with nt + sc1 (KVX_SCATTER_POOL_POL), instead of global instructions with plain nt:
+// tiles split between waves (split_shift > 0: 8-16 KiB and 64 KiB or larger) with the
+// staging in HBM.  Measured on MI355X, interleaved rounds in two processes each: the
+// int8_kv scatter (64 KiB tiles, 4 parts) gains 4.0-5.4 points of HBM peak, mixed (64 KiB)
+// 0.7-1.0, the TP-2 shard (16 KiB) 0.4-0.6, the TP-4 shard (8 KiB) -0.4 to +0.1; whole 32
+// KiB tiles lose 0.6-0.9, so they keep the global form.
+__host__ __device__ inline uint32_t scatter_buffer_form(int dir, const Launch &a, bool host_staging)
+{
+    return (dir == KV_SCATTER && a.page_layout == KV_PAGE_TOKEN_MAJOR && a.split_shift > 0 && !host_staging)
+               ? 1u
+               : 0u;
 }
 
 // Segment size for a gather over tiles of tile_bytes (0: one tile per wave item).

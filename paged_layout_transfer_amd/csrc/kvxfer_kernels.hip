@@ -281,6 +281,17 @@ __device__ __forceinline__ void scatter_tile(const gvec *__restrict__ chunk, gve
                                   KVX_SCATTER_PIPELINE);
 }
 
+// The same copy through buffer instructions, so the pool stores can carry sc1 as well
+// as nt (KVX_SCATTER_POOL_POL); taken for tiles split between waves (scatter_buffer_form).
+template <bool NT>
+__device__ __forceinline__ void scatter_tile_buf(const uint8_t *chunk, const uint8_t *pool, uint32_t nvec,
+                                                 uint32_t lane)
+{
+    copy_loop<KVX_SCATTER_UNROLL>(BufSide<NT ? KVX_POL_NT : 0>(chunk, nvec * 16u),
+                                  BufSide<NT ? KVX_SCATTER_POOL_POL : 0>(pool, nvec * 16u), nvec, lane,
+                                  KVX_SCATTER_PIPELINE);
+}
+
 // The permuted (pool) side of a head-major tile touches each cache line of the block
 // from several wave instructions (one per token whose head row shares the line), so
 // whether those accesses bypass the caches is a separate choice.
@@ -831,6 +842,7 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
             uint8_t *pool = block + first * 16ll;
             uint8_t *chunk = chunk_tile + first * 16ll;
             if (DIR == KV_GATHER) gather_tile<NT>(pool, chunk, count, lane);
+            else if (PAGE == KVX_PAGE_TM_SCATTER_BUF) scatter_tile_buf<NT>(chunk, pool, count, lane);
             else scatter_tile<NT>(as_global(chunk), as_global(pool), count, lane);
         }
     }
@@ -868,6 +880,8 @@ static const void *pick_page(const Launch &a)
         return a.hm_lds ? pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS>(a)
                         : pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a);
     }
+    if constexpr (DIR == KV_SCATTER)
+        if (a.scatter_buf) return pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_BUF>(a);
     return pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
 }
 

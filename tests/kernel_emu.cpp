@@ -623,7 +623,8 @@ extern "C" int64_t emu_arena(int64_t size, const int64_t *sizes, int64_t n_calls
 // The launch-shape rules of the library's host preparation, for direct checks.
 // The launch decisions for one call: out[0] split shift, out[1] segment bytes, out[2]
 // LDS-staged head-major rows, out[3] whole-page head-major path, out[4] 4 x 4 transpose,
-// out[5] workgroups remapped per XCD (with the staging in HBM).
+// out[5] workgroups remapped per XCD, out[6] scatter through buffer instructions (both
+// with the staging in HBM).
 extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
                                const kv_chunk_spec *spec, int64_t *out)
 {
@@ -640,6 +641,8 @@ extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_sp
     out[4] = a.hm_t4;
     a.seg_bytes = (uint32_t)out[1];
     out[5] = kvx::xcd_remap_for(direction, a, false);
+    a.split_shift = (uint32_t)out[0];
+    out[6] = kvx::scatter_buffer_form(direction, a, false);
     return KV_OK;
 }
 
