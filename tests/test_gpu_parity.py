@@ -347,15 +347,19 @@ def test_head_major_lds_cases(seed):
                  dma=seed % 4 == 0, flags=flags)
 
 
+@pytest.mark.parametrize("cached", [False, True])
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("name", sorted(cases.RULE_SHAPES))
-def test_launch_rule_boundaries(name, layout):
+def test_launch_rule_boundaries(name, layout, cached):
     """Each launch path at the tile sizes around its rule, both chunk layouts, with 1-2
-    spans that start 0-2 pages in and end in a partial page; whole buffers compared."""
+    spans that start 0-2 pages in and end in a partial page, with the default
+    nontemporal accesses and with KV_FLAG_CACHED (each kernel form has both); whole
+    buffers compared."""
     pool, spans, chunks = cases.rule_case(name, layout)
     regions, staging = _random(pool, chunks, 98_500 + layout)
+    flags = K.KV_FLAG_CACHED if cached else 0
     for d in DIRS:
-        _compare(d, pool, spans, chunks, regions, staging, "rule-%s-%d" % (name, layout))
+        _compare(d, pool, spans, chunks, regions, staging, "rule-%s-%d-%d" % (name, layout, cached), flags=flags)
 
 
 EXTREMES = {
