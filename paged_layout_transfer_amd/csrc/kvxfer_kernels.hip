@@ -18,7 +18,11 @@
 //      cache-streaming stores so a transfer does not evict the working set of
 //      concurrent compute kernels: "Non-Intrusive Resource Sizing").  Gather goes
 //      through buffer instructions so that its sequential chunk stores can also
-//      carry the sc1 bit; scatter through global instructions.
+//      carry the sc1 bit; scatter through global instructions, except tiles split
+//      between waves, whose pool stores carry nt + sc1 through buffer instructions
+//      (scatter_buffer_form).
+// Gathers of tiles walked whole or in parts hand each XCD a contiguous stretch of the
+// work items (launch_block, xcd_remap_for).
 // No matrix instructions, and LDS only for head-major pages whose head rows are not
 // whole 16-byte vectors (copy_head_major_lds): it is a pure byte copy, bound by HBM
 // (both sides in HBM) or by the host link (chunks in pinned host memory).
