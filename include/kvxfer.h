@@ -272,11 +272,17 @@ KV_API int kv_validate_targets(const kv_pool_desc *desc, const kv_span *spans, i
  * `stream`, preceded by one small stream-ordered descriptor upload.  spans is a
  * host array of n_spans (1 .. KV_MAX_SPANS) entries; each block_table is a
  * device pointer.  n_spans == 0, or spans that are all empty, is a no-op.  Loads
- * and stores are nontemporal.  Returns after enqueueing.  Not for graph capture:
- * while `stream` is capturing, the call is refused with KV_ERR_CAPTURE (its
- * span-record arena is recycled under events the host waits on, and its first call
- * on a pool allocates); capture kv_transfer_chunks_noalloc instead.  The same holds
- * for kv_scatter_chunks. */
+ * and stores are nontemporal.  Returns after enqueueing.
+ * Under HIP graph capture (the same holds for kv_scatter_chunks): a call is captured as
+ * its one kernel, every replay repeating the call, when its span records ride in the
+ * kernel arguments (at most 16 non-empty spans), the pool has made a call outside the
+ * capture before (the first call allocates the pool's device state), KV_FLAG_VALIDATE
+ * is not set (its table check copies to the host) and the pool's timing is off.  Any
+ * other call is refused with KV_ERR_CAPTURE and enqueues nothing (more records go
+ * through the pool's arena, which is recycled under events the host waits on).  A
+ * replay reads the pool's region table and writes its error word (kv_pool_get_error),
+ * so the pool must outlive the graph, and kv_pool_destroy must not be called while a
+ * replay may still run (it waits only for calls made outside a graph). */
 KV_API int kv_gather_chunks(kv_pool *pool, const kv_span *spans, int32_t n_spans,
                      const kv_chunk_spec *spec, hipStream_t stream);
 

@@ -536,6 +536,14 @@ int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_sp
     return KV_OK;
 }
 
+// The span records a validated call makes: one per non-empty span.
+int32_t records_of(const kv_span *spans, int32_t n_spans)
+{
+    int32_t n = 0;
+    for (int32_t i = 0; i < n_spans; ++i) n += spans[i].t_end > spans[i].t_begin;
+    return n;
+}
+
 // KV_ERR_CAPTURE if `stream` is capturing a graph (or its capture was invalidated),
 // KV_OK if not, KV_ERR_HIP if the runtime cannot tell.
 int refuse_capture(hipStream_t stream)
@@ -554,15 +562,35 @@ int transfer(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_chunk_s
     int rc = validate_call(&p->desc, spans, n_spans, spec, &info, p->plans.data(), p->ranges.data());
     if (rc) return rc;
     if (info.tiles == 0) return KV_OK;
-    // The arena is recycled under events the host waits on, and the first call on a
-    // pool allocates: neither may be captured into a graph.
-    rc = refuse_capture(stream);
-    if (rc) return rc;
+    // Under graph capture only a call the graph can replay as it stands is taken: its
+    // span records ride in the kernel arguments, the pool's device state exists already
+    // (the first call allocates it), and there is no host-side table check and no timing
+    // event.  Such a call takes no arena stretch (the arena is recycled under events the
+    // host waits on).
+    hipStreamCaptureStatus cst = hipStreamCaptureStatusNone;
+    if (!hip_ok(hipStreamIsCapturing(stream, &cst), "hipStreamIsCapturing")) return KV_ERR_HIP;
+    const bool capturing = cst != hipStreamCaptureStatusNone;
+    if (capturing && (cst != hipStreamCaptureStatusActive || records_of(spans, n_spans) > KVX_INLINE_SPANS ||
+                      p->device < 0 || (spec->flags & KV_FLAG_VALIDATE) || p->timing))
+        return KV_ERR_CAPTURE;
     kvx::AllocRange staging;
     rc = check_buffers(p, spans, n_spans, spec, true, &staging);
     if (rc) return rc;
     rc = device_setup(p);
     if (rc) return rc;
+    if (capturing) {
+        kvx::SpanDev recs[KVX_INLINE_SPANS];
+        kvx::Launch a;
+        uint32_t n_rec = 0;
+        rc = prepare_with(&p->desc, spans, n_spans, spec, recs, &n_rec, &a, &info, p->plans.data(),
+                          p->ranges.data());
+        if (rc) return rc;
+        std::memcpy(a.inl, recs, n_rec * sizeof(kvx::SpanDev));
+        a.regions = p->d_regions;
+        a.spans = nullptr;
+        a.err = p->d_err;
+        return launch_prepared(p, a, direction, spec, staging, stream);
+    }
     if (spec->flags & KV_FLAG_VALIDATE) {
         rc = validate_tables(p, spans, n_spans, direction, stream);
         if (rc) return rc;
@@ -620,9 +648,7 @@ int transfer_noalloc(kv_pool *p, int direction, const kv_span *spans, int32_t n_
     if (info.tiles == 0) return KV_OK;
     // Records beyond those the kernel arguments carry are copied from the pool's host
     // image, which a captured copy would read only when the graph runs.
-    int32_t n_nonempty = 0;
-    for (int32_t i = 0; i < n_spans; ++i) n_nonempty += spans[i].t_end > spans[i].t_begin;
-    if (n_nonempty > KVX_INLINE_SPANS) {
+    if (records_of(spans, n_spans) > KVX_INLINE_SPANS) {
         rc = refuse_capture(stream);
         if (rc) return rc;
     }

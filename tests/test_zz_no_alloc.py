@@ -11,8 +11,8 @@ one left behind.  A block id out of range must set the caller's error word.
 Under graph capture: a noalloc call whose span records ride in the kernel arguments
 is captured and replayed (each replay after another pool's call has rewritten the
 device scratch, each checked against the allocating entry point); a noalloc call with
-more records, and the allocating entry points, are refused while the stream captures;
-several calls captured into one graph replay in order.
+more records, and the allocating entry points with that many records, are refused while
+the stream captures; several calls captured into one graph replay in order.
 """
 from __future__ import annotations
 
@@ -205,10 +205,10 @@ def test_noalloc_call_replays_from_a_captured_graph(direction, mode):
 
 
 def test_capture_refuses_calls_that_cannot_replay():
-    """While a stream captures: the allocating entry points, and a noalloc call with more
-    span records than the kernel arguments carry, return KV_ERR_CAPTURE and enqueue
-    nothing; the capture itself stays valid, and the same calls made eagerly afterwards
-    match the oracle."""
+    """While a stream captures: calls with more span records than the kernel arguments
+    carry, through the allocating entry points and the noalloc one, return
+    KV_ERR_CAPTURE and enqueue nothing; the capture itself stays valid, and the same
+    calls made eagerly afterwards match the oracle."""
     dev = _dev()
     c = Call(*_case(87_000, 40, True), seed=51, dev=dev)
     x = torch.zeros(16, device=dev)
