@@ -224,7 +224,9 @@ KV_API int kv_pool_create(const kv_pool_desc *desc, kv_pool **out);
 
 /* Frees the handle and its device state, after waiting for the transfers it
  * queued that are still in flight (their fence events; other device work is not
- * waited for).  The caller's regions are untouched.  NULL is accepted.
+ * waited for, nor are replays of calls captured into graphs: those must have finished,
+ * and such graphs must not run again).  The caller's regions are untouched.  NULL is
+ * accepted.
  * No passage: library infrastructure (the handle's lifetime). */
 KV_API int kv_pool_destroy(kv_pool *pool);
 
