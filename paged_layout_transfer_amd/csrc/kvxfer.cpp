@@ -519,8 +519,10 @@ int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_sp
 {
     a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
-    uint32_t grid = kvx::default_grid(kvx::work_items(a));
     const bool host_staging = staging_in_host_memory(p, spec->base, staging);
+    a.part_bytes = kvx::scatter_part_bytes(direction, a, host_staging);
+    if (a.part_bytes) a.split_shift = 0;
+    uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
     else if (host_staging) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);
     a.xcd_remap = kvx::xcd_remap_for(direction, a, host_staging);

@@ -135,6 +135,9 @@ namespace kvx {
 #ifndef KVX_GATHER_POOL_POL
 #define KVX_GATHER_POOL_POL KVX_POL_NT                   // gather's loads of pool pages
 #endif
+#ifndef KVX_FIXED_PART_POW2
+#define KVX_FIXED_PART_POW2 0  // 1: power-of-two scatter tiles of 128 KiB or more take fixed parts too
+#endif
 #ifndef KVX_SCATTER_POOL_POL
 #define KVX_SCATTER_POOL_POL (KVX_POL_NT | KVX_POL_SC1)  // buffer-form scatter's pool stores
 #endif
@@ -221,7 +224,9 @@ struct Launch {
     // head-major pages of 4-byte-word rows moved a whole page at a time (hm_page_ok), with
     // the multiplier dividing by the words of one head's page (block_size * hm_rd)
     uint32_t hm_page;
-    uint32_t hm_pad_;
+    // > 0: each tile is copied as parts of this many bytes (the last one shorter) by as
+    // many waves, instead of 2^split_shift equal parts (scatter_part_bytes)
+    uint32_t part_bytes;
     uint64_t hm_m_brd;
     // 1: the workgroups hand each XCD a contiguous eighth of the work items
     // (launch_block, xcd_remap_for)
@@ -249,11 +254,13 @@ static_assert(offsetof(Launch, inl) % alignof(SpanDev) == 0, "inline span record
 // Kernel-internal page layout values: head-major pages staged through LDS in token
 // slabs, in head-group slabs (hm_lds_head_slab), and a whole page at a time (hm_page_ok);
 // token-major pages whose split scatter tiles go through buffer instructions
-// (scatter_buffer_form).
+// (scatter_buffer_form), and whose scatter tiles go in fixed-size parts
+// (scatter_part_bytes).
 #define KVX_PAGE_HM_LDS 2
 #define KVX_PAGE_HM_LDS_HEADS 3
 #define KVX_PAGE_HM_LDS_PAGE 4
 #define KVX_PAGE_TM_SCATTER_BUF 5
+#define KVX_PAGE_TM_SCATTER_FIXED 6
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
 // vector q of that head's row -- and its offset (in vectors) inside a head-major
@@ -580,6 +587,28 @@ __host__ __device__ inline uint32_t scatter_buffer_form(int dir, const Launch &a
                : 0u;
 }
 
+// Fixed-size parts for a scatter's token-major tiles (0: the split_shift rule): tiles
+// of more than 32 KiB that are whole multiples of KVX_SCATTER_FIXED_PART but not powers
+// of two, with the staging in HBM, go in parts of KVX_SCATTER_FIXED_PART bytes, each
+// starting on a 16 KiB boundary of the tile, copied by neighbouring waves in the global
+// form.  Measured on MI355X in interleaved rounds, shuffled table, ~2 GiB per launch:
+// 48, 80 and 96 KiB tiles scatter at 69.3 / 69.5 / 71.2 % of HBM peak this way against
+// 65.0 / 64.0 / 64.8 % whole or in 4 equal parts; tiles that are not multiples of 16 KiB
+// (20-40 KiB, the 36 KiB MLA latent) gain nothing from such parts.
+#ifndef KVX_SCATTER_FIXED_PART
+#define KVX_SCATTER_FIXED_PART 16384
+#endif
+__host__ __device__ inline uint32_t scatter_part_bytes(int dir, const Launch &a, bool host_staging)
+{
+    const int64_t T = a.tile_bytes;
+    if (dir != KV_SCATTER || a.page_layout != KV_PAGE_TOKEN_MAJOR || host_staging || KVX_SCATTER_FIXED_PART <= 0)
+        return 0u;
+    const bool pow2 = (T & (T - 1)) == 0;
+    if (T > 32768 && T % KVX_SCATTER_FIXED_PART == 0 && (!pow2 || (KVX_FIXED_PART_POW2 && T >= 131072)))
+        return (uint32_t)KVX_SCATTER_FIXED_PART;
+    return 0u;
+}
+
 // Segment size for a gather over tiles of tile_bytes (0: one tile per wave item).
 __host__ __device__ constexpr uint32_t gather_seg_bytes(int dir, uint32_t page_layout, int64_t tile_bytes)
 {
@@ -605,12 +634,18 @@ __host__ __device__ inline int gather_seg_unroll(int64_t tile_bytes, int64_t seg
     return g % 8192 == 0 ? 8 : g % 4096 == 0 ? 4 : 2;
 }
 
+// Parts of each tile in the tile walk: part_bytes-sized parts, or 2^split_shift.
+__host__ __device__ inline int64_t parts_per_tile(const Launch &a)
+{
+    return a.part_bytes ? (a.tile_bytes + a.part_bytes - 1) / a.part_bytes : (int64_t)1 << a.split_shift;
+}
+
 // Work items of a call: segments of the tiles laid end to end at a tile_bytes pitch,
 // or tiles times their parts.
 __host__ __device__ inline int64_t work_items(const Launch &a)
 {
     return a.seg_bytes ? (a.total_tiles * a.tile_bytes + a.seg_bytes - 1) / a.seg_bytes
-                       : a.total_tiles << a.split_shift;
+                       : a.total_tiles * parts_per_tile(a);
 }
 
 // The piece [lo, hi) of tile `tile` (bytes from the tile's start) that segment
@@ -633,6 +668,21 @@ __host__ __device__ inline void part_range(uint32_t nvec, uint32_t part, uint32_
     const uint32_t hi = (uint32_t)((uint64_t)nvec * (part + 1) / split);
     *first = lo;
     *count = hi - lo;
+}
+
+// The vectors [first, first + count) of a token-major tile of nvec vectors that work
+// item part `part` copies: a part_bytes-sized part (empty past a partial tile's end),
+// or one of the 2^split_shift near-equal parts.
+__host__ __device__ inline void tile_part(const Launch &a, uint32_t nvec, uint32_t part, uint32_t *first,
+                                          uint32_t *count)
+{
+    if (a.part_bytes) {
+        const uint32_t pv = a.part_bytes >> 4, lo = part * pv;
+        *first = lo < nvec ? lo : nvec;
+        *count = (lo + pv < nvec ? lo + pv : nvec) - *first;
+        return;
+    }
+    part_range(nvec, part, 1u << a.split_shift, first, count);
 }
 
 // Host: validate a call and fill the launch descriptor (all fields but regions,

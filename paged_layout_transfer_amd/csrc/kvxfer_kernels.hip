@@ -785,14 +785,20 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         return;
     }
 
-    // Work item = one of a tile's 2^split_shift parts; the waves of a workgroup take
-    // consecutive items, so a split tile is copied by neighbouring waves.  Workgroups
+    // Work item = one of a tile's parts (2^split_shift, or part_bytes-sized); the waves
+    // of a workgroup take consecutive items, so a split tile is copied by neighbouring
+    // waves.  Workgroups
     // take their items in launch_block order (per XCD contiguous when a.xcd_remap).
+    // (the fixed-size parts of a.part_bytes only in their own instantiation, so the
+    // other walks keep the shift arithmetic alone)
+    constexpr bool FIXED = PAGE == KVX_PAGE_TM_SCATTER_FIXED;
     const uint32_t shift = a.split_shift;
-    const int64_t items = a.total_tiles << shift;
+    const int64_t ppt = FIXED ? parts_per_tile(a) : (int64_t)1 << shift;
+    const int64_t items = a.total_tiles * ppt;
     const uint32_t block = launch_block(blockIdx.x, gridDim.x, a.xcd_remap);
     for (int64_t item = (int64_t)block * kWavesPerBlock + wave; item < items; item += step) {
-        const int64_t tile = item >> shift;
+        const int64_t tile = FIXED ? item / ppt : item >> shift;
+        const uint32_t part = FIXED ? (uint32_t)(item - tile * ppt) : (uint32_t)(item & ((1 << shift) - 1));
         // tiles only grow along the loop, so the span search starts at the last span
         s = find_span(spans, s, a.n_spans, tile);
         const SpanDev sp = load_span(spans + s);
@@ -816,7 +822,6 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
             // parts of a split tile are ranges of slabs
             __shared__ __attribute__((aligned(16))) uint32_t slices[kWavesPerBlock][KVX_HM_LDS_SLICE / 4];
             const uint32_t n_tok = t.nbytes / a.tok;
-            const uint32_t part = (uint32_t)(item & ((1 << shift) - 1));
             if (PAGE == KVX_PAGE_HM_LDS_HEADS) {  // head-group slabs
                 part_range(hm_lds_slabs(n_tok, a.hm_heads, a.hm_hg[DIR], a.hm_htj[DIR]), part, 1u << shift,
                            &first, &count);
@@ -833,12 +838,12 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         if (PAGE == KV_PAGE_HEAD_MAJOR && a.hm_t4) {
             // parts of a split tile are ranges of 4x4 blocks
             const uint32_t n_tok = t.nbytes / a.tok;
-            part_range(hm_t4_units(n_tok, a.hm_heads), (uint32_t)(item & ((1 << shift) - 1)), 1u << shift,
-                       &first, &count);
+            part_range(hm_t4_units(n_tok, a.hm_heads), part, 1u << shift, &first, &count);
             copy_head_major_t4<DIR, NT>(block, chunk_tile, first, first + count, n_tok, lane, a);
             continue;
         }
-        part_range(t.nbytes >> 4, (uint32_t)(item & ((1 << shift) - 1)), 1u << shift, &first, &count);
+        if (FIXED) tile_part(a, t.nbytes >> 4, part, &first, &count);
+        else part_range(t.nbytes >> 4, part, 1u << shift, &first, &count);
         if (PAGE == KV_PAGE_HEAD_MAJOR) {
             copy_head_major<DIR, KVX_HM_UNROLL, NT>(as_global(block), chunk_tile, first, first + count,
                                                     lane, a);
@@ -884,8 +889,10 @@ static const void *pick_page(const Launch &a)
         return a.hm_lds ? pick_policy<DIR, LAYOUT, KVX_PAGE_HM_LDS>(a)
                         : pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a);
     }
-    if constexpr (DIR == KV_SCATTER)
+    if constexpr (DIR == KV_SCATTER) {
         if (a.scatter_buf) return pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_BUF>(a);
+        if (a.part_bytes) return pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_FIXED>(a);
+    }
     return pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
 }
 

@@ -167,8 +167,9 @@ def head_major_case(rng: np.random.Generator, H: int, D: int, E: int, bs: int):
 # Shapes on each side of the launch rules, (H, D, E, block_size) -> what the launch does:
 # token-major tiles of 4-6 KiB take one wave; 8-14 KiB tiles, and 16-18 KiB scatters, go
 # in 4 parts; 16-48 KiB gathers that are not whole 32 KiB tiles walk 32 KiB segments (of
-# 2, 4 or 8-vector groups by the pieces they cut); 20-48 KiB scatters and 32 KiB tiles go
-# whole; 64 KiB and larger tiles go in parts (72 KiB gathers in segments).  Head-major:
+# 2, 4 or 8-vector groups by the pieces they cut); 20-40 KiB scatters and 32 KiB tiles go
+# whole; 64 KiB and larger tiles go in parts (72 KiB gathers in segments); scatters of
+# 48, 80, 96 and 144 KiB in 16 KiB parts.  Head-major:
 # pages of at most 8 KiB with rows other than the 4 x 4 case through the LDS slabs, the
 # 4 x 4 register transpose, and the cursor walk for larger pages of other rows.
 RULE_SHAPES = {
@@ -177,7 +178,8 @@ RULE_SHAPES = {
     "tm_16k": (0, 8, 64, 2, 16), "tm_18k": (0, 9, 64, 2, 16), "tm_20k": (0, 5, 128, 2, 16),
     "tm_24k": (0, 3, 128, 2, 32), "tm_28k": (0, 7, 128, 2, 16), "tm_32k": (0, 8, 128, 2, 16),
     "tm_36k": (0, 1, 576, 1, 64), "tm_40k": (0, 5, 128, 2, 32), "tm_48k": (0, 3, 128, 2, 64),
-    "tm_64k": (0, 8, 128, 2, 32), "tm_72k": (0, 9, 128, 2, 32),
+    "tm_64k": (0, 8, 128, 2, 32), "tm_72k": (0, 9, 128, 2, 32), "tm_80k": (0, 5, 128, 2, 64),
+    "tm_96k": (0, 3, 128, 2, 128), "tm_144k": (0, 9, 128, 2, 64),
     "hm_8k_2x256": (1, 2, 128, 2, 16), "hm_8k_1x512": (1, 1, 256, 2, 16), "hm_4k_2x128": (1, 2, 64, 2, 16),
     "hm_4k_8x32": (1, 8, 32, 1, 16), "hm_8k_t4": (1, 4, 128, 2, 8), "hm_16k_t4": (1, 4, 128, 2, 16),
     "hm_12k_3x256": (1, 3, 128, 2, 16), "hm_16k_1x256": (1, 1, 128, 2, 64), "hm_24k_3x512": (1, 3, 256, 2, 16),

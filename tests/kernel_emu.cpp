@@ -72,6 +72,8 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
 
     a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
+    a.part_bytes = kvx::scatter_part_bytes(direction, a, false);   // staging as if in HBM
+    if (a.part_bytes) a.split_shift = 0;
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
         grid = (uint32_t)spec->max_workgroups;
@@ -142,7 +144,7 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
         if (k != pieces.size()) ++*violations;
         return KV_OK;
     }
-    const uint32_t split = 1u << a.split_shift;
+    const uint32_t split = (uint32_t)kvx::parts_per_tile(a);
     const int64_t items = info.tiles * split;
     std::vector<uint8_t> seen((size_t)items, 0);
     // head-major 4x4-block walk: every vector of every tile written once
@@ -475,7 +477,8 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
                     }
                     continue;
                 }
-                kvx::part_range(t.nbytes >> 4, (uint32_t)(item % split), split, &first, &count);
+                kvx::tile_part(a, t.nbytes >> 4, (uint32_t)(item % split), &first, &count);
+                if (first + count > (t.nbytes >> 4)) { ++*violations; continue; }
                 if (a.page_layout == KV_PAGE_HEAD_MAJOR) {
                     // each lane's cursor, as the kernel advances it, 64 vectors at a time
                     uint8_t *block = static_cast<uint8_t *>(d->bases[t.region]) + poff;
@@ -623,8 +626,8 @@ extern "C" int64_t emu_arena(int64_t size, const int64_t *sizes, int64_t n_calls
 // The launch-shape rules of the library's host preparation, for direct checks.
 // The launch decisions for one call: out[0] split shift, out[1] segment bytes, out[2]
 // LDS-staged head-major rows, out[3] whole-page head-major path, out[4] 4 x 4 transpose,
-// out[5] workgroups remapped per XCD, out[6] scatter through buffer instructions (both
-// with the staging in HBM).
+// out[5] workgroups remapped per XCD, out[6] scatter through buffer instructions,
+// out[7] fixed part bytes of a scatter's tiles (all with the staging in HBM).
 extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_span *spans, int32_t n_spans,
                                const kv_chunk_spec *spec, int64_t *out)
 {
@@ -641,7 +644,10 @@ extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_sp
     out[4] = a.hm_t4;
     a.seg_bytes = (uint32_t)out[1];
     out[5] = kvx::xcd_remap_for(direction, a, false);
-    a.split_shift = (uint32_t)out[0];
+    out[7] = kvx::scatter_part_bytes(direction, a, false);
+    a.split_shift = out[7] ? 0u : (uint32_t)out[0];
+    a.part_bytes = (uint32_t)out[7];
+    out[0] = a.split_shift;
     out[6] = kvx::scatter_buffer_form(direction, a, false);
     return KV_OK;
 }

@@ -478,34 +478,43 @@ def _rule(lib, direction, H, D, E, bs=16, page_layout=0):
     tab = np.arange(4, dtype=np.int32)
     sp = K.make_spans([(tab.ctypes.data, 4, 0, bs, 0)])
     spec = K.make_chunk_spec(K.KV_LAYER_FIRST, 2, bs, 0, 2, FAKE_BASE + (1 << 30), 2 * 2 * bs * tok, 1)
-    out = (ctypes.c_int64 * 7)()
+    out = (ctypes.c_int64 * 8)()
     assert lib.emu_launch_rule(direction, ctypes.byref(desc), sp, 1, ctypes.byref(spec), out) == 0
-    return dict(shift=out[0], seg=out[1], lds=out[2], page=out[3], t4=out[4], xcd=out[5], sbuf=out[6])
+    return dict(shift=out[0], seg=out[1], lds=out[2], page=out[3], t4=out[4], xcd=out[5], sbuf=out[6],
+                part=out[7])
 
 
 @pytest.mark.parametrize("H,D,E,gather,scatter", [
     # token-major tiles: 4 KiB one wave; 8-12 KiB gathers and 8-16 KiB scatters in 4 parts
     # of 2 KiB or more; 16-31 KiB gathers in 32 KiB segments; 20-32 KiB scatters whole;
-    # 64 KiB gathers in 2 parts, scatters in 4.  (split shift, segment bytes, XCD remap):
-    # gathers of 8 KiB tiles or more outside the segment walk remap their workgroups, and
-    # split scatters go through buffer instructions
-    (1, 128, 2, (0, 0, 0), (0, 0, 0)),
-    (2, 128, 2, (2, 0, 1), (2, 0, 0)),
-    (3, 128, 2, (2, 0, 1), (2, 0, 0)),
-    (4, 128, 2, (None, 32768, 0), (2, 0, 0)),
-    (5, 128, 2, (None, 32768, 0), (0, 0, 0)),
-    (8, 128, 2, (0, 0, 1), (0, 0, 0)),
-    (16, 128, 2, (1, 0, 1), (2, 0, 0)),
-    (9, 128, 2, (None, 32768, 0), (0, 0, 0)),
+    # 64 KiB gathers in 2 parts, scatters in 4; scatters of 48, 80 and 96 KiB (multiples of
+    # 16 KiB that are not powers of two) in 16 KiB parts.  (split shift, segment bytes, XCD
+    # remap, fixed part bytes): gathers of 8 KiB tiles or more outside the segment walk
+    # remap their workgroups, and scatters split in 2^k parts go through buffer
+    # instructions
+    (1, 128, 2, (0, 0, 0, 0), (0, 0, 0, 0)),
+    (2, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
+    (3, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
+    (4, 128, 2, (None, 32768, 0, 0), (2, 0, 0, 0)),
+    (5, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 0)),
+    (8, 128, 2, (0, 0, 1, 0), (0, 0, 0, 0)),
+    (16, 128, 2, (1, 0, 1, 0), (2, 0, 0, 0)),
+    (9, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 0)),
+    (12, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
+    (20, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
+    (24, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
+    (32, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
 ])
 def test_token_major_launch_rules(emu, H, D, E, gather, scatter):
-    """The measured split, segment and workgroup-order rules, pinned to worked tile sizes."""
-    for d, (shift, seg, xcd) in ((K.KV_GATHER, gather), (K.KV_SCATTER, scatter)):
+    """The measured split, segment, part and workgroup-order rules, pinned to worked
+    tile sizes."""
+    for d, (shift, seg, xcd, part) in ((K.KV_GATHER, gather), (K.KV_SCATTER, scatter)):
         r = _rule(emu, d, H, D, E)
         assert r["seg"] == seg, (d, r)
         if shift is not None:
             assert r["shift"] == shift, (d, r)
         assert r["xcd"] == xcd, (d, r)
+        assert r["part"] == part, (d, r)
         assert r["sbuf"] == int(d == K.KV_SCATTER and r["shift"] > 0), (d, r)
         assert not (r["lds"] or r["page"] or r["t4"])
 
@@ -533,7 +542,7 @@ def test_head_major_path_rules(emu, H, D, E, bs, path):
         # only the 4 x 4 gather remaps its workgroups per XCD; head-major scatters keep
         # their own copy loops
         assert r["xcd"] == int(d == K.KV_GATHER and path == "t4"), (d, r)
-        assert r["sbuf"] == 0, (d, r)
+        assert r["sbuf"] == 0 and r["part"] == 0, (d, r)
 
 
 @pytest.mark.parametrize("grid", [1, 7, 8, 9, 15, 16, 17, 64, 100, 1000, 4096 + 5, 32768, 65535])
