@@ -135,8 +135,11 @@ namespace kvx {
 #ifndef KVX_GATHER_POOL_POL
 #define KVX_GATHER_POOL_POL KVX_POL_NT                   // gather's loads of pool pages
 #endif
-#ifndef KVX_FIXED_PART_POW2
-#define KVX_FIXED_PART_POW2 0  // 1: power-of-two scatter tiles of 128 KiB or more take fixed parts too
+#ifndef KVX_SCATTER_SMALL_PART
+#define KVX_SCATTER_SMALL_PART 4096    // scatter parts of 16-64 KiB tiles (scatter_part_bytes)
+#endif
+#ifndef KVX_SCATTER_FIXED_PART
+#define KVX_SCATTER_FIXED_PART 16384   // scatter parts of larger 16 KiB-multiple tiles
 #endif
 #ifndef KVX_SCATTER_POOL_POL
 #define KVX_SCATTER_POOL_POL (KVX_POL_NT | KVX_POL_SC1)  // buffer-form scatter's pool stores
@@ -254,13 +257,14 @@ static_assert(offsetof(Launch, inl) % alignof(SpanDev) == 0, "inline span record
 // Kernel-internal page layout values: head-major pages staged through LDS in token
 // slabs, in head-group slabs (hm_lds_head_slab), and a whole page at a time (hm_page_ok);
 // token-major pages whose split scatter tiles go through buffer instructions
-// (scatter_buffer_form), and whose scatter tiles go in fixed-size parts
-// (scatter_part_bytes).
+// (scatter_buffer_form), whose scatter tiles go in fixed-size parts (scatter_part_bytes),
+// and both.
 #define KVX_PAGE_HM_LDS 2
 #define KVX_PAGE_HM_LDS_HEADS 3
 #define KVX_PAGE_HM_LDS_PAGE 4
 #define KVX_PAGE_TM_SCATTER_BUF 5
 #define KVX_PAGE_TM_SCATTER_FIXED 6
+#define KVX_PAGE_TM_SCATTER_FIXED_BUF 7
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
 // vector q of that head's row -- and its offset (in vectors) inside a head-major
@@ -575,37 +579,39 @@ __host__ __device__ inline uint32_t xcd_remap_for(int dir, const Launch &a, bool
 
 // Whether a scatter's token-major tiles go through buffer instructions, the pool stores
 // with nt + sc1 (KVX_SCATTER_POOL_POL), instead of global instructions with plain nt:
-// tiles split between waves (split_shift > 0: 8-16 KiB and 64 KiB or larger) with the
-// staging in HBM.  Measured on MI355X, interleaved rounds in two processes each: the
-// int8_kv scatter (64 KiB tiles, 4 parts) gains 4.0-5.4 points of HBM peak, mixed (64 KiB)
-// 0.7-1.0, the TP-2 shard (16 KiB) 0.4-0.6, the TP-4 shard (8 KiB) -0.4 to +0.1; whole 32
-// KiB tiles lose 0.6-0.9, so they keep the global form.
+// tiles split between waves in 2^k parts (8 to under 20 KiB, and from 64 KiB) or in
+// 4 KiB parts (scatter_part_bytes), with the staging in HBM.  Measured on MI355X,
+// interleaved rounds in two processes each: the int8_kv scatter (64 KiB tiles, 4 parts)
+// gains 4.0-5.4 points of HBM peak, mixed (64 KiB) 0.7-1.0, the TP-2 shard (16 KiB)
+// 0.4-0.6, the TP-4 shard (8 KiB) -0.4 to +0.1, and 32 KiB tiles in 4 KiB parts 0.5-0.8
+// more than in the global form; whole 32 KiB tiles lose 0.6-0.9, and 16 KiB parts of
+// larger tiles do better in the global form.
 __host__ __device__ inline uint32_t scatter_buffer_form(int dir, const Launch &a, bool host_staging)
 {
-    return (dir == KV_SCATTER && a.page_layout == KV_PAGE_TOKEN_MAJOR && a.split_shift > 0 && !host_staging)
-               ? 1u
-               : 0u;
+    const bool split = a.split_shift > 0 || (a.part_bytes > 0 && a.part_bytes < KVX_SCATTER_FIXED_PART);
+    return (dir == KV_SCATTER && a.page_layout == KV_PAGE_TOKEN_MAJOR && split && !host_staging) ? 1u : 0u;
 }
 
-// Fixed-size parts for a scatter's token-major tiles (0: the split_shift rule): tiles
-// of more than 32 KiB that are whole multiples of KVX_SCATTER_FIXED_PART but not powers
-// of two, with the staging in HBM, go in parts of KVX_SCATTER_FIXED_PART bytes, each
-// starting on a 16 KiB boundary of the tile, copied by neighbouring waves in the global
-// form.  Measured on MI355X in interleaved rounds, shuffled table, ~2 GiB per launch:
-// 48, 80 and 96 KiB tiles scatter at 69.3 / 69.5 / 71.2 % of HBM peak this way against
-// 65.0 / 64.0 / 64.8 % whole or in 4 equal parts; tiles that are not multiples of 16 KiB
-// (20-40 KiB, the 36 KiB MLA latent) gain nothing from such parts.
-#ifndef KVX_SCATTER_FIXED_PART
-#define KVX_SCATTER_FIXED_PART 16384
-#endif
+// Fixed-size parts for a scatter's token-major tiles into HBM staging (0: the
+// split_shift rule), each part starting at a multiple of its size within the tile and
+// copied by its own wave, neighbouring waves taking one tile's parts:
+//  * tiles of 20 KiB (where the small-tile split ends, KVX_SMALL_SCATTER_MAX) to less
+//    than 64 KiB: 4 KiB parts (KVX_SCATTER_SMALL_PART), in the buffer form
+//    (scatter_buffer_form).  Measured on MI355X in interleaved rounds, shuffled tables:
+//    20-60 KiB tiles +0.6 to +3.7 points of HBM peak against whole tiles, the llama8b
+//    call's 32 KiB tiles +1.9 to +3.9 (in a 32 GiB pool; +0.9 in a 16 GiB one, none in an
+//    8 GiB one), the MLA latent's 36 KiB tiles +1.4 to +3.1; 32 KiB tiles in 8 KiB parts
+//    lose 2, in 2 KiB parts 0.6, 18 KiB tiles 1.1 against their 4 equal parts, and 64 KiB
+//    or larger tiles in 4 KiB parts lose 1-8.
+//  * larger tiles that are whole multiples of 16 KiB but not powers of two: 16 KiB parts
+//    (KVX_SCATTER_FIXED_PART) in the global form: 80, 96 and 144 KiB tiles +2.3 to +6.5
+//    points against 4 equal parts.
 __host__ __device__ inline uint32_t scatter_part_bytes(int dir, const Launch &a, bool host_staging)
 {
     const int64_t T = a.tile_bytes;
-    if (dir != KV_SCATTER || a.page_layout != KV_PAGE_TOKEN_MAJOR || host_staging || KVX_SCATTER_FIXED_PART <= 0)
-        return 0u;
-    const bool pow2 = (T & (T - 1)) == 0;
-    if (T > 32768 && T % KVX_SCATTER_FIXED_PART == 0 && (!pow2 || (KVX_FIXED_PART_POW2 && T >= 131072)))
-        return (uint32_t)KVX_SCATTER_FIXED_PART;
+    if (dir != KV_SCATTER || a.page_layout != KV_PAGE_TOKEN_MAJOR || host_staging) return 0u;
+    if (T >= KVX_SMALL_SCATTER_MAX && T < 65536) return (uint32_t)KVX_SCATTER_SMALL_PART;
+    if (T >= 65536 && T % KVX_SCATTER_FIXED_PART == 0 && (T & (T - 1)) != 0) return (uint32_t)KVX_SCATTER_FIXED_PART;
     return 0u;
 }
 

@@ -1,7 +1,8 @@
 // kvxfer_kernels.hip -- the gather/scatter tile-copy kernel for gfx950.
 //
-// One 64-lane wavefront copies one (layer, kv, page) tile -- or one part of a large
-// or 8-16 KiB tile, or, for a gather over token-major tiles of 16 KiB or more that are
+// One 64-lane wavefront copies one (layer, kv, page) tile -- or one part of a tile
+// split between waves (8-20 KiB tiles, scatter tiles of 20 KiB or more, gather tiles of
+// 64 KiB or more), or, for a gather over token-major tiles of 16 KiB or more that are
 // not whole 32 KiB segments, one 32 KiB segment of the tiles laid end to end -- per
 // iteration of a grid-stride loop.  Per
 // tile it
@@ -791,7 +792,7 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     // take their items in launch_block order (per XCD contiguous when a.xcd_remap).
     // (the fixed-size parts of a.part_bytes only in their own instantiation, so the
     // other walks keep the shift arithmetic alone)
-    constexpr bool FIXED = PAGE == KVX_PAGE_TM_SCATTER_FIXED;
+    constexpr bool FIXED = PAGE == KVX_PAGE_TM_SCATTER_FIXED || PAGE == KVX_PAGE_TM_SCATTER_FIXED_BUF;
     const uint32_t shift = a.split_shift;
     const int64_t ppt = FIXED ? parts_per_tile(a) : (int64_t)1 << shift;
     const int64_t items = a.total_tiles * ppt;
@@ -851,7 +852,8 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
             uint8_t *pool = block + first * 16ll;
             uint8_t *chunk = chunk_tile + first * 16ll;
             if (DIR == KV_GATHER) gather_tile<NT>(pool, chunk, count, lane);
-            else if (PAGE == KVX_PAGE_TM_SCATTER_BUF) scatter_tile_buf<NT>(chunk, pool, count, lane);
+            else if (PAGE == KVX_PAGE_TM_SCATTER_BUF || PAGE == KVX_PAGE_TM_SCATTER_FIXED_BUF)
+                scatter_tile_buf<NT>(chunk, pool, count, lane);
             else scatter_tile<NT>(as_global(chunk), as_global(pool), count, lane);
         }
     }
@@ -890,8 +892,10 @@ static const void *pick_page(const Launch &a)
                         : pick_policy<DIR, LAYOUT, KV_PAGE_HEAD_MAJOR>(a);
     }
     if constexpr (DIR == KV_SCATTER) {
+        if (a.part_bytes)
+            return a.scatter_buf ? pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_FIXED_BUF>(a)
+                                 : pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_FIXED>(a);
         if (a.scatter_buf) return pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_BUF>(a);
-        if (a.part_bytes) return pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_FIXED>(a);
     }
     return pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
 }

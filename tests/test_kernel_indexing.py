@@ -487,20 +487,21 @@ def _rule(lib, direction, H, D, E, bs=16, page_layout=0):
 @pytest.mark.parametrize("H,D,E,gather,scatter", [
     # token-major tiles: 4 KiB one wave; 8-12 KiB gathers and 8-16 KiB scatters in 4 parts
     # of 2 KiB or more; 16-31 KiB gathers in 32 KiB segments; 20-32 KiB scatters whole;
-    # 64 KiB gathers in 2 parts, scatters in 4; scatters of 48, 80 and 96 KiB (multiples of
-    # 16 KiB that are not powers of two) in 16 KiB parts.  (split shift, segment bytes, XCD
-    # remap, fixed part bytes): gathers of 8 KiB tiles or more outside the segment walk
-    # remap their workgroups, and scatters split in 2^k parts go through buffer
+    # 64 KiB gathers in 2 parts; scatters of more than 16 and less than 64 KiB in 4 KiB
+    # parts, 64 and 128 KiB scatters in 4, and 80 and 96 KiB scatters (multiples of 16 KiB
+    # that are not powers of two) in 16 KiB parts.  (split shift, segment bytes, XCD remap,
+    # fixed part bytes): gathers of 8 KiB tiles or more outside the segment walk remap
+    # their workgroups; scatters split in 2^k parts or in 4 KiB parts go through buffer
     # instructions
     (1, 128, 2, (0, 0, 0, 0), (0, 0, 0, 0)),
     (2, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
     (3, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
     (4, 128, 2, (None, 32768, 0, 0), (2, 0, 0, 0)),
-    (5, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 0)),
-    (8, 128, 2, (0, 0, 1, 0), (0, 0, 0, 0)),
+    (5, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 4096)),
+    (8, 128, 2, (0, 0, 1, 0), (0, 0, 0, 4096)),
     (16, 128, 2, (1, 0, 1, 0), (2, 0, 0, 0)),
-    (9, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 0)),
-    (12, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
+    (9, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 4096)),
+    (12, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 4096)),
     (20, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
     (24, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
     (32, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
@@ -515,7 +516,8 @@ def test_token_major_launch_rules(emu, H, D, E, gather, scatter):
             assert r["shift"] == shift, (d, r)
         assert r["xcd"] == xcd, (d, r)
         assert r["part"] == part, (d, r)
-        assert r["sbuf"] == int(d == K.KV_SCATTER and r["shift"] > 0), (d, r)
+        buffer_form = d == K.KV_SCATTER and (r["shift"] > 0 or r["part"] == 4096)
+        assert r["sbuf"] == int(buffer_form), (d, r)
         assert not (r["lds"] or r["page"] or r["t4"])
 
 
