@@ -291,11 +291,17 @@ def hbm_leg(args, dev):
                   for i in range(len(lens))]
         spans_a = K.make_spans([(tb, tb.numel(), t0, t1, fc) for tb, (t0, t1), fc in
                                 zip(tabs_a, w["requests"], plan["first_chunk"])])
-        for name, fn in (("gather", K.kv_gather_chunks), ("scatter", K.kv_scatter_chunks)):
-            fn(P.h, spans_a, spec, stream)
+        # the scatter again with the caller's hint that the pages lie in runs of adjacent
+        # blocks (KV_FLAG_PAGE_RUNS: tiles whole instead of in 4 KiB parts)
+        spec_runs = K.make_chunk_spec(chunks["layout"], chunks["chunk_layers"], chunks["chunk_tokens"], 0, L,
+                                      S, plan["slot_bytes"], plan["n_chunks"], args.max_workgroups,
+                                      K.KV_FLAG_PAGE_RUNS)
+        for name, fn, sp in (("gather", K.kv_gather_chunks, spec), ("scatter", K.kv_scatter_chunks, spec),
+                             ("scatter_page_runs_hint", K.kv_scatter_chunks, spec_runs)):
+            fn(P.h, spans_a, sp, stream)
             K.kv_pool_timing_start(P.h)
             for _ in range(max(10, args.steps)):
-                fn(P.h, spans_a, spec, stream)
+                fn(P.h, spans_a, sp, stream)
             each = K.kv_pool_timing_read_each(P.h)
             alloc_order[name] = dict(kernel_ms_median=round(float(np.median(each)), 4),
                                      hbm_frac=round(2 * payload / (float(np.median(each)) * 1e-3) / 1e9
@@ -303,8 +309,9 @@ def hbm_leg(args, dev):
         assert K.kv_pool_get_error(P.h, stream) == 0
         K.kv_pool_free_blocks(P.h, ids)
         del tabs_a
-        log("allocator-ordered blocks: gather %.1f%%, scatter %.1f%% of HBM peak" % (
-            100 * alloc_order["gather"]["hbm_frac"], 100 * alloc_order["scatter"]["hbm_frac"]))
+        log("allocator-ordered blocks: gather %.1f%%, scatter %.1f%% (%.1f%% with the page-runs hint) of HBM peak"
+            % (100 * alloc_order["gather"]["hbm_frac"], 100 * alloc_order["scatter"]["hbm_frac"],
+               100 * alloc_order["scatter_page_runs_hint"]["hbm_frac"]))
 
     small = small_calls(P, tabs[0], w, pool, spec, chunks, S, stream) if args.small_calls else None
 

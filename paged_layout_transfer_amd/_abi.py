@@ -30,6 +30,7 @@ KV_SCATTER = 1
 KV_FLAG_VALIDATE = 0x1
 KV_FLAG_DMA_STRIDED = 0x2
 KV_FLAG_CACHED = 0x4
+KV_FLAG_PAGE_RUNS = 0x8
 KV_DEVERR_BLOCK_RANGE = 0x1
 KV_RING_COHERENT = 0x0
 KV_RING_NONCOHERENT = 0x1

@@ -112,7 +112,7 @@ int check_spec(const kv_pool_desc *d, const kv_chunk_spec *s)
     if (s->slot_bytes % 16 != 0) return KV_ERR_ALIGN;
     if (s->n_slots > INT64_MAX / s->slot_bytes) return KV_ERR_ARG;
     if (s->max_workgroups < 0) return KV_ERR_ARG;
-    if (s->flags & ~(KV_FLAG_VALIDATE | KV_FLAG_DMA_STRIDED | KV_FLAG_CACHED)) return KV_ERR_ARG;
+    if (s->flags & ~(KV_FLAG_VALIDATE | KV_FLAG_DMA_STRIDED | KV_FLAG_CACHED | KV_FLAG_PAGE_RUNS)) return KV_ERR_ARG;
     return KV_OK;
 }
 
@@ -520,7 +520,7 @@ int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_sp
     a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     const bool host_staging = staging_in_host_memory(p, spec->base, staging);
-    a.part_bytes = kvx::scatter_part_bytes(direction, a, host_staging);
+    a.part_bytes = kvx::scatter_part_bytes(direction, a, host_staging, (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
     if (a.part_bytes) a.split_shift = 0;
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);

@@ -602,15 +602,18 @@ __host__ __device__ inline uint32_t scatter_buffer_form(int dir, const Launch &a
 //    call's 32 KiB tiles +1.9 to +3.9 (in a 32 GiB pool; +0.9 in a 16 GiB one, none in an
 //    8 GiB one), the MLA latent's 36 KiB tiles +1.4 to +3.1; 32 KiB tiles in 8 KiB parts
 //    lose 2, in 2 KiB parts 0.6, 18 KiB tiles 1.1 against their 4 equal parts, and 64 KiB
-//    or larger tiles in 4 KiB parts lose 1-8.
+//    or larger tiles in 4 KiB parts lose 1-8.  Pages in runs of adjacent blocks scatter
+//    faster whole (74-77 % against 71-72 % for 32 KiB tiles), which the kernel cannot see
+//    from the launch: page_runs (KV_FLAG_PAGE_RUNS, the caller's hint) keeps such tiles
+//    whole.
 //  * larger tiles that are whole multiples of 16 KiB but not powers of two: 16 KiB parts
 //    (KVX_SCATTER_FIXED_PART) in the global form: 80, 96 and 144 KiB tiles +2.3 to +6.5
 //    points against 4 equal parts.
-__host__ __device__ inline uint32_t scatter_part_bytes(int dir, const Launch &a, bool host_staging)
+__host__ __device__ inline uint32_t scatter_part_bytes(int dir, const Launch &a, bool host_staging, bool page_runs)
 {
     const int64_t T = a.tile_bytes;
     if (dir != KV_SCATTER || a.page_layout != KV_PAGE_TOKEN_MAJOR || host_staging) return 0u;
-    if (T >= KVX_SMALL_SCATTER_MAX && T < 65536) return (uint32_t)KVX_SCATTER_SMALL_PART;
+    if (T >= KVX_SMALL_SCATTER_MAX && T < 65536) return page_runs ? 0u : (uint32_t)KVX_SCATTER_SMALL_PART;
     if (T >= 65536 && T % KVX_SCATTER_FIXED_PART == 0 && (T & (T - 1)) != 0) return (uint32_t)KVX_SCATTER_FIXED_PART;
     return 0u;
 }

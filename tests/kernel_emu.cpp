@@ -72,7 +72,8 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
 
     a.split_shift = kvx::launch_split_shift(a, direction);
     a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
-    a.part_bytes = kvx::scatter_part_bytes(direction, a, false);   // staging as if in HBM
+    a.part_bytes = kvx::scatter_part_bytes(direction, a, false,      // staging as if in HBM
+                                           (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
     if (a.part_bytes) a.split_shift = 0;
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
@@ -644,7 +645,7 @@ extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_sp
     out[4] = a.hm_t4;
     a.seg_bytes = (uint32_t)out[1];
     out[5] = kvx::xcd_remap_for(direction, a, false);
-    out[7] = kvx::scatter_part_bytes(direction, a, false);
+    out[7] = kvx::scatter_part_bytes(direction, a, false, (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
     a.split_shift = out[7] ? 0u : (uint32_t)out[0];
     a.part_bytes = (uint32_t)out[7];
     out[0] = a.split_shift;

@@ -150,6 +150,7 @@ CALL_CASES = [
     (dict(n_slots=0), [_span()], K.KV_ERR_ARG),
     (dict(max_workgroups=-1), [_span()], K.KV_ERR_ARG),
     (dict(flags=0x100), [_span()], K.KV_ERR_ARG),
+    (dict(flags=0x10), [_span()], K.KV_ERR_ARG),     # the first bit past KV_FLAG_PAGE_RUNS
     # ring ownership: two spans, one chunk each, same slot
     (dict(n_slots=4), [_span(fc=1), _span(fc=5)], K.KV_ERR_RING),
     (dict(n_slots=1), [_span(fc=0), _span(fc=1)], K.KV_ERR_RING),   # more chunks than slots

@@ -347,19 +347,19 @@ def test_head_major_lds_cases(seed):
                  dma=seed % 4 == 0, flags=flags)
 
 
-@pytest.mark.parametrize("cached", [False, True])
+@pytest.mark.parametrize("flags", [0, K.KV_FLAG_CACHED, K.KV_FLAG_PAGE_RUNS])
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("name", sorted(cases.RULE_SHAPES))
-def test_launch_rule_boundaries(name, layout, cached):
+def test_launch_rule_boundaries(name, layout, flags):
     """Each launch path at the tile sizes around its rule, both chunk layouts, with 1-2
     spans that start 0-2 pages in and end in a partial page, with the default
-    nontemporal accesses and with KV_FLAG_CACHED (each kernel form has both); whole
-    buffers compared."""
+    nontemporal accesses, with KV_FLAG_CACHED (each kernel form has both) and with the
+    KV_FLAG_PAGE_RUNS hint (whole tiles where 4 KiB parts are the default); whole buffers
+    compared."""
     pool, spans, chunks = cases.rule_case(name, layout)
     regions, staging = _random(pool, chunks, 98_500 + layout)
-    flags = K.KV_FLAG_CACHED if cached else 0
     for d in DIRS:
-        _compare(d, pool, spans, chunks, regions, staging, "rule-%s-%d-%d" % (name, layout, cached), flags=flags)
+        _compare(d, pool, spans, chunks, regions, staging, "rule-%s-%d-%d" % (name, layout, flags), flags=flags)
 
 
 EXTREMES = {

@@ -470,14 +470,14 @@ def test_extent_check_reuses_a_walk_over_pieces_while_its_ends_stand(emu):
 FAKE_BASE = 1 << 40   # addresses are only formed, never dereferenced, by the launch rules
 
 
-def _rule(lib, direction, H, D, E, bs=16, page_layout=0):
+def _rule(lib, direction, H, D, E, bs=16, page_layout=0, flags=0):
     """The launch decisions for a one-page call of a pool with H x D x E-byte rows."""
     tok = H * D * E
     desc = K.make_pool_desc(2, 2, H, D, E, bs, 4, bs * tok, [FAKE_BASE + i * (1 << 24) for i in range(4)],
                             page_layout)
     tab = np.arange(4, dtype=np.int32)
     sp = K.make_spans([(tab.ctypes.data, 4, 0, bs, 0)])
-    spec = K.make_chunk_spec(K.KV_LAYER_FIRST, 2, bs, 0, 2, FAKE_BASE + (1 << 30), 2 * 2 * bs * tok, 1)
+    spec = K.make_chunk_spec(K.KV_LAYER_FIRST, 2, bs, 0, 2, FAKE_BASE + (1 << 30), 2 * 2 * bs * tok, 1, 0, flags)
     out = (ctypes.c_int64 * 8)()
     assert lib.emu_launch_rule(direction, ctypes.byref(desc), sp, 1, ctypes.byref(spec), out) == 0
     return dict(shift=out[0], seg=out[1], lds=out[2], page=out[3], t4=out[4], xcd=out[5], sbuf=out[6],
@@ -519,6 +519,22 @@ def test_token_major_launch_rules(emu, H, D, E, gather, scatter):
         buffer_form = d == K.KV_SCATTER and (r["shift"] > 0 or r["part"] == 4096)
         assert r["sbuf"] == int(buffer_form), (d, r)
         assert not (r["lds"] or r["page"] or r["t4"])
+
+
+@pytest.mark.parametrize("H,D,E,part", [(5, 128, 2, 4096), (8, 128, 2, 4096), (9, 128, 2, 4096), (12, 128, 2, 4096),
+                                         (20, 128, 2, 16384), (16, 128, 2, 0), (4, 128, 2, 0)])
+def test_page_runs_hint_keeps_20_to_64_kib_scatter_tiles_whole(emu, H, D, E, part):
+    """KV_FLAG_PAGE_RUNS takes the 4 KiB parts away from 20-64 KiB scatter tiles (copied
+    whole, in the global form) and changes nothing else."""
+    plain = _rule(emu, K.KV_SCATTER, H, D, E)
+    runs = _rule(emu, K.KV_SCATTER, H, D, E, flags=K.KV_FLAG_PAGE_RUNS)
+    assert plain["part"] == part
+    if part == 4096:
+        assert runs["part"] == 0 and runs["shift"] == 0 and runs["sbuf"] == 0
+    else:
+        assert runs == plain
+    for d in (K.KV_GATHER,):
+        assert _rule(emu, d, H, D, E, flags=K.KV_FLAG_PAGE_RUNS) == _rule(emu, d, H, D, E)
 
 
 @pytest.mark.parametrize("H,D,E,bs,path", [
