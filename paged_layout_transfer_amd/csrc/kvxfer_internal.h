@@ -560,19 +560,31 @@ __host__ __device__ constexpr uint32_t launch_block(uint32_t b, uint32_t G, uint
     return (remap == 0u || b >= (G & ~7u)) ? b : (b & 7u) * ((G & ~7u) >> 3) + (b >> 3);
 }
 
-// Whether a launch remaps its workgroups (launch_block): gathers into HBM staging of
-// tiles walked whole or in parts (not the segment walk), token-major tiles of at least
-// KVX_XCD_REMAP_MIN bytes or head-major pages through the 4 x 4 register transpose.
-// Measured on MI355X, in interleaved rounds in two processes each: gathers of 8, 32 and
-// 64 KiB token-major tiles and of 32 KiB head-major pages of 256-byte rows gain 0.8-2.4
-// points of HBM peak; 4 KiB tiles lose 2.5 and the LDS-staged head-major pages 2-3.5, and
-// scatters gain nothing (no consistent direction), so those keep the plain order.
+// Whether a launch remaps its workgroups (launch_block), with the staging in HBM:
+//  * gathers of tiles walked whole or in parts (not the segment walk), token-major tiles
+//    of at least KVX_XCD_REMAP_MIN bytes or head-major pages through the 4 x 4 register
+//    transpose.  Measured on MI355X, in interleaved rounds in two processes each: gathers
+//    of 8, 32 and 64 KiB token-major tiles and of 32 KiB head-major pages of 256-byte rows
+//    gain 0.8-2.4 points of HBM peak; 4 KiB tiles lose 2.5 and the LDS-staged head-major
+//    pages 2-3.5, so those keep the plain order;
+//  * scatters in 4 KiB parts: 20-56 KiB tiles +2.2 to +6.1 points, the MLA latent's 36 KiB
+//    +2.8 to +3.0, page-first 32 KiB +3.6, but 32 KiB tiles with layer-first chunks -0.6
+//    to -1.5, which keep the plain order (as do whole and 2^k-part scatter tiles, which
+//    show no consistent direction).
 #ifndef KVX_XCD_REMAP_MIN
 #define KVX_XCD_REMAP_MIN 8192
 #endif
 __host__ __device__ inline uint32_t xcd_remap_for(int dir, const Launch &a, bool host_staging)
 {
-    if (dir != KV_GATHER || host_staging || a.seg_bytes || a.hm_lds) return 0u;
+    if (dir == KV_SCATTER) {
+        // scatters in 4 KiB parts (scatter_part_bytes), except power-of-two tiles (32 KiB:
+        // whole workgroups per tile) with layer-first chunks
+        const bool pow2 = (a.tile_bytes & (a.tile_bytes - 1)) == 0;
+        return (!host_staging && a.part_bytes == KVX_SCATTER_SMALL_PART && !(pow2 && a.layout == KV_LAYER_FIRST))
+                   ? 1u
+                   : 0u;
+    }
+    if (host_staging || a.seg_bytes || a.hm_lds) return 0u;
     if (a.page_layout == KV_PAGE_TOKEN_MAJOR) return a.tile_bytes >= KVX_XCD_REMAP_MIN ? 1u : 0u;
     return a.hm_t4 ? 1u : 0u;
 }

@@ -644,11 +644,11 @@ extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_sp
     out[3] = a.hm_page;
     out[4] = a.hm_t4;
     a.seg_bytes = (uint32_t)out[1];
-    out[5] = kvx::xcd_remap_for(direction, a, false);
     out[7] = kvx::scatter_part_bytes(direction, a, false, (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
     a.split_shift = out[7] ? 0u : (uint32_t)out[0];
     a.part_bytes = (uint32_t)out[7];
     out[0] = a.split_shift;
+    out[5] = kvx::xcd_remap_for(direction, a, false);
     out[6] = kvx::scatter_buffer_form(direction, a, false);
     return KV_OK;
 }

@@ -470,14 +470,14 @@ def test_extent_check_reuses_a_walk_over_pieces_while_its_ends_stand(emu):
 FAKE_BASE = 1 << 40   # addresses are only formed, never dereferenced, by the launch rules
 
 
-def _rule(lib, direction, H, D, E, bs=16, page_layout=0, flags=0):
+def _rule(lib, direction, H, D, E, bs=16, page_layout=0, flags=0, layout=K.KV_LAYER_FIRST):
     """The launch decisions for a one-page call of a pool with H x D x E-byte rows."""
     tok = H * D * E
     desc = K.make_pool_desc(2, 2, H, D, E, bs, 4, bs * tok, [FAKE_BASE + i * (1 << 24) for i in range(4)],
                             page_layout)
     tab = np.arange(4, dtype=np.int32)
     sp = K.make_spans([(tab.ctypes.data, 4, 0, bs, 0)])
-    spec = K.make_chunk_spec(K.KV_LAYER_FIRST, 2, bs, 0, 2, FAKE_BASE + (1 << 30), 2 * 2 * bs * tok, 1, 0, flags)
+    spec = K.make_chunk_spec(layout, 2, bs, 0, 2, FAKE_BASE + (1 << 30), 2 * 2 * bs * tok, 1, 0, flags)
     out = (ctypes.c_int64 * 8)()
     assert lib.emu_launch_rule(direction, ctypes.byref(desc), sp, 1, ctypes.byref(spec), out) == 0
     return dict(shift=out[0], seg=out[1], lds=out[2], page=out[3], t4=out[4], xcd=out[5], sbuf=out[6],
@@ -485,23 +485,23 @@ def _rule(lib, direction, H, D, E, bs=16, page_layout=0, flags=0):
 
 
 @pytest.mark.parametrize("H,D,E,gather,scatter", [
-    # token-major tiles: 4 KiB one wave; 8-12 KiB gathers and 8-16 KiB scatters in 4 parts
-    # of 2 KiB or more; 16-31 KiB gathers in 32 KiB segments; 20-32 KiB scatters whole;
-    # 64 KiB gathers in 2 parts; scatters of more than 16 and less than 64 KiB in 4 KiB
-    # parts, 64 and 128 KiB scatters in 4, and 80 and 96 KiB scatters (multiples of 16 KiB
-    # that are not powers of two) in 16 KiB parts.  (split shift, segment bytes, XCD remap,
-    # fixed part bytes): gathers of 8 KiB tiles or more outside the segment walk remap
-    # their workgroups; scatters split in 2^k parts or in 4 KiB parts go through buffer
-    # instructions
+    # token-major tiles: 4 KiB one wave; 8-12 KiB gathers and 8-18 KiB scatters in 4 parts
+    # of 2 KiB or more; 16-31 KiB gathers in 32 KiB segments; 64 KiB gathers in 2 parts;
+    # scatters of 20 to under 64 KiB in 4 KiB parts, 64 and 128 KiB scatters in 4, and 80
+    # and 96 KiB scatters (multiples of 16 KiB that are not powers of two) in 16 KiB parts.
+    # (split shift, segment bytes, XCD remap, fixed part bytes): gathers of 8 KiB tiles or
+    # more outside the segment walk remap their workgroups, and so do scatters in 4 KiB
+    # parts other than 32 KiB tiles with layer-first chunks (these calls are layer-first);
+    # scatters split in 2^k parts or in 4 KiB parts go through buffer instructions
     (1, 128, 2, (0, 0, 0, 0), (0, 0, 0, 0)),
     (2, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
     (3, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
     (4, 128, 2, (None, 32768, 0, 0), (2, 0, 0, 0)),
-    (5, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 4096)),
+    (5, 128, 2, (None, 32768, 0, 0), (0, 0, 1, 4096)),
     (8, 128, 2, (0, 0, 1, 0), (0, 0, 0, 4096)),
     (16, 128, 2, (1, 0, 1, 0), (2, 0, 0, 0)),
-    (9, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 4096)),
-    (12, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 4096)),
+    (9, 128, 2, (None, 32768, 0, 0), (0, 0, 1, 4096)),
+    (12, 128, 2, (None, 32768, 0, 0), (0, 0, 1, 4096)),
     (20, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
     (24, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
     (32, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
@@ -519,6 +519,15 @@ def test_token_major_launch_rules(emu, H, D, E, gather, scatter):
         buffer_form = d == K.KV_SCATTER and (r["shift"] > 0 or r["part"] == 4096)
         assert r["sbuf"] == int(buffer_form), (d, r)
         assert not (r["lds"] or r["page"] or r["t4"])
+
+
+@pytest.mark.parametrize("H,D,E,lf,pf", [(5, 128, 2, 1, 1), (8, 128, 2, 0, 1), (9, 128, 2, 1, 1), (16, 128, 2, 0, 0),
+                                         (2, 128, 2, 0, 0), (20, 128, 2, 0, 0)])
+def test_scatter_workgroup_order_by_chunk_layout(emu, H, D, E, lf, pf):
+    """Scatters in 4 KiB parts remap their workgroups per XCD, except 32 KiB tiles with
+    layer-first chunks; other scatters keep the plain order in either layout."""
+    assert _rule(emu, K.KV_SCATTER, H, D, E)["xcd"] == lf
+    assert _rule(emu, K.KV_SCATTER, H, D, E, layout=K.KV_PAGE_FIRST)["xcd"] == pf
 
 
 @pytest.mark.parametrize("H,D,E,part", [(5, 128, 2, 4096), (8, 128, 2, 4096), (9, 128, 2, 4096), (12, 128, 2, 4096),
