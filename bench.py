@@ -1289,11 +1289,11 @@ def main():
                        for d in per_dir},
         "target_frac": 0.70,
         "below_target": sorted(d for d in per_dir if per_dir[d]["hbm_frac"] < 0.70),
-        "note": "scatter writes each 32 KiB page as an isolated block; its rate depends on where the "
-                "pool sits in memory: this 32 GiB pool is one allocation whose regions share one 64 GiB "
-                "window of it, the slow case (pool_placement.window_split times the same call with "
-                "the regions split across two windows; allocator_ordered_blocks into the blocks the "
-                "library's allocator hands a fresh pool)",
+        "note": "scatter writes each 32 KiB page (in 4 KiB parts) as an isolated block; its rate depends "
+                "on where the pool sits in memory: this 32 GiB pool is one allocation whose regions share "
+                "one 64 GiB window of it, the slow case (pool_placement.window_split times the same call "
+                "with the regions split across two windows; allocator_ordered_blocks into the blocks the "
+                "library's allocator hands a fresh pool, with and without the KV_FLAG_PAGE_RUNS hint)",
     }
     out = {
         "metric": METRIC,
