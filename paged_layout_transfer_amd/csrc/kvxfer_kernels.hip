@@ -786,12 +786,11 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
         return;
     }
 
-    // Work item = one of a tile's parts (2^split_shift, or part_bytes-sized); the waves
-    // of a workgroup take consecutive items, so a split tile is copied by neighbouring
-    // waves.  Workgroups
-    // take their items in launch_block order (per XCD contiguous when a.xcd_remap).
-    // (the fixed-size parts of a.part_bytes only in their own instantiation, so the
-    // other walks keep the shift arithmetic alone)
+    // Work item = one of a tile's parts: 2^split_shift near-equal ones, or, in the
+    // fixed-part instantiations only (so the other walks keep the shift arithmetic
+    // alone), part_bytes-sized ones.  The waves of a workgroup take consecutive items, so
+    // a split tile is copied by neighbouring waves; workgroups take their items in
+    // launch_block order (contiguous per XCD when a.xcd_remap).
     constexpr bool FIXED = PAGE == KVX_PAGE_TM_SCATTER_FIXED || PAGE == KVX_PAGE_TM_SCATTER_FIXED_BUF;
     const uint32_t shift = a.split_shift;
     const int64_t ppt = FIXED ? parts_per_tile(a) : (int64_t)1 << shift;
