@@ -362,6 +362,18 @@ def test_launch_rule_boundaries(name, layout, flags):
         _compare(d, pool, spans, chunks, regions, staging, "rule-%s-%d-%d" % (name, layout, flags), flags=flags)
 
 
+@pytest.mark.parametrize("wg", [1, 7, 9])
+@pytest.mark.parametrize("name", ["tm_24k", "tm_32k", "tm_36k", "tm_48k", "tm_64k", "tm_80k", "hm_16k_t4"])
+def test_launch_rule_shapes_on_capped_grids(name, wg):
+    """The fixed-part, buffer-form and per-XCD-ordered walks on grids of 1, 7 and 9
+    workgroups (each wave loops over many items; 7 and 9 leave workgroups outside the
+    per-XCD permutation's whole eighths), page-first chunks; whole buffers compared."""
+    pool, spans, chunks = cases.rule_case(name, 1)
+    regions, staging = _random(pool, chunks, 98_700 + wg)
+    for d in DIRS:
+        _compare(d, pool, spans, chunks, regions, staging, "rule-capped-%s-%d" % (name, wg), max_workgroups=wg)
+
+
 EXTREMES = {
     # 1-token pages of 16-byte tokens: every tile is one vector
     "one_token_pages": dict(L=3, KV=2, H=1, D=16, E=1, bs=1, N=900, spans=[(0, 500), (0, 77)], CT=64, CL=3),

@@ -152,6 +152,15 @@ def test_emulated_launch_rule_shapes_match_oracle(emu, name, layout):
     _copy_case(emu, pool, spans, chunks, 98_500 + layout)
 
 
+@pytest.mark.parametrize("wg", [1, 7, 9])
+@pytest.mark.parametrize("name", ["tm_24k", "tm_32k", "tm_36k", "tm_48k", "tm_64k", "tm_80k", "hm_16k_t4"])
+def test_emulated_launch_rule_shapes_on_capped_grids(emu, name, wg):
+    """The same calls on grids of 1, 7 and 9 workgroups: every item taken once, every
+    access inside its buffer, the bytes equal to the oracle's."""
+    pool, spans, chunks = cases.rule_case(name, 1)
+    _copy_case(emu, pool, spans, chunks, 98_700 + wg, max_workgroups=wg)
+
+
 FULL = ["tiny", "llama8b", "llama70b", "mixed", "mla_fp8", "int8_kv", "llama8b_hnd", "fp8_hnd_d64", "llama8b_tp8",
         "hnd_rows24", "hnd_h100_r12", "llama8b_tp2", "llama8b_tp4", "llama8b_hnd_tp4"]
 
