@@ -517,11 +517,11 @@ int check_buffers(kv_pool *p, const kv_span *spans, int32_t n_spans, const kv_ch
 int launch_prepared(kv_pool *p, kvx::Launch &a, int direction, const kv_chunk_spec *spec,
                     const kvx::AllocRange &staging, hipStream_t stream)
 {
-    a.split_shift = kvx::launch_split_shift(a, direction);
-    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     const bool host_staging = staging_in_host_memory(p, spec->base, staging);
-    a.part_bytes = kvx::scatter_part_bytes(direction, a, host_staging, (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
+    a.split_shift = kvx::launch_split_shift(a, direction);
+    a.part_bytes = kvx::part_bytes_for(direction, a, host_staging, (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
     if (a.part_bytes) a.split_shift = 0;
+    a.seg_bytes = a.part_bytes ? 0u : kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0) grid = std::min<uint32_t>(grid, (uint32_t)spec->max_workgroups);
     else if (host_staging) grid = std::min<uint32_t>(grid, KVX_HOST_GRID_CAP);

@@ -136,7 +136,10 @@ namespace kvx {
 #define KVX_GATHER_POOL_POL KVX_POL_NT                   // gather's loads of pool pages
 #endif
 #ifndef KVX_SCATTER_SMALL_PART
-#define KVX_SCATTER_SMALL_PART 4096    // scatter parts of 16-64 KiB tiles (scatter_part_bytes)
+#define KVX_SCATTER_SMALL_PART 4096    // scatter parts of 20-64 KiB tiles (part_bytes_for)
+#endif
+#ifndef KVX_GATHER_FIXED_PART
+#define KVX_GATHER_FIXED_PART 4096     // gather parts of 20-64 KiB tiles that are not powers of two
 #endif
 #ifndef KVX_SCATTER_FIXED_PART
 #define KVX_SCATTER_FIXED_PART 16384   // scatter parts of larger 16 KiB-multiple tiles
@@ -228,7 +231,7 @@ struct Launch {
     // the multiplier dividing by the words of one head's page (block_size * hm_rd)
     uint32_t hm_page;
     // > 0: each tile is copied as parts of this many bytes (the last one shorter) by as
-    // many waves, instead of 2^split_shift equal parts (scatter_part_bytes)
+    // many waves, instead of 2^split_shift equal parts (part_bytes_for)
     uint32_t part_bytes;
     uint64_t hm_m_brd;
     // 1: the workgroups hand each XCD a contiguous eighth of the work items
@@ -257,13 +260,13 @@ static_assert(offsetof(Launch, inl) % alignof(SpanDev) == 0, "inline span record
 // Kernel-internal page layout values: head-major pages staged through LDS in token
 // slabs, in head-group slabs (hm_lds_head_slab), and a whole page at a time (hm_page_ok);
 // token-major pages whose split scatter tiles go through buffer instructions
-// (scatter_buffer_form), whose scatter tiles go in fixed-size parts (scatter_part_bytes),
-// and both.
+// (scatter_buffer_form), whose tiles go in fixed-size parts (part_bytes_for), and both
+// (scatter only).
 #define KVX_PAGE_HM_LDS 2
 #define KVX_PAGE_HM_LDS_HEADS 3
 #define KVX_PAGE_HM_LDS_PAGE 4
 #define KVX_PAGE_TM_SCATTER_BUF 5
-#define KVX_PAGE_TM_SCATTER_FIXED 6
+#define KVX_PAGE_TM_FIXED 6
 #define KVX_PAGE_TM_SCATTER_FIXED_BUF 7
 
 // Position of a 16-byte vector of a tile in token-major order -- token j, head h,
@@ -577,7 +580,7 @@ __host__ __device__ constexpr uint32_t launch_block(uint32_t b, uint32_t G, uint
 __host__ __device__ inline uint32_t xcd_remap_for(int dir, const Launch &a, bool host_staging)
 {
     if (dir == KV_SCATTER) {
-        // scatters in 4 KiB parts (scatter_part_bytes), except power-of-two tiles (32 KiB:
+        // scatters in 4 KiB parts (part_bytes_for), except power-of-two tiles (32 KiB:
         // whole workgroups per tile) with layer-first chunks
         const bool pow2 = (a.tile_bytes & (a.tile_bytes - 1)) == 0;
         return (!host_staging && a.part_bytes == KVX_SCATTER_SMALL_PART && !(pow2 && a.layout == KV_LAYER_FIRST))
@@ -592,7 +595,7 @@ __host__ __device__ inline uint32_t xcd_remap_for(int dir, const Launch &a, bool
 // Whether a scatter's token-major tiles go through buffer instructions, the pool stores
 // with nt + sc1 (KVX_SCATTER_POOL_POL), instead of global instructions with plain nt:
 // tiles split between waves in 2^k parts (8 to under 20 KiB, and from 64 KiB) or in
-// 4 KiB parts (scatter_part_bytes), with the staging in HBM.  Measured on MI355X,
+// 4 KiB parts (part_bytes_for), with the staging in HBM.  Measured on MI355X,
 // interleaved rounds in two processes each: the int8_kv scatter (64 KiB tiles, 4 parts)
 // gains 4.0-5.4 points of HBM peak, mixed (64 KiB) 0.7-1.0, the TP-2 shard (16 KiB)
 // 0.4-0.6, the TP-4 shard (8 KiB) -0.4 to +0.1, and 32 KiB tiles in 4 KiB parts 0.5-0.8
@@ -604,9 +607,16 @@ __host__ __device__ inline uint32_t scatter_buffer_form(int dir, const Launch &a
     return (dir == KV_SCATTER && a.page_layout == KV_PAGE_TOKEN_MAJOR && split && !host_staging) ? 1u : 0u;
 }
 
-// Fixed-size parts for a scatter's token-major tiles into HBM staging (0: the
-// split_shift rule), each part starting at a multiple of its size within the tile and
-// copied by its own wave, neighbouring waves taking one tile's parts:
+// Fixed-size parts for token-major tiles with HBM staging (0: the split_shift rule and,
+// for gathers, the segment walk), each part starting at a multiple of its size within
+// the tile and copied by its own wave, neighbouring waves taking one tile's parts:
+//  * gathers of tiles of 20 KiB to under 64 KiB that are not powers of two: 4 KiB parts
+//    (KVX_GATHER_FIXED_PART), in the per-XCD order (xcd_remap_for), instead of the 32 KiB
+//    segment walk.  Measured on MI355X in interleaved rounds, two processes: the MLA
+//    latent's 36 KiB tiles +3.5 to +3.9 points of HBM peak (71.4 -> 75.3 %), 20-56 KiB
+//    tiles with layer-first chunks +1.9 to +4.9, page-first 36 KiB +4.1, page-first 24 and
+//    48 KiB -0.8 to 0; 12 KiB parts lose 2, and 32 KiB tiles keep whole (in 4, 8 or 16 KiB
+//    parts: -2.4 to -6.6).  Scatters:
 //  * tiles of 20 KiB (where the small-tile split ends, KVX_SMALL_SCATTER_MAX) to less
 //    than 64 KiB: 4 KiB parts (KVX_SCATTER_SMALL_PART), in the buffer form
 //    (scatter_buffer_form).  Measured on MI355X in interleaved rounds, shuffled tables:
@@ -621,10 +631,12 @@ __host__ __device__ inline uint32_t scatter_buffer_form(int dir, const Launch &a
 //  * larger tiles that are whole multiples of 16 KiB but not powers of two: 16 KiB parts
 //    (KVX_SCATTER_FIXED_PART) in the global form: 80, 96 and 144 KiB tiles +2.3 to +6.5
 //    points against 4 equal parts.
-__host__ __device__ inline uint32_t scatter_part_bytes(int dir, const Launch &a, bool host_staging, bool page_runs)
+__host__ __device__ inline uint32_t part_bytes_for(int dir, const Launch &a, bool host_staging, bool page_runs)
 {
     const int64_t T = a.tile_bytes;
-    if (dir != KV_SCATTER || a.page_layout != KV_PAGE_TOKEN_MAJOR || host_staging) return 0u;
+    if (a.page_layout != KV_PAGE_TOKEN_MAJOR || host_staging) return 0u;
+    if (dir == KV_GATHER)
+        return (T >= 20480 && T < 65536 && (T & (T - 1)) != 0) ? (uint32_t)KVX_GATHER_FIXED_PART : 0u;
     if (T >= KVX_SMALL_SCATTER_MAX && T < 65536) return page_runs ? 0u : (uint32_t)KVX_SCATTER_SMALL_PART;
     if (T >= 65536 && T % KVX_SCATTER_FIXED_PART == 0 && (T & (T - 1)) != 0) return (uint32_t)KVX_SCATTER_FIXED_PART;
     return 0u;

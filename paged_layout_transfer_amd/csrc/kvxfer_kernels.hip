@@ -791,7 +791,7 @@ __global__ void __launch_bounds__(kThreads) tile_copy(const Launch a)
     // alone), part_bytes-sized ones.  The waves of a workgroup take consecutive items, so
     // a split tile is copied by neighbouring waves; workgroups take their items in
     // launch_block order (contiguous per XCD when a.xcd_remap).
-    constexpr bool FIXED = PAGE == KVX_PAGE_TM_SCATTER_FIXED || PAGE == KVX_PAGE_TM_SCATTER_FIXED_BUF;
+    constexpr bool FIXED = PAGE == KVX_PAGE_TM_FIXED || PAGE == KVX_PAGE_TM_SCATTER_FIXED_BUF;
     const uint32_t shift = a.split_shift;
     const int64_t ppt = FIXED ? parts_per_tile(a) : (int64_t)1 << shift;
     const int64_t items = a.total_tiles * ppt;
@@ -893,8 +893,10 @@ static const void *pick_page(const Launch &a)
     if constexpr (DIR == KV_SCATTER) {
         if (a.part_bytes)
             return a.scatter_buf ? pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_FIXED_BUF>(a)
-                                 : pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_FIXED>(a);
+                                 : pick_policy<DIR, LAYOUT, KVX_PAGE_TM_FIXED>(a);
         if (a.scatter_buf) return pick_policy<DIR, LAYOUT, KVX_PAGE_TM_SCATTER_BUF>(a);
+    } else {
+        if (a.part_bytes) return pick_policy<DIR, LAYOUT, KVX_PAGE_TM_FIXED>(a);
     }
     return pick_policy<DIR, LAYOUT, KV_PAGE_TOKEN_MAJOR>(a);
 }

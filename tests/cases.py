@@ -166,10 +166,11 @@ def head_major_case(rng: np.random.Generator, H: int, D: int, E: int, bs: int):
 
 # Shapes on each side of the launch rules, (H, D, E, block_size) -> what the launch does:
 # token-major tiles of 4-6 KiB take one wave; 8-14 KiB tiles, and 16-18 KiB scatters, go
-# in 4 parts; 16-48 KiB gathers that are not whole 32 KiB tiles walk 32 KiB segments (of
-# 2, 4 or 8-vector groups by the pieces they cut); 20-56 KiB scatters go in 4 KiB parts,
-# 32 KiB gathers whole; 64 KiB and larger tiles go in parts (72 KiB gathers in segments),
-# scatters of 80, 96 and 144 KiB in 16 KiB parts.  Head-major:
+# in 4 parts; 16-18 KiB gathers, and non-power-of-two gathers from 64 KiB, walk 32 KiB
+# segments (of 2, 4 or 8-vector groups by the pieces they cut); 20-56 KiB scatters, and
+# such gathers that are not powers of two, go in 4 KiB parts, 32 KiB gathers whole;
+# 64 KiB and larger tiles go in parts (72 KiB gathers in segments), scatters of 80, 96 and
+# 144 KiB in 16 KiB parts.  Head-major:
 # pages of at most 8 KiB with rows other than the 4 x 4 case through the LDS slabs, the
 # 4 x 4 register transpose, and the cursor walk for larger pages of other rows.
 RULE_SHAPES = {

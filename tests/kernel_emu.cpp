@@ -71,10 +71,10 @@ extern "C" int emu_transfer(int direction, const kv_pool_desc *d, const kv_span 
         if (spans[i].t_end > spans[i].t_begin) tlen.push_back(spans[i].table_len);
 
     a.split_shift = kvx::launch_split_shift(a, direction);
-    a.seg_bytes = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
-    a.part_bytes = kvx::scatter_part_bytes(direction, a, false,      // staging as if in HBM
-                                           (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
+    a.part_bytes = kvx::part_bytes_for(direction, a, false,      // staging as if in HBM
+                                       (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
     if (a.part_bytes) a.split_shift = 0;
+    a.seg_bytes = a.part_bytes ? 0u : kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     uint32_t grid = kvx::default_grid(kvx::work_items(a));
     if (spec->max_workgroups > 0 && (uint32_t)spec->max_workgroups < grid)
         grid = (uint32_t)spec->max_workgroups;
@@ -639,15 +639,15 @@ extern "C" int emu_launch_rule(int direction, const kv_pool_desc *d, const kv_sp
     const int rc = kvx::prepare_call(d, spans, n_spans, spec, records, &n_rec, &a, &info);
     if (rc) return rc;
     out[0] = kvx::launch_split_shift(a, direction);
-    out[1] = kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
     out[2] = a.hm_lds;
     out[3] = a.hm_page;
     out[4] = a.hm_t4;
-    a.seg_bytes = (uint32_t)out[1];
-    out[7] = kvx::scatter_part_bytes(direction, a, false, (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
+    out[7] = kvx::part_bytes_for(direction, a, false, (spec->flags & KV_FLAG_PAGE_RUNS) != 0);
     a.split_shift = out[7] ? 0u : (uint32_t)out[0];
     a.part_bytes = (uint32_t)out[7];
     out[0] = a.split_shift;
+    out[1] = out[7] ? 0 : kvx::gather_seg_bytes(direction, a.page_layout, a.tile_bytes);
+    a.seg_bytes = (uint32_t)out[1];
     out[5] = kvx::xcd_remap_for(direction, a, false);
     out[6] = kvx::scatter_buffer_form(direction, a, false);
     return KV_OK;

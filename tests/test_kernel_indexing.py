@@ -495,22 +495,24 @@ def _rule(lib, direction, H, D, E, bs=16, page_layout=0, flags=0, layout=K.KV_LA
 
 @pytest.mark.parametrize("H,D,E,gather,scatter", [
     # token-major tiles: 4 KiB one wave; 8-12 KiB gathers and 8-18 KiB scatters in 4 parts
-    # of 2 KiB or more; 16-31 KiB gathers in 32 KiB segments; 64 KiB gathers in 2 parts;
-    # scatters of 20 to under 64 KiB in 4 KiB parts, 64 and 128 KiB scatters in 4, and 80
-    # and 96 KiB scatters (multiples of 16 KiB that are not powers of two) in 16 KiB parts.
-    # (split shift, segment bytes, XCD remap, fixed part bytes): gathers of 8 KiB tiles or
-    # more outside the segment walk remap their workgroups, and so do scatters in 4 KiB
-    # parts other than 32 KiB tiles with layer-first chunks (these calls are layer-first);
-    # scatters split in 2^k parts or in 4 KiB parts go through buffer instructions
+    # of 2 KiB or more; 16 KiB gathers, and those of 64 KiB or more that are not powers of
+    # two, in 32 KiB segments; 20-64 KiB gathers that are not powers of two, and 20-64 KiB
+    # scatters, in 4 KiB parts; 64 KiB gathers in 2 parts, 64 and 128 KiB scatters in 4,
+    # and 80 and 96 KiB scatters (multiples of 16 KiB that are not powers of two) in 16 KiB
+    # parts.  (split shift, segment bytes, XCD remap, fixed part bytes): gathers of 8 KiB
+    # tiles or more outside the segment walk remap their workgroups, and so do scatters in
+    # 4 KiB parts other than 32 KiB tiles with layer-first chunks (these calls are
+    # layer-first); scatters split in 2^k parts or in 4 KiB parts go through buffer
+    # instructions
     (1, 128, 2, (0, 0, 0, 0), (0, 0, 0, 0)),
     (2, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
     (3, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
     (4, 128, 2, (None, 32768, 0, 0), (2, 0, 0, 0)),
-    (5, 128, 2, (None, 32768, 0, 0), (0, 0, 1, 4096)),
+    (5, 128, 2, (0, 0, 1, 4096), (0, 0, 1, 4096)),
     (8, 128, 2, (0, 0, 1, 0), (0, 0, 0, 4096)),
     (16, 128, 2, (1, 0, 1, 0), (2, 0, 0, 0)),
-    (9, 128, 2, (None, 32768, 0, 0), (0, 0, 1, 4096)),
-    (12, 128, 2, (None, 32768, 0, 0), (0, 0, 1, 4096)),
+    (9, 128, 2, (0, 0, 1, 4096), (0, 0, 1, 4096)),
+    (12, 128, 2, (0, 0, 1, 4096), (0, 0, 1, 4096)),
     (20, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
     (24, 128, 2, (None, 32768, 0, 0), (0, 0, 0, 16384)),
     (32, 128, 2, (2, 0, 1, 0), (2, 0, 0, 0)),
@@ -551,8 +553,8 @@ def test_page_runs_hint_keeps_20_to_64_kib_scatter_tiles_whole(emu, H, D, E, par
         assert runs["part"] == 0 and runs["shift"] == 0 and runs["sbuf"] == 0
     else:
         assert runs == plain
-    for d in (K.KV_GATHER,):
-        assert _rule(emu, d, H, D, E, flags=K.KV_FLAG_PAGE_RUNS) == _rule(emu, d, H, D, E)
+    # gathers ignore the hint
+    assert _rule(emu, K.KV_GATHER, H, D, E, flags=K.KV_FLAG_PAGE_RUNS) == _rule(emu, K.KV_GATHER, H, D, E)
 
 
 @pytest.mark.parametrize("H,D,E,bs,path", [
