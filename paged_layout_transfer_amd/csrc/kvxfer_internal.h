@@ -86,6 +86,13 @@ namespace kvx {
 #ifndef KVX_GATHER_SEG_MIN
 #define KVX_GATHER_SEG_MIN 16384
 #endif
+#ifndef KVX_HM_LDS_SPLIT_MIN
+// head-major pages staged through LDS slabs (not whole) from this size go in 4 parts:
+// measured on MI355X, 24 KiB pages of 24-byte rows gather at 73.5-73.7 % of HBM peak that
+// way against 64.7-64.8 % whole (2 parts: 68.6-68.9 %) and scatter at 63.5-63.8 % against
+// 61.2-61.3 %
+#define KVX_HM_LDS_SPLIT_MIN 16384
+#endif
 #ifndef KVX_MAX_SPLIT_SHIFT
 #define KVX_MAX_SPLIT_SHIFT 2     // at most 4 waves per tile
 #endif
@@ -382,11 +389,13 @@ __host__ __device__ constexpr uint32_t split_shift_for(int dir, int64_t tile_byt
 }
 
 // log2 of the parts each tile of a prepared call is split into for direction dir: a
-// head-major page moved whole through one wave's slice (hm_page) is never split, small
-// token-major tiles follow the SMALL_* rule, the rest split_shift_for.
+// head-major page moved whole through one wave's slice (hm_page) is never split, other
+// LDS-staged head-major pages of KVX_HM_LDS_SPLIT_MIN bytes or more go in 4 (ranges of
+// slabs), small token-major tiles follow the SMALL_* rule, the rest split_shift_for.
 __host__ __device__ inline uint32_t launch_split_shift(const Launch &a, int dir)
 {
     if (a.hm_page) return 0u;
+    if (a.hm_lds && a.tile_bytes >= KVX_HM_LDS_SPLIT_MIN) return KVX_MAX_SPLIT_SHIFT;
     const int64_t small_max = dir == KV_GATHER ? KVX_SMALL_GATHER_MAX : KVX_SMALL_SCATTER_MAX;
     if (a.page_layout == KV_PAGE_TOKEN_MAJOR && a.tile_bytes >= KVX_SMALL_SPLIT_MIN && a.tile_bytes < small_max) {
         uint32_t sh = 0;

@@ -577,6 +577,9 @@ def test_head_major_path_rules(emu, H, D, E, bs, path):
         r = _rule(emu, d, H, D, E, bs, page_layout=1)
         got = "t4" if r["t4"] else "page" if r["page"] else "lds" if r["lds"] else "cursor"
         assert got == path, (H, D, E, bs, r)
+        # LDS-staged pages (not whole) of 16 KiB or more go in 4 parts
+        if path == "lds":
+            assert r["shift"] == (2 if H * D * E * bs >= 16384 else 0), (d, r)
         # only the 4 x 4 gather remaps its workgroups per XCD; head-major scatters keep
         # their own copy loops
         assert r["xcd"] == int(d == K.KV_GATHER and path == "t4"), (d, r)
