@@ -93,8 +93,17 @@ namespace kvx {
 // 61.2-61.3 %
 #define KVX_HM_LDS_SPLIT_MIN 16384
 #endif
+#ifndef KVX_HM_T4_SCATTER_SPLIT_MIN
+// head-major pages moved by the 4 x 4 transpose are scattered from this size to under
+// twice it in 8 parts (ranges of the page's 4 KiB blocks of 4 tokens x 4 heads), one per
+// wave; larger pages follow split_shift_for (not measured split finer): measured on
+// MI355X, 32 KiB pages of 256-byte rows scatter at 69.8 % of HBM peak that way against
+// 68.4 % whole (8 parts with the per-XCD order 69.4 %, 4 parts with it 67.8 %)
+#define KVX_HM_T4_SCATTER_SPLIT_MIN 32768
+#endif
+#define KVX_HM_T4_SCATTER_SHIFT 3
 #ifndef KVX_MAX_SPLIT_SHIFT
-#define KVX_MAX_SPLIT_SHIFT 2     // at most 4 waves per tile
+#define KVX_MAX_SPLIT_SHIFT 2     // at most 4 waves per tile (other than the case above)
 #endif
 #ifndef KVX_GATHER_UNROLL
 #define KVX_GATHER_UNROLL 8    // 16-byte vectors per lane per group, gather
@@ -389,12 +398,17 @@ __host__ __device__ constexpr uint32_t split_shift_for(int dir, int64_t tile_byt
 }
 
 // log2 of the parts each tile of a prepared call is split into for direction dir: a
-// head-major page moved whole through one wave's slice (hm_page) is never split, other
-// LDS-staged head-major pages of KVX_HM_LDS_SPLIT_MIN bytes or more go in 4 (ranges of
-// slabs), small token-major tiles follow the SMALL_* rule, the rest split_shift_for.
+// head-major page moved whole through one wave's slice (hm_page) is never split,
+// scatters of 4 x 4-transposed pages of KVX_HM_T4_SCATTER_SPLIT_MIN bytes to under twice
+// that go in 8 (ranges of 4 KiB blocks), other LDS-staged head-major pages of KVX_HM_LDS_SPLIT_MIN
+// bytes or more in 4 (ranges of slabs), small token-major tiles follow the SMALL_* rule,
+// the rest split_shift_for.
 __host__ __device__ inline uint32_t launch_split_shift(const Launch &a, int dir)
 {
     if (a.hm_page) return 0u;
+    if (a.hm_t4 && dir == KV_SCATTER && a.tile_bytes >= KVX_HM_T4_SCATTER_SPLIT_MIN &&
+        a.tile_bytes < 2 * KVX_HM_T4_SCATTER_SPLIT_MIN)
+        return KVX_HM_T4_SCATTER_SHIFT;
     if (a.hm_lds && a.tile_bytes >= KVX_HM_LDS_SPLIT_MIN) return KVX_MAX_SPLIT_SHIFT;
     const int64_t small_max = dir == KV_GATHER ? KVX_SMALL_GATHER_MAX : KVX_SMALL_SCATTER_MAX;
     if (a.page_layout == KV_PAGE_TOKEN_MAJOR && a.tile_bytes >= KVX_SMALL_SPLIT_MIN && a.tile_bytes < small_max) {

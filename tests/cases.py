@@ -172,7 +172,8 @@ def head_major_case(rng: np.random.Generator, H: int, D: int, E: int, bs: int):
 # 64 KiB and larger tiles go in parts (72 KiB gathers in segments), scatters of 80, 96 and
 # 144 KiB in 16 KiB parts.  Head-major:
 # pages of at most 8 KiB with rows other than the 4 x 4 case through the LDS slabs, the
-# 4 x 4 register transpose, and the cursor walk for larger pages of other rows.
+# 4 x 4 register transpose (scattered in 8 parts from 32 to under 64 KiB), LDS slabs of
+# 16 KiB pages and more in 4 parts, and the cursor walk for larger pages of other rows.
 RULE_SHAPES = {
     "tm_4k": (0, 1, 128, 2, 16), "tm_6k": (0, 3, 64, 2, 16), "tm_8k": (0, 2, 128, 2, 16),
     "tm_10k": (0, 5, 64, 2, 16), "tm_12k": (0, 3, 128, 2, 16), "tm_14k": (0, 7, 64, 2, 16),
@@ -184,7 +185,8 @@ RULE_SHAPES = {
     "hm_8k_2x256": (1, 2, 128, 2, 16), "hm_8k_1x512": (1, 1, 256, 2, 16), "hm_4k_2x128": (1, 2, 64, 2, 16),
     "hm_4k_8x32": (1, 8, 32, 1, 16), "hm_8k_t4": (1, 4, 128, 2, 8), "hm_16k_t4": (1, 4, 128, 2, 16),
     "hm_12k_3x256": (1, 3, 128, 2, 16), "hm_16k_1x256": (1, 1, 128, 2, 64), "hm_24k_3x512": (1, 3, 256, 2, 16),
-    "hm_24k_6x256": (1, 6, 128, 2, 16),
+    "hm_24k_6x256": (1, 6, 128, 2, 16), "hm_32k_t4": (1, 8, 128, 2, 16), "hm_48k_t4": (1, 12, 128, 2, 16),
+    "hm_64k_t4": (1, 16, 128, 2, 16), "hm_32k_16x128": (1, 16, 64, 2, 16), "hm_24k_16x24": (1, 16, 12, 2, 64),
 }
 
 

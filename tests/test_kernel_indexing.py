@@ -580,6 +580,10 @@ def test_head_major_path_rules(emu, H, D, E, bs, path):
         # LDS-staged pages (not whole) of 16 KiB or more go in 4 parts
         if path == "lds":
             assert r["shift"] == (2 if H * D * E * bs >= 16384 else 0), (d, r)
+        # 4 x 4-transposed pages of 32 to under 64 KiB are scattered in 8 parts (one 4 KiB
+        # block of 4 tokens x 4 heads each for 32 KiB pages), gathered whole
+        if path == "t4" and H * D * E * bs < 65536:
+            assert r["shift"] == (3 if d == K.KV_SCATTER and H * D * E * bs >= 32768 else 0), (d, r)
         # only the 4 x 4 gather remaps its workgroups per XCD; head-major scatters keep
         # their own copy loops
         assert r["xcd"] == int(d == K.KV_GATHER and path == "t4"), (d, r)
